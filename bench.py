@@ -1,0 +1,205 @@
+"""MoE-layer forward benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload v3] [--cpu-sample S]
+
+One step = one whole layer forward (route -> dispatch -> routed expert FFN ->
+shared expert -> combine) over one batch of T tokens, inputs and weights
+resident in HBM.  Prints one JSON line: tokens/s for the whole step, per-stage
+times from HIP events on the stream the kernels run on, the roofline of the
+dominant kernel (the routed up-projection GEMM + SwiGLU), and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/sec on 1 MI355X; GEMM MFMA % peak; route/permute GB/s"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="v3")
+    ap.add_argument("--cpu-sample", type=int, default=512, help="tokens the CPU oracle runs (0: skip)")
+    return ap.parse_args()
+
+
+def workload_name(cfg) -> str:
+    s = (f"{cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} G={cfg.G} k={cfg.k} M={cfg.M} d_ff={cfg.d_ff} "
+         f"{cfg.dtype}")
+    if cfg.local:
+        s += f" experts [{cfg.e_begin},{cfg.e_end}) only"
+    else:
+        s += f" + {cfg.n_shared} shared expert"
+    if cfg.skew:
+        s += ", Zipf(1.2) logit offset"
+    return s
+
+
+def algorithmic(cfg):
+    """Per-launch algorithmic work of each stage."""
+    T, d, E, k, d_ff = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    P = T * k if not cfg.local else None
+    act = 4 if cfg.dtype == "f32" else 2
+    return {
+        "route_flops": 2 * T * d * E,
+        "route_select_bytes": T * E * 4 + E * 4 + T * k * 8 + ((T + 63) // 64) * E * 4,
+        "dispatch_bytes": lambda rows: T * d * act + rows * (d * act) + 12 * T * k,
+        "ffn_up_flops": lambda rows: 4 * d * d_ff * rows,
+        "ffn_down_flops": lambda rows: 2 * d * d_ff * rows,
+        "shared_flops": 6 * d * d_ff * T,
+        "combine_bytes": lambda rows: rows * d * act + 8 * T * k + (T * d * act if not cfg.local else 0)
+        + T * d * (4 * 2 if cfg.local else act),
+        "pairs": P,
+    }
+
+
+def cpu_baseline(cfg, inp, ex, S):
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import combine as OC, dispatch as OD, ffn as OF, route as OR
+
+    S = min(S, cfg.T)
+    x = inp["x"][:S].float().cpu().numpy()
+    wg = inp["w_gate"].cpu().numpy()
+    bias = inp["bias"].cpu().numpy()
+    off = None if inp["logit_offset"] is None else inp["logit_offset"].cpu().numpy()
+    # weights as the GPU holds them, copied to host memory before timing; the
+    # oracle converts each expert to fp64 as it streams through them
+    w13_h = ex["w13"].cpu()
+    w2_h = ex["w2"].cpu()
+    sh13 = ex["sh_w13"][0].cpu()
+    sh2 = ex["sh_w2"][0].cpu()
+    f = lambda t: t.float().numpy()
+    t0 = time.perf_counter()
+    L, idx, w = OR.route(x, wg, bias, cfg.G, cfg.M, cfg.k, cfg.gk, off)
+    counts, offsets, dest, src = OD.dispatch(idx, cfg.E, cfg.e_begin, cfg.e_end)
+    yp, _ = OF.grouped_ffn(OD.pack(x, src), offsets, None, None,
+                           weight_fn=lambda i: (f(w13_h[i]), f(w2_h[i])))
+    if cfg.local:
+        out = OC.combine(yp, dest, w, out_init=np.zeros((S, cfg.d)))
+    else:
+        ysh, _ = OF.expert_forward(x, f(sh13), f(sh2))
+        out = OC.combine(yp, dest, w, ysh=ysh)
+    t = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": S / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {S} of the {cfg.T} tokens, whole layer (route, dispatch, all routed "
+                      f"experts they reach, shared expert, combine) in fp64 numpy; {t:.1f} s; "
+                      f"host affinity {len(os.sched_getaffinity(0))} cpus",
+            "seconds": t}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+
+    import moe_expert_routing_sqrt_amd as M
+    from moe_inputs import configs as C, generate as gen
+
+    cfg = C.get(a.workload)
+    dev = torch.device("cuda:0")
+    t_setup = time.perf_counter()
+    inp = gen.make_router(cfg, device=dev)
+    ex = gen.make_experts(cfg, device=dev)
+    layer = M.MoELayer(cfg.T, cfg.d, cfg.E, cfg.G, cfg.M, cfg.k, cfg.d_ff, cfg.dtype, inp["w_gate"],
+                       inp["bias"], ex["w13"], ex["w2"], ex["sh_w13"], ex["sh_w2"],
+                       logit_offset=inp["logit_offset"], e_begin=cfg.e_begin, e_end=cfg.e_end,
+                       group_topk=cfg.gk)
+    x = inp["x"]
+    torch.cuda.synchronize()
+    print(f"setup {time.perf_counter() - t_setup:.1f}s: {workload_name(cfg)}", file=sys.stderr, flush=True)
+
+    for _ in range(a.warmup):
+        layer.forward(x)
+    torch.cuda.synchronize()
+    print(f"warmup {a.warmup} done", file=sys.stderr, flush=True)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = [[ev() for _ in range(7)] for _ in range(a.steps)]
+    start, end = ev(), ev()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(a.steps):
+        layer.forward(x, marks=marks[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = start.elapsed_time(end) / a.steps
+    print(f"timed {a.steps} steps: {ms_per_step:.3f} ms/step (host wall {wall / a.steps * 1e3:.3f})",
+          file=sys.stderr, flush=True)
+
+    names = ("route", "dispatch", "ffn_up", "ffn_down", "shared", "combine")
+    st_ms = {n: sum(m[i].elapsed_time(m[i + 1]) for m in marks) / a.steps for i, n in enumerate(names)}
+    rows = int(layer.dbufs["offsets"][-1].item())
+    alg = algorithmic(cfg)
+    peak_mm = PEAK_FP8_TFLOPS if cfg.dtype == "fp8" else PEAK_BF16_TFLOPS
+    tf = lambda flops, ms: flops / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
+    gbs = lambda byts, ms: byts / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+    stages = {
+        "route": {"ms": st_ms["route"], "gate_tflops": tf(alg["route_flops"], st_ms["route"])},
+        "dispatch": {"ms": st_ms["dispatch"], "gb_s": gbs(alg["dispatch_bytes"](rows), st_ms["dispatch"])},
+        "ffn_up": {"ms": st_ms["ffn_up"], "tflops": tf(alg["ffn_up_flops"](rows), st_ms["ffn_up"])},
+        "ffn_down": {"ms": st_ms["ffn_down"], "tflops": tf(alg["ffn_down_flops"](rows), st_ms["ffn_down"])},
+        "shared": {"ms": st_ms["shared"], "tflops": tf(alg["shared_flops"] if layer.has_shared else 0,
+                                                        st_ms["shared"])},
+        "combine": {"ms": st_ms["combine"], "gb_s": gbs(alg["combine_bytes"](rows), st_ms["combine"])},
+    }
+    for s in ("dispatch", "combine"):
+        stages[s]["frac_hbm"] = stages[s]["gb_s"] / PEAK_HBM_GBS
+    for s in ("ffn_up", "ffn_down", "shared"):
+        stages[s]["frac_mfma"] = stages[s]["tflops"] / peak_mm
+    gemm_ms = st_ms["ffn_up"] + st_ms["ffn_down"] + st_ms["shared"]
+    gemm_flops = alg["ffn_up_flops"](rows) + alg["ffn_down_flops"](rows) + (alg["shared_flops"] if layer.has_shared else 0)
+    up = stages["ffn_up"]
+    result = {
+        "metric": METRIC,
+        "value": cfg.T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "e4m3"}[cfg.dtype],
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02^2) weights, U(-0.1,0.1) bias)",
+        "config": {"workload": workload_name(cfg), "T": cfg.T, "d": cfg.d, "E": cfg.E, "G": cfg.G,
+                   "k": cfg.k, "M": cfg.M, "d_ff": cfg.d_ff, "routed_rows": rows},
+        "roofline": {"kernel": "routed up-projection GEMM + SwiGLU (moe_expert_ffn MOE_FFN_UP)",
+                     "bound": "mfma", "achieved": up["tflops"], "peak": peak_mm, "unit": "TFLOP/s",
+                     "frac": up["tflops"] / peak_mm, "traffic": None,
+                     "avg_ms": up["ms"], "flops_per_launch": alg["ffn_up_flops"](rows)},
+        "gemm_mfma_frac": tf(gemm_flops, gemm_ms) / peak_mm,
+        "stages": stages,
+    }
+    if a.cpu_sample > 0:
+        print("cpu baseline ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, ex, a.cpu_sample)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

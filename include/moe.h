@@ -1,0 +1,227 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) mixture-of-experts layer forward.
+ *
+ * One MoE layer forward on one GPU, in four calls that run back to back on a
+ * HIP stream (deepmox ch.5 "The network becomes part of the forward pass": a
+ * forward chunk dispatches tokens to experts, runs the expert MLP, combines;
+ * zenaique "Why all to all dominates MoE step time": two exchanges per
+ * forward, dispatch and combine):
+ *
+ *   moe_route       gate logits, sqrt(softplus) affinities, bias-adjusted
+ *                   node-limited top-k, renormalised gate weights, per-block
+ *                   expert histogram
+ *   moe_dispatch    per-expert counts, exclusive scan, stable permutation,
+ *                   packed expert-contiguous (= group-ordered) token rows
+ *   moe_expert_ffn  grouped SwiGLU expert FFN (routed experts, or the shared
+ *                   expert as one group over all tokens)
+ *   moe_combine     gate-weighted sum of expert rows back in token order
+ *
+ * Conventions for every call
+ *   - Pointers are device pointers unless marked "host".  The caller owns and
+ *     allocates every buffer, including workspaces; the library never
+ *     allocates, frees or synchronises, and reads no device value back to the
+ *     host (data-dependent sizes such as per-expert counts stay on the device,
+ *     so row buffers are sized for the worst case T*k).
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) in call order.  Calls are reentrant given distinct buffers.
+ *   - Everything is row-major.  Weights are [out, in], so the reduction
+ *     dimension is contiguous for both products.  bf16 is IEEE bfloat16 (bit
+ *     pattern in a uint16), e4m3 is OCP E4M3FN in a uint8.
+ *   - Return value: MOE_OK or a negative MOE_ERR_*.  Arguments are checked on
+ *     the host before anything is launched; on an error nothing is launched
+ *     and no output is touched.  MOE_ERR_HIP reports a failed launch
+ *     (hipGetLastError); outputs are then undefined.  T = 0 is a no-op.
+ *     Non-finite logits are outside the contract.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1)  /* null pointer, inconsistent shape, bad range */
+#define MOE_ERR_UNSUPPORTED (-2)  /* valid, but not a shape/dtype this build runs */
+#define MOE_ERR_WORKSPACE (-3)    /* workspace smaller than *_workspace_size() */
+#define MOE_ERR_HIP (-4)          /* a kernel launch failed */
+
+/* element types */
+#define MOE_F32 0
+#define MOE_BF16 1
+#define MOE_E4M3 2
+
+/* moe_route flags */
+#define MOE_ROUTE_LOGITS_IN 1     /* skip the gate product: read `logits` as input */
+
+/* moe_expert_ffn stages */
+#define MOE_FFN_UP 1              /* h = silu(x W1^T) * (x W3^T)   */
+#define MOE_FFN_DOWN 2            /* y = h W2^T                    */
+#define MOE_FFN_ALL 3
+
+/* tokens per row of the block histogram written by moe_route */
+#define MOE_ROUTE_BLOCK 64
+/* fp8 scale granularity: 1 x 128 activation tiles, 128 x 128 weight blocks */
+#define MOE_FP8_TILE 128
+
+typedef void* moe_stream_t; /* hipStream_t */
+
+/*
+ * Layer shape.
+ *   T tokens, d model width, E routed experts in G groups of E/G consecutive
+ *   experts (group = "node" of node-limited routing: zenaique "MoE
+ *   node-limited routing", definition; deepnotes "The real cluster": 4
+ *   consecutive experts per GPU), at most M groups per token, k experts per
+ *   token, group_topk affinities summed per group score (ceil(k/M)), d_ff
+ *   expert hidden width.
+ * Checked: T >= 0; d, E, G, M, k, group_topk, d_ff > 0; G divides E;
+ *   M <= G; group_topk <= E/G; k <= M*E/G.
+ */
+typedef struct moe_shape {
+  int64_t T;
+  int32_t d, E, G, M, k, group_topk, d_ff;
+} moe_shape;
+
+int moe_abi_version(void);
+const char* moe_status_str(int status);
+
+/*
+ * moe_gate_prepare - store the fp32 router weight for the gate product.
+ *   w_gate  [d, E] fp32 (in)
+ *   w_prep  [3, E, d] bf16 (out): planes hi, mid, lo with hi+mid+lo == w
+ *           exactly in fp32 (each plane the round-to-nearest bf16 of what the
+ *           planes before it leave).  bf16 x times a bf16 plane is exact in
+ *           fp32, so the gate product runs on bf16 matrix cores and stays
+ *           fp32-accurate (the router is kept out of low precision: deepnotes
+ *           "The iteration loop", the FP8 recipe excludes the router gate).
+ * One-time weight preparation, like loading a checkpoint; not part of a step.
+ */
+int moe_gate_prepare(int32_t d, int32_t E, const float* w_gate, void* w_prep, moe_stream_t stream);
+
+/*
+ * moe_route - routing for T tokens (mastering-deepseek-v4 "MoE + Expert-
+ * Parallel Overlap (Exp08)", Implemented: top-k gating over Sqrt(Softplus)
+ * affinities, per-expert bias for balancing; zenaique "MoE node-limited
+ * routing": at most M nodes per token).
+ *   x             [T, d] in x_dtype (MOE_BF16 or MOE_F32); unused with LOGITS_IN
+ *   w_prep        [3, E, d] bf16 from moe_gate_prepare; unused with LOGITS_IN
+ *   bias          [E] fp32 per-expert selection bias
+ *   logit_offset  [E] fp32 added to every token's logits, or NULL
+ *   logits        [T, E] fp32: out = x . W_g (fp32-accurate), or in with
+ *                 MOE_ROUTE_LOGITS_IN
+ *   topk_idx      [T, k] int32 out: chosen experts, biased affinity
+ *                 descending, ties to the lower expert index
+ *   topk_w        [T, k] fp32 out: s_j / (s_0 + s_1 + ... ) over the chosen
+ *                 experts, s = unbiased affinity, left-to-right fp32 sum
+ *   block_counts  [ceil(T/MOE_ROUTE_BLOCK), E] int32 out: pairs routed to each
+ *                 expert within each block of MOE_ROUTE_BLOCK tokens
+ * From logits on, every value is produced by a fixed fp32 operation sequence
+ * (affinity = sqrt(max(l,0) + log1p(exp(-|l|))) with Cody-Waite exp and the
+ * Goldberg log1p; group score = top group_topk biased affinities summed
+ * largest first; top-M groups, ties to the lower group; experts outside kept
+ * groups excluded), so results are reproducible bit for bit from the logits.
+ * Supported: E <= 256 with E a multiple of 64 or E <= 64; E/G a multiple of
+ * ceil(E/64) forming a power-of-two number of 64-lane wave lanes;
+ * group_topk <= 4; k <= 16.  MOE_BF16 x needs d % 64 == 0 and E % 64 == 0.
+ */
+int moe_route(const moe_shape* shape, const void* x, int x_dtype, const void* w_prep,
+              const float* bias, const float* logit_offset, float* logits, int32_t* topk_idx,
+              float* topk_w, int32_t* block_counts, int flags, moe_stream_t stream);
+
+/*
+ * moe_dispatch - pack token rows into an expert-contiguous buffer (deepmox
+ * ch.5, dispatch; zenaique "Why all to all dominates": dispatch ships each
+ * token's row to the holders of its k experts; shivam2003 "Worked example":
+ * bytes = tokens x hidden x bytes per direction).  Only experts in
+ * [e_begin, e_end) are packed (one expert-parallel rank's share; pass 0, E for
+ * all).  With consecutive experts per group the buffer is group-ordered: it
+ * is this GPU's all-to-all send layout.
+ *   topk_idx, block_counts  from moe_route
+ *   x        [T, d] in x_dtype (MOE_BF16 or MOE_F32)
+ *   out_dtype  x_dtype (plain copy) or MOE_E4M3 from MOE_BF16 x (d % 128 == 0)
+ *   counts   [n] int32 out, n = e_end - e_begin: pairs per local expert
+ *   offsets  [n + 1] int32 out: exclusive prefix sum, offsets[0] = 0
+ *   dest     [T, k] int32 out: packed row of pair (t, j), -1 if not local
+ *   src      [T*k] int32 out: token of packed row r, for r < offsets[n]
+ *   xp       [T*k, d] out: xp[r] = x[src[r]] (copied, or quantised to e4m3
+ *            with one fp32 scale per 1 x 128 tile: scale = amax/448, or 1
+ *            for an all-zero tile; code = e4m3(x / scale) rounded to
+ *            nearest-even, saturating)
+ *   xp_scale [T*k, d/128] fp32 out for MOE_E4M3, else ignored (may be NULL)
+ *   ws       workspace of at least moe_dispatch_workspace_size() bytes
+ * Row numbering is stable: within an expert, rows follow token order.
+ */
+size_t moe_dispatch_workspace_size(const moe_shape* shape, int32_t e_begin, int32_t e_end);
+int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const int32_t* block_counts,
+                 int32_t e_begin, int32_t e_end, const void* x, int x_dtype, int out_dtype,
+                 int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src, void* xp,
+                 float* xp_scale, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_expert_ffn - grouped SwiGLU experts (mastering-deepseek-v4 Exp08,
+ * Implemented: shared always-active experts plus fine-grained routed ones;
+ * 6*d*d_ff flops per token-expert pair, i.e. three d x d_ff matrices).
+ * Expert i processes rows [offsets[i], offsets[i+1]) of xp:
+ *     h = silu(x W1_i^T) * (x W3_i^T),   y = h W2_i^T,   silu(a) = a/(1+e^-a)
+ * The shared expert is the same call with n_exp = 1 over x itself
+ * (offsets = {0, T}).
+ *   n_exp     number of experts in this call (<= 1024)
+ *   offsets   [n_exp + 1] int32 (device), non-decreasing, offsets[0] = 0,
+ *             offsets[n_exp] <= max_rows
+ *   max_rows  host upper bound on offsets[n_exp]: sizes the launch
+ *   dtype     MOE_F32, MOE_BF16 or MOE_E4M3 (the storage type of xp, the
+ *             weights and h); accumulation is fp32 throughout
+ *   xp        [max_rows, d];  xp_scale [max_rows, d/128] fp32 for e4m3
+ *   w13       [n_exp, 2*d_ff, d]: rows 0..d_ff-1 = W1 (gate), d_ff.. = W3 (up)
+ *   w2        [n_exp, d, d_ff]
+ *   w13_scale [n_exp, 2*d_ff/128, d/128], w2_scale [n_exp, d/128, d_ff/128]
+ *             fp32 block scales for e4m3, else ignored
+ *   h         [max_rows, d_ff] intermediate in dtype (bf16 for MOE_BF16);
+ *             h_scale [max_rows, d_ff/128] for e4m3
+ *   yp        [max_rows, d] out: fp32 for MOE_F32, bf16 otherwise
+ *   stages    MOE_FFN_UP, MOE_FFN_DOWN or MOE_FFN_ALL
+ * Supported: MOE_BF16 needs d % 256 == 0 and d_ff % 128 == 0; MOE_E4M3 needs
+ * d % 256 == 0 and d_ff % 128 == 0; MOE_F32 any d, d_ff.
+ */
+int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int32_t d,
+                   int32_t d_ff, int dtype, const void* xp, const float* xp_scale,
+                   const void* w13, const float* w13_scale, const void* w2,
+                   const float* w2_scale, void* h, float* h_scale, void* yp, int stages,
+                   moe_stream_t stream);
+
+/*
+ * moe_combine - out[t] = ysh[t] + sum_j topk_w[t,j] * yp[dest[t,j]]
+ * (deepmox ch.5, combine), slots with dest = -1 skipped, summed in fp32 in
+ * slot order starting from ysh (or from 0 without ysh).
+ *   dest, topk_w  [T, k] from moe_dispatch / moe_route
+ *   yp     [rows, d] in y_dtype (MOE_BF16 or MOE_F32)
+ *   ysh    [T, d] in y_dtype (shared-expert output) or NULL
+ *   out    [T, d] in out_dtype (MOE_BF16 or MOE_F32)
+ *   accumulate  0: out = sum;  1: out += sum (out must be MOE_F32; one
+ *               expert-parallel rank scatter-adding its share)
+ */
+int moe_combine(const moe_shape* shape, const int32_t* dest, const float* topk_w, const void* yp,
+                int y_dtype, const void* ysh, void* out, int out_dtype, int accumulate,
+                moe_stream_t stream);
+
+/*
+ * moe_quantize_blocks_e4m3 - fp32 [n, rows, cols] -> e4m3 codes
+ * [n, rows, cols] with one fp32 scale per 128 x 128 block
+ * [n, rows/128, cols/128] (scale = amax/448, or 1 for an all-zero block;
+ * code = e4m3(w / scale), nearest-even, saturating).  Weight preparation for
+ * the fp8 workload; rows and cols must be multiples of 128.
+ */
+int moe_quantize_blocks_e4m3(int64_t n, int32_t rows, int32_t cols, const float* w, uint8_t* q,
+                             float* scale, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

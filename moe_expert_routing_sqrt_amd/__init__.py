@@ -1,0 +1,231 @@
+"""MI355X (gfx950) MoE-layer forward: Python binding of libmoe_mi355x.so.
+
+The functions here only marshal torch tensors (device memory) and the current
+HIP stream into the C ABI declared in include/moe.h; every step of the layer
+runs in the library's HIP kernels.  There is no CPU or PyTorch fallback: if the
+library is missing, or a tensor is not on the GPU, calls raise.
+
+    route(shape, x, w_prep, bias)            -> logits, topk_idx, topk_w, block_counts
+    dispatch(shape, topk_idx, block_counts, x) -> counts, offsets, dest, src, xp, xp_scale
+    expert_ffn(offsets, max_rows, xp, w13, w2) -> yp
+    combine(shape, dest, topk_w, yp, ysh)    -> out
+    MoELayer                                 weights + buffers, forward(x) = the four calls
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN, MOE_FFN_UP,  # noqa: F401
+                   MOE_FP8_TILE, MOE_ROUTE_BLOCK, MOE_ROUTE_LOGITS_IN, MoeError, MoeShape)
+
+__all__ = ["shape", "gate_prepare", "route", "dispatch", "expert_ffn", "combine",
+           "quantize_blocks_e4m3", "MoELayer", "MoeError", "lib"]
+
+
+def lib():
+    return _lib.load()
+
+
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.uint8: MOE_E4M3,
+       torch.float8_e4m3fn: MOE_E4M3}
+_TORCH = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.uint8}
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}") from None
+
+
+def _ptr(t: Optional[torch.Tensor]) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the MoE library must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MoE library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device=None) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: Optional[torch.Tensor], numel: int, name: str):
+    if t is not None and t.numel() < numel:
+        raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
+
+
+def shape(T, d, E, G, M, k, d_ff, group_topk=None) -> MoeShape:
+    gk = -(-k // M) if group_topk is None else group_topk
+    return MoeShape(int(T), int(d), int(E), int(G), int(M), int(k), int(gk), int(d_ff))
+
+
+def n_blocks(T: int) -> int:
+    return (T + MOE_ROUTE_BLOCK - 1) // MOE_ROUTE_BLOCK
+
+
+def gate_prepare(w_gate: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 W_g [d, E] -> [3, E, d] bf16 planes summing exactly to W_g."""
+    d, E = w_gate.shape
+    if w_gate.dtype != torch.float32:
+        raise TypeError("w_gate must be fp32")
+    if out is None:
+        out = torch.empty((3, E, d), dtype=torch.bfloat16, device=w_gate.device)
+    _need(out, 3 * E * d, "w_prep")
+    _lib.check("moe_gate_prepare", lib().moe_gate_prepare(d, E, _ptr(w_gate), _ptr(out), _stream()))
+    return out
+
+
+def route(sh: MoeShape, x: Optional[torch.Tensor], w_prep: Optional[torch.Tensor], bias: torch.Tensor,
+          logit_offset: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+          logits_in: bool = False, idx=None, w=None, block_counts=None):
+    T, E, k = sh.T, sh.E, sh.k
+    dev = bias.device
+    if logits is None:
+        if logits_in:
+            raise ValueError("logits_in needs logits")
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev) if idx is None else idx
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
+    if block_counts is None:
+        block_counts = torch.empty((n_blocks(T), E), dtype=torch.int32, device=dev)
+    _need(logits, T * E, "logits")
+    _need(idx, T * k, "topk_idx")
+    _need(w, T * k, "topk_w")
+    _need(block_counts, n_blocks(T) * E, "block_counts")
+    _need(bias, E, "bias")
+    _need(logit_offset, E, "logit_offset")
+    x_dtype = MOE_BF16
+    if not logits_in:
+        _need(x, T * sh.d, "x")
+        _need(w_prep, 3 * E * sh.d, "w_prep")
+        x_dtype = _dt(x)
+    st = lib().moe_route(ctypes.byref(sh), _ptr(x) if not logits_in else 0, x_dtype,
+                         _ptr(w_prep) if not logits_in else 0, _ptr(bias), _ptr(logit_offset),
+                         _ptr(logits), _ptr(idx), _ptr(w), _ptr(block_counts),
+                         MOE_ROUTE_LOGITS_IN if logits_in else 0, _stream())
+    _lib.check("moe_route", st)
+    return logits, idx, w, block_counts
+
+
+def dispatch_workspace_bytes(sh: MoeShape, e_begin=0, e_end=None) -> int:
+    e_end = sh.E if e_end is None else e_end
+    return lib().moe_dispatch_workspace_size(ctypes.byref(sh), e_begin, e_end)
+
+
+def dispatch(sh: MoeShape, idx: torch.Tensor, block_counts: torch.Tensor, x: torch.Tensor,
+             e_begin: int = 0, e_end: Optional[int] = None, out_dtype: Optional[int] = None,
+             bufs: Optional[dict] = None) -> dict:
+    e_end = sh.E if e_end is None else e_end
+    n = e_end - e_begin
+    T, k, d = sh.T, sh.k, sh.d
+    dev = x.device
+    x_dtype = _dt(x)
+    out_dtype = x_dtype if out_dtype is None else out_dtype
+    b = {} if bufs is None else bufs
+    rows = T * k
+    if "counts" not in b:
+        b["counts"] = torch.empty(n, dtype=torch.int32, device=dev)
+        b["offsets"] = torch.empty(n + 1, dtype=torch.int32, device=dev)
+        b["dest"] = torch.empty((T, k), dtype=torch.int32, device=dev)
+        b["src"] = torch.empty(rows, dtype=torch.int32, device=dev)
+        b["xp"] = torch.empty((rows, d), dtype=_TORCH[out_dtype], device=dev)
+        b["xp_scale"] = (torch.empty((rows, d // MOE_FP8_TILE), dtype=torch.float32, device=dev)
+                         if out_dtype == MOE_E4M3 else None)
+        wsb = dispatch_workspace_bytes(sh, e_begin, e_end)
+        b["ws"] = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
+    _need(b["counts"], n, "counts")
+    _need(b["offsets"], n + 1, "offsets")
+    _need(b["dest"], T * k, "dest")
+    _need(b["src"], rows, "src")
+    _need(b["xp"], rows * d, "xp")
+    _need(x, T * d, "x")
+    _need(idx, T * k, "topk_idx")
+    _need(block_counts, n_blocks(T) * sh.E, "block_counts")
+    if out_dtype == MOE_E4M3:
+        _need(b["xp_scale"], rows * (d // MOE_FP8_TILE), "xp_scale")
+    st = lib().moe_dispatch(ctypes.byref(sh), _ptr(idx), _ptr(block_counts), e_begin, e_end, _ptr(x),
+                            x_dtype, out_dtype, _ptr(b["counts"]), _ptr(b["offsets"]), _ptr(b["dest"]),
+                            _ptr(b["src"]), _ptr(b["xp"]), _ptr(b["xp_scale"]), _ptr(b["ws"]),
+                            b["ws"].numel(), _stream())
+    _lib.check("moe_dispatch", st)
+    return b
+
+
+def expert_ffn(offsets: torch.Tensor, max_rows: int, xp: Optional[torch.Tensor], w13, w2,
+               dtype: Optional[int] = None, xp_scale=None, w13_scale=None, w2_scale=None,
+               h: Optional[torch.Tensor] = None, h_scale=None, yp: Optional[torch.Tensor] = None,
+               stages: int = MOE_FFN_ALL, d: Optional[int] = None, d_ff: Optional[int] = None):
+    """Grouped SwiGLU experts over rows [offsets[i], offsets[i+1]) of xp."""
+    n_exp = offsets.numel() - 1
+    ref = w13 if w13 is not None else w2
+    dtype = _dt(ref) if dtype is None else dtype
+    if w13 is not None:
+        d_ff = w13.shape[1] // 2
+        d = w13.shape[2]
+    else:
+        d, d_ff = w2.shape[1], w2.shape[2]
+    dev = offsets.device
+    if h is None:
+        h = torch.empty((max_rows, d_ff), dtype=_TORCH[dtype], device=dev)
+    if dtype == MOE_E4M3 and h_scale is None:
+        h_scale = torch.empty((max_rows, d_ff // MOE_FP8_TILE), dtype=torch.float32, device=dev)
+    if yp is None and stages & MOE_FFN_DOWN:
+        yp = torch.empty((max_rows, d), dtype=torch.float32 if dtype == MOE_F32 else torch.bfloat16,
+                         device=dev)
+    if stages & MOE_FFN_UP:
+        _need(xp, max_rows * d, "xp")
+        _need(w13, n_exp * 2 * d_ff * d, "w13")
+    if stages & MOE_FFN_DOWN:
+        _need(w2, n_exp * d * d_ff, "w2")
+        _need(yp, max_rows * d, "yp")
+    _need(h, max_rows * d_ff, "h")
+    st = lib().moe_expert_ffn(n_exp, _ptr(offsets), max_rows, d, d_ff, dtype, _ptr(xp), _ptr(xp_scale),
+                              _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(h),
+                              _ptr(h_scale), _ptr(yp), stages, _stream())
+    _lib.check("moe_expert_ffn", st)
+    return yp, h, h_scale
+
+
+def combine(sh: MoeShape, dest: torch.Tensor, topk_w: torch.Tensor, yp: torch.Tensor,
+            ysh: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+            out_dtype: Optional[int] = None, accumulate: bool = False) -> torch.Tensor:
+    T, d = sh.T, sh.d
+    y_dtype = _dt(yp)
+    if out is None:
+        out_dtype = y_dtype if out_dtype is None else out_dtype
+        out = torch.empty((T, d), dtype=_TORCH[out_dtype], device=yp.device)
+    out_dtype = _dt(out)
+    _need(out, T * d, "out")
+    _need(ysh, T * d, "ysh")
+    _need(dest, T * sh.k, "dest")
+    _need(topk_w, T * sh.k, "topk_w")
+    st = lib().moe_combine(ctypes.byref(sh), _ptr(dest), _ptr(topk_w), _ptr(yp), y_dtype, _ptr(ysh),
+                           _ptr(out), out_dtype, 1 if accumulate else 0, _stream())
+    _lib.check("moe_combine", st)
+    return out
+
+
+def quantize_blocks_e4m3(w: torch.Tensor, q=None, scale=None):
+    """fp32 [..., rows, cols] -> e4m3 codes (uint8) + fp32 128x128 block scales."""
+    rows, cols = w.shape[-2], w.shape[-1]
+    n = w.numel() // (rows * cols)
+    if q is None:
+        q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    if scale is None:
+        scale = torch.empty((*w.shape[:-2], rows // MOE_FP8_TILE, cols // MOE_FP8_TILE),
+                            dtype=torch.float32, device=w.device)
+    _need(q, w.numel(), "q")
+    _need(scale, n * (rows // MOE_FP8_TILE) * (cols // MOE_FP8_TILE), "scale")
+    st = lib().moe_quantize_blocks_e4m3(n, rows, cols, _ptr(w), _ptr(q), _ptr(scale), _stream())
+    _lib.check("moe_quantize_blocks_e4m3", st)
+    return q, scale
+
+
+from .layer import MoELayer  # noqa: E402

@@ -1,0 +1,180 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 1024;  // per moe_expert_ffn call
+constexpr int kXcds = 8;           // MI355X: 8 accelerator complex dies, 32 CUs each
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// round to nearest, ties to even (inputs are finite)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// ---------------------------------------------------------------- e4m3 (OCP E4M3FN)
+
+// Nearest e4m3 value, ties to the even code, saturating at +-448.  The sign
+// bit follows the input's sign (small negatives give -0, code 0x80).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a > 0x43E00000u) {                     // |v| > 448
+    code = 0x7Eu;
+  } else if (a < 0x3C800000u) {              // |v| < 2^-6: subnormal step 2^-9
+    float q = __builtin_rintf(__uint_as_float(a) * 512.0f);
+    code = static_cast<uint32_t>(q);         // 0..8 (8 = 2^-6, the first normal)
+  } else {
+    int e = static_cast<int>(a >> 23) - 127;  // -6..8
+    uint32_t frac = a & 0x7FFFFFu;
+    uint32_t q = frac >> 20;
+    uint32_t rem = frac & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) q += 1u;
+    code = (static_cast<uint32_t>(e + 7) << 3) + q;  // a carry moves to the next binade
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  float mag = e == 0 ? static_cast<float>(m) * 0.001953125f
+                     : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// fp32 scale of an e4m3 tile from its largest magnitude
+__device__ __forceinline__ float e4m3_tile_scale(float amax) {
+  return amax == 0.0f ? 1.0f : amax / 448.0f;
+}
+
+// ---------------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  lo = __shfl_xor(lo, mask, kWave);
+  hi = __shfl_xor(hi, mask, kWave);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- grouped tile map
+//
+// A grouped GEMM launch covers n_exp row groups (experts): group i owns rows
+// [offsets[i], offsets[i+1]).  Each group is cut into ceil(rows/BM) row tiles;
+// each row tile meets n_tiles column tiles.  Logical tiles are numbered group by
+// group, and inside a group column-tile-major with the row tiles innermost, so
+// consecutive tiles share a weight tile and a group's tiles run together.
+// Work-group w is remapped so that each XCD (w % 8) walks one contiguous slice
+// of the logical tiles: the tiles that share weights and activations then sit in
+// one XCD's L2.  Offsets live on the device; the map is rebuilt by every
+// work-group from them (a few hundred ints), so no host sync and no planning
+// kernel are needed.
+
+struct TileInfo {
+  int group;    // expert within the call
+  int m_tile;   // row tile within the group
+  int n_tile;   // column tile
+  int row0;     // first row of the tile
+  int rows;     // valid rows in the tile (1..BM)
+};
+
+// s_pre: LDS scratch of n_exp + 1 ints.  Returns false for a work-group with no
+// tile (uniform across the work-group).  Must be called by all threads.
+__device__ __forceinline__ bool map_tile(const int* __restrict__ offsets, int n_exp,
+                                         int64_t rows_total, int BM, int n_tiles, int* s_pre,
+                                         TileInfo& ti) {
+  const int tid = threadIdx.x;
+  if (offsets == nullptr) {  // one group of rows_total rows
+    n_exp = 1;
+    if (tid == 0) {
+      s_pre[0] = 0;
+      s_pre[1] = static_cast<int>((rows_total + BM - 1) / BM);
+    }
+  } else if (tid < kWave) {
+    // wave 0: per-lane chunk of consecutive groups, then a wave prefix scan
+    const int per = (n_exp + kWave - 1) / kWave;
+    const int g0 = tid * per;
+    int sum = 0;
+    for (int g = g0; g < g0 + per && g < n_exp; ++g) {
+      int n = offsets[g + 1] - offsets[g];
+      sum += (n + BM - 1) / BM;
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      int v = __shfl_up(incl, o, kWave);
+      if (tid >= o) incl += v;
+    }
+    int run = incl - sum;
+    if (tid == 0) s_pre[0] = 0;
+    for (int g = g0; g < g0 + per && g < n_exp; ++g) {
+      int n = offsets[g + 1] - offsets[g];
+      run += (n + BM - 1) / BM;
+      s_pre[g + 1] = run;
+    }
+  }
+  __syncthreads();
+  const int total = s_pre[n_exp] * n_tiles;
+  const int rr = (total + kXcds - 1) / kXcds * kXcds;
+  const int w = blockIdx.x;
+  if (w >= rr) return false;
+  const int L = (w % kXcds) * (rr / kXcds) + w / kXcds;
+  if (L >= total) return false;
+  // group g with s_pre[g]*n_tiles <= L < s_pre[g+1]*n_tiles
+  int lo = 0, hi = n_exp;  // invariant: s_pre[lo]*nt <= L < s_pre[hi]*nt
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (s_pre[mid] * n_tiles <= L) lo = mid; else hi = mid;
+  }
+  const int g = lo;
+  const int mt = s_pre[g + 1] - s_pre[g];
+  const int i = L - s_pre[g] * n_tiles;
+  ti.group = g;
+  ti.n_tile = i / mt;
+  ti.m_tile = i % mt;
+  const int base = offsets == nullptr ? 0 : offsets[g];
+  const int end = offsets == nullptr ? static_cast<int>(rows_total) : offsets[g + 1];
+  ti.row0 = base + ti.m_tile * BM;
+  ti.rows = min(BM, end - ti.row0);
+  return true;
+}
+
+// upper bound on the row tiles of a grouped launch
+inline int64_t max_row_tiles(int64_t max_rows, int n_exp, int BM) {
+  return (max_rows + BM - 1) / BM + (n_exp > 1 ? n_exp : 0);
+}
+
+}  // namespace moe

@@ -1,0 +1,59 @@
+// Host-side launchers of the gfx950 kernels (internal to the library; the C
+// ABI in moe.h checks arguments and calls these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// gate logits
+hipError_t launch_gate_gemm_bf16(const uint16_t* x, const uint16_t* w_prep, float* logits,
+                                 int64_t T, int d, int E, hipStream_t s);
+hipError_t launch_gate_gemm_simt(const void* x, int x_dtype, const uint16_t* w_prep,
+                                 float* logits, int64_t T, int d, int E, hipStream_t s);
+bool gate_gemm_bf16_supported(int d, int E);
+
+// selection + block histogram
+hipError_t launch_route_select(const float* logits, const float* bias, const float* offset,
+                               int32_t* idx, float* w, int32_t* block_counts, int64_t T, int E,
+                               int G, int M, int k, int gk, hipStream_t s);
+bool route_select_supported(int E, int G, int k, int gk);
+
+// dispatch
+hipError_t launch_dispatch(const int32_t* idx, const int32_t* block_counts, int64_t T, int k,
+                           int E, int e_begin, int e_end, const void* x, int x_dtype,
+                           int out_dtype, int d, int32_t* counts, int32_t* offsets,
+                           int32_t* dest, int32_t* src, void* xp, float* xp_scale, int32_t* base,
+                           hipStream_t s);
+
+// grouped expert FFN
+hipError_t launch_ffn_up_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
+                              int d_ff, const uint16_t* xp, const uint16_t* w13, uint16_t* h,
+                              hipStream_t s);
+hipError_t launch_ffn_down_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
+                                int d_ff, const uint16_t* h, const uint16_t* w2, uint16_t* yp,
+                                hipStream_t s);
+hipError_t launch_ffn_simt(int stage, int n_exp, const int32_t* offsets, int64_t max_rows, int d,
+                           int d_ff, int dtype, const void* in, const void* w, void* out,
+                           hipStream_t s);
+hipError_t launch_ffn_up_fp8(int n_exp, const int32_t* offsets, int64_t max_rows, int d, int d_ff,
+                             const uint8_t* xp, const float* xp_scale, const uint8_t* w13,
+                             const float* w13_scale, uint8_t* h, float* h_scale, hipStream_t s);
+hipError_t launch_ffn_down_fp8(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
+                               int d_ff, const uint8_t* h, const float* h_scale,
+                               const uint8_t* w2, const float* w2_scale, uint16_t* yp,
+                               hipStream_t s);
+
+// combine
+hipError_t launch_combine(int64_t T, int k, int d, const int32_t* dest, const float* w,
+                          const void* yp, int y_dtype, const void* ysh, void* out,
+                          int out_dtype, int accumulate, hipStream_t s);
+
+// weight preparation
+hipError_t launch_gate_prepare(int d, int E, const float* w_gate, uint16_t* w_prep,
+                               hipStream_t s);
+hipError_t launch_quantize_blocks(int64_t n, int rows, int cols, const float* w, uint8_t* q,
+                                  float* scale, hipStream_t s);
+
+}  // namespace moe

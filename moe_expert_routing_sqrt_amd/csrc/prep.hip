@@ -1,0 +1,92 @@
+// Weight preparation kernels (run once per weight load, not per step).
+//
+//  gate_prepare     fp32 W_g [d, E] -> three bf16 planes [3, E, d] with
+//                   hi + mid + lo == W exactly: hi = bf16(w), mid = bf16(w - hi),
+//                   lo = bf16(w - hi - mid).  Each residual is exact in fp32
+//                   and fits the next plane's 8 significant bits, so the gate
+//                   product can run on bf16 matrix cores with exact products
+//                   (the router stays out of low precision: deepnotes "The
+//                   iteration loop").
+//  quantize_blocks  fp32 [n, R, C] -> e4m3 codes with one fp32 scale per
+//                   128 x 128 block (the fp8 workload's weight format).
+#pragma clang fp contract(off)
+
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void gate_prepare_kernel(int d, int E, const float* __restrict__ w,
+                                                           uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over E*d, d fastest
+  if (i >= (int64_t)E * d) return;
+  const int e = static_cast<int>(i / d), kk = static_cast<int>(i % d);
+  const float v = w[(int64_t)kk * E + e];
+  const uint16_t hi = f32_to_bf16(v);
+  const float r1 = v - bf16_to_f32(hi);
+  const uint16_t mid = f32_to_bf16(r1);
+  const float r2 = r1 - bf16_to_f32(mid);
+  const uint16_t lo = f32_to_bf16(r2);
+  const int64_t plane = (int64_t)E * d;
+  out[i] = hi;
+  out[plane + i] = mid;
+  out[2 * plane + i] = lo;
+}
+
+constexpr int kBlk = MOE_FP8_TILE;
+
+__global__ __launch_bounds__(256) void quantize_blocks_kernel(int rows, int cols,
+                                                              const float* __restrict__ w,
+                                                              uint8_t* __restrict__ q,
+                                                              float* __restrict__ scale) {
+  __shared__ float s_red[4];
+  const int rb = rows / kBlk, cb = cols / kBlk;
+  const int64_t blk = blockIdx.x;
+  const int64_t mat = blk / ((int64_t)rb * cb);
+  const int br = static_cast<int>((blk / cb) % rb), bc = static_cast<int>(blk % cb);
+  const float* base = w + mat * rows * (int64_t)cols + (int64_t)br * kBlk * cols + bc * kBlk;
+  uint8_t* qbase = q + mat * rows * (int64_t)cols + (int64_t)br * kBlk * cols + bc * kBlk;
+  const int tid = threadIdx.x;
+  float amax = 0.0f;
+  for (int i = tid; i < kBlk * kBlk / 4; i += 256) {
+    const int r = i / (kBlk / 4), c4 = i % (kBlk / 4);
+    const float4 v = reinterpret_cast<const float4*>(base + (int64_t)r * cols)[c4];
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+  if ((tid & 63) == 0) s_red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  const float sc = e4m3_tile_scale(amax);
+  if (tid == 0) scale[blk] = sc;
+  for (int i = tid; i < kBlk * kBlk / 4; i += 256) {
+    const int r = i / (kBlk / 4), c4 = i % (kBlk / 4);
+    const float4 v = reinterpret_cast<const float4*>(base + (int64_t)r * cols)[c4];
+    const uint32_t packed = f32_to_e4m3(v.x / sc) | (f32_to_e4m3(v.y / sc) << 8) |
+                            (f32_to_e4m3(v.z / sc) << 16) | (f32_to_e4m3(v.w / sc) << 24);
+    reinterpret_cast<uint32_t*>(qbase + (int64_t)r * cols)[c4] = packed;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gate_prepare(int d, int E, const float* w_gate, uint16_t* w_prep,
+                               hipStream_t s) {
+  const int64_t n = (int64_t)E * d;
+  hipLaunchKernelGGL(gate_prepare_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, d, E,
+                     w_gate, w_prep);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_blocks(int64_t n, int rows, int cols, const float* w, uint8_t* q,
+                                  float* scale, hipStream_t s) {
+  const int64_t nb = n * (rows / kBlk) * (cols / kBlk);
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_blocks_kernel, dim3((unsigned)nb), dim3(256), 0, s, rows, cols, w, q,
+                     scale);
+  return hipGetLastError();
+}
+
+}  // namespace moe

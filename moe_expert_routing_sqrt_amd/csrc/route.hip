@@ -1,0 +1,257 @@
+// Routing on gfx950: affinities, bias-adjusted node-limited top-k, gate
+// weights and the per-block expert histogram (mastering-deepseek-v4 "MoE +
+// Expert-Parallel Overlap (Exp08)", Implemented: Sqrt(Softplus) affinities,
+// top-k gating, per-expert bias; zenaique "MoE node-limited routing": a
+// token's experts span at most M nodes).
+//
+// One wave64 per token.  Lane l holds experts [l*EPL, (l+1)*EPL) (EPL =
+// ceil(E/64)), so a group of E/G consecutive experts is an aligned run of
+// lanes and group reductions are xor-butterflies inside the run.  Orderings use
+// 64-bit keys (ordered fp32 bits << 32 | ~index): the largest key is the
+// largest value, ties to the lower index.
+//
+// Every floating-point value is produced by one fixed fp32 operation sequence
+// with no contraction (this file is compiled with -ffp-contract=off,
+// correctly rounded divide and sqrt, and fp32 denormals kept), so the result
+// is a deterministic function of the fp32 logits:
+//   softplus(l) = max(l,0) + log1p(exp(-|l|))
+//   exp(-a): Cody & Waite 1980 range reduction (ln2 split in two), degree-7
+//            Taylor polynomial in Horner form, ldexp; 0 for a > 87
+//   log1p(u): Goldberg 1991 Thm 4 (w = 1+u; u if w == 1 else
+//            log(w)*u/(w-1)); log(w) by frexp into [sqrt(1/2), sqrt(2)) and
+//            2*atanh((m-1)/(m+1)) to the f^11 term, plus e*ln2 in two parts
+//   s = sqrt(softplus(l));  b = s + bias
+//   group score = its group_topk largest b added largest first;
+//   keep the M best groups (ties to the lower group), choose the k best b in
+//   them (ties to the lower expert), w_j = s_j / (((s_0 + s_1) + s_2) + ...).
+#pragma clang fp contract(off)
+
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr float kInvLn2 = 1.44269502162933349609375f;
+constexpr float kLn2Hi = 0.693359375f;
+constexpr float kLn2Lo = -0.000212194441701285541057586669922f;
+constexpr float kSqrtHalf = 0.707106769084930419921875f;
+constexpr float kExpCutoff = 87.0f;
+
+__device__ __forceinline__ float exp_neg_spec(float a) {
+  const float ac = a > kExpCutoff ? 0.0f : a;
+  const float n = __builtin_rintf(ac * kInvLn2);
+  const float r = (n * kLn2Hi - ac) + n * kLn2Lo;
+  float p = 1.0f / 5040.0f;
+  p = p * r + 1.0f / 720.0f;
+  p = p * r + 1.0f / 120.0f;
+  p = p * r + 1.0f / 24.0f;
+  p = p * r + 1.0f / 6.0f;
+  p = p * r + 1.0f / 2.0f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  const float res = ldexpf(p, -static_cast<int>(n));
+  return a > kExpCutoff ? 0.0f : res;
+}
+
+__device__ __forceinline__ float log1p_spec(float u) {
+  const float w = u + 1.0f;
+  if (w == 1.0f) return u;
+  int e;
+  float m = frexpf(w, &e);
+  if (m < kSqrtHalf) {
+    m = m * 2.0f;
+    e = e - 1;
+  }
+  const float f = (m - 1.0f) / (m + 1.0f);
+  const float f2 = f * f;
+  float q = 2.0f / 11.0f;
+  q = q * f2 + 2.0f / 9.0f;
+  q = q * f2 + 2.0f / 7.0f;
+  q = q * f2 + 2.0f / 5.0f;
+  q = q * f2 + 2.0f / 3.0f;
+  q = q * f2 + 2.0f;
+  const float logm = f * q;
+  const float ef = static_cast<float>(e);
+  const float logw = ef * kLn2Hi + (logm + ef * kLn2Lo);
+  return (logw * u) / (w - 1.0f);
+}
+
+__device__ __forceinline__ float affinity_spec(float l) {
+  const float pos = l > 0.0f ? l : 0.0f;
+  const float sp = pos + log1p_spec(exp_neg_spec(fabsf(l)));
+  return sqrtf(sp);
+}
+
+__device__ __forceinline__ uint64_t make_key(float v, int idx) {
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(u) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(idx));
+}
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+  uint32_t u = static_cast<uint32_t>(key >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ int key_index(uint64_t key) {
+  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+}
+
+constexpr int kTokPerBlock = MOE_ROUTE_BLOCK;
+constexpr int kWavesPerWg = 8;
+
+struct RouteArgs {
+  const float* logits;
+  const float* bias;
+  const float* offset;
+  int32_t* idx;
+  float* w;
+  int32_t* block_counts;
+  int64_t T;
+  int E, G, M, k, gk;
+};
+
+template <int EPL>
+__global__ __launch_bounds__(kWavesPerWg * kWave) void route_select_kernel(const RouteArgs p) {
+  __shared__ int s_cnt[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < p.E; e += blockDim.x) s_cnt[e] = 0;
+  __syncthreads();
+
+  const int E = p.E;
+  const int gsz = E / p.G;
+  const int lpg = gsz / EPL;          // lanes per group (power of two)
+  const int e0 = lane * EPL;
+  const bool lane_ok = e0 < E;
+  const int my_group = lane_ok ? e0 / gsz : 0;
+  float bias_l[EPL], off_l[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    bias_l[i] = lane_ok ? p.bias[e0 + i] : 0.0f;
+    off_l[i] = (lane_ok && p.offset != nullptr) ? p.offset[e0 + i] : 0.0f;
+  }
+
+  const int64_t t_begin = (int64_t)blockIdx.x * kTokPerBlock;
+  for (int tt = wave; tt < kTokPerBlock; tt += kWavesPerWg) {
+    const int64_t t = t_begin + tt;
+    if (t >= p.T) break;
+    float s[EPL], b[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      float l = lane_ok ? p.logits[t * E + e0 + i] : 0.0f;
+      if (p.offset != nullptr) l = l + off_l[i];
+      s[i] = affinity_spec(l);
+      float bb = s[i] + bias_l[i];
+      b[i] = bb == 0.0f ? 0.0f : bb;  // one zero: +0
+    }
+
+    // group score: the gk largest b of the group, added largest first
+    bool used[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) used[i] = false;
+    float gscore = 0.0f;
+    for (int r = 0; r < p.gk; ++r) {
+      uint64_t key = 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        uint64_t kk = (lane_ok && !used[i]) ? make_key(b[i], e0 + i) : 0;
+        key = kk > key ? kk : key;
+      }
+      for (int m = 1; m < lpg; m <<= 1) {
+        uint64_t o = shfl_xor_u64(key, m);
+        key = o > key ? o : key;
+      }
+      const float v = key_value(key);
+      gscore = r == 0 ? v : gscore + v;
+      const int win = key_index(key);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) used[i] = used[i] || (e0 + i == win);
+    }
+
+    // keep the M best groups
+    uint64_t gkey = lane_ok ? make_key(gscore, my_group) : 0;
+    bool gsel = false;
+    for (int r = 0; r < p.M; ++r) {
+      const uint64_t m = wave_max_u64(gkey);
+      if (lane_ok && gkey == m) {
+        gsel = true;
+        gkey = 0;
+      }
+    }
+
+    // k best experts inside the kept groups
+    bool taken[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) taken[i] = false;
+    float S = 0.0f, my_s = 0.0f;
+    int my_idx = 0;
+    for (int j = 0; j < p.k; ++j) {
+      uint64_t key = 0;
+      float best_s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        uint64_t kk = (gsel && !taken[i]) ? make_key(b[i], e0 + i) : 0;
+        if (kk > key) {
+          key = kk;
+          best_s = s[i];
+        }
+      }
+      const uint64_t m = wave_max_u64(key);
+      const int win = key_index(m);
+      const int owner = win / EPL;
+      const float s_win = __shfl(best_s, owner, kWave);
+      if (lane == owner) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) taken[i] = taken[i] || (e0 + i == win);
+      }
+      S = j == 0 ? s_win : S + s_win;
+      if (lane == j) {
+        my_idx = win;
+        my_s = s_win;
+      }
+    }
+    if (lane < p.k) {
+      p.idx[t * p.k + lane] = my_idx;
+      p.w[t * p.k + lane] = my_s / S;
+      if (my_idx >= 0 && my_idx < E) atomicAdd(&s_cnt[my_idx], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) p.block_counts[(int64_t)blockIdx.x * E + e] = s_cnt[e];
+}
+
+template <int EPL>
+hipError_t launch_sel(const RouteArgs& a, hipStream_t s) {
+  const int64_t nblk = (a.T + kTokPerBlock - 1) / kTokPerBlock;
+  hipLaunchKernelGGL(route_select_kernel<EPL>, dim3((unsigned)nblk), dim3(kWavesPerWg * kWave), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool route_select_supported(int E, int G, int k, int gk) {
+  if (E > 256 || (E > 64 && E % 64 != 0)) return false;
+  const int epl = (E + 63) / 64;
+  const int gsz = E / G;
+  if (gsz % epl != 0) return false;
+  const int lpg = gsz / epl;
+  if ((lpg & (lpg - 1)) != 0) return false;
+  return gk <= 4 && k <= 16;
+}
+
+hipError_t launch_route_select(const float* logits, const float* bias, const float* offset,
+                               int32_t* idx, float* w, int32_t* block_counts, int64_t T, int E,
+                               int G, int M, int k, int gk, hipStream_t s) {
+  RouteArgs a{logits, bias, offset, idx, w, block_counts, T, E, G, M, k, gk};
+  switch ((E + 63) / 64) {
+    case 1: return launch_sel<1>(a, s);
+    case 2: return launch_sel<2>(a, s);
+    case 3: return launch_sel<3>(a, s);
+    default: return launch_sel<4>(a, s);
+  }
+}
+
+}  // namespace moe

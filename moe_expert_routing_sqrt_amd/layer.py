@@ -1,0 +1,114 @@
+"""MoELayer: one MoE layer forward on one GPU, weights resident and every
+buffer allocated once, so forward() only enqueues the library's kernels.
+
+forward(x) = moe_route -> moe_dispatch -> moe_expert_ffn (routed: up, down)
+             -> moe_expert_ffn (shared expert) -> moe_combine
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from . import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN, MOE_FFN_UP, MOE_FP8_TILE,
+               combine, dispatch, expert_ffn, gate_prepare, n_blocks, quantize_blocks_e4m3, route,
+               shape)
+
+STAGES = ("route", "dispatch", "ffn_up", "ffn_down", "shared", "combine")
+
+
+class MoELayer:
+    def __init__(self, T: int, d: int, E: int, G: int, M: int, k: int, d_ff: int, dtype: str,
+                 w_gate: torch.Tensor, bias: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor,
+                 sh_w13: Optional[torch.Tensor] = None, sh_w2: Optional[torch.Tensor] = None,
+                 logit_offset: Optional[torch.Tensor] = None, e_begin: int = 0,
+                 e_end: Optional[int] = None, group_topk: Optional[int] = None):
+        dev = bias.device
+        self.sh = shape(T, d, E, G, M, k, d_ff, group_topk)
+        self.T, self.d, self.E, self.k, self.d_ff = T, d, E, k, d_ff
+        self.e_begin, self.e_end = e_begin, (E if e_end is None else e_end)
+        self.local = (self.e_begin, self.e_end) != (0, E)
+        self.dtype = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_E4M3}[dtype]
+        self.bias = bias
+        self.logit_offset = logit_offset
+        self.w_prep = gate_prepare(w_gate)
+
+        # expert weights in the compute format (fp8: e4m3 codes + 128x128 block scales)
+        if self.dtype == MOE_E4M3:
+            self.w13, self.w13_s = quantize_blocks_e4m3(w13)
+            self.w2, self.w2_s = quantize_blocks_e4m3(w2)
+            if sh_w13 is not None:
+                self.sh_w13, self.sh_w13_s = quantize_blocks_e4m3(sh_w13)
+                self.sh_w2, self.sh_w2_s = quantize_blocks_e4m3(sh_w2)
+        else:
+            self.w13, self.w2, self.w13_s, self.w2_s = w13, w2, None, None
+            self.sh_w13, self.sh_w2 = sh_w13, sh_w2
+            self.sh_w13_s = self.sh_w2_s = None
+        self.has_shared = sh_w13 is not None and not self.local
+
+        act = torch.float32 if self.dtype == MOE_F32 else torch.bfloat16
+        store = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.uint8}[self.dtype]
+        rows = T * k
+        self.max_rows = rows
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.block_counts = torch.empty((n_blocks(T), E), dtype=torch.int32, device=dev)
+        self.dbufs = None
+        self.h = torch.empty((rows, d_ff), dtype=store, device=dev)
+        self.h_s = (torch.empty((rows, d_ff // MOE_FP8_TILE), dtype=torch.float32, device=dev)
+                    if self.dtype == MOE_E4M3 else None)
+        self.yp = torch.empty((rows, d), dtype=act, device=dev)
+        if self.has_shared:
+            self.sh_offsets = torch.tensor([0, T], dtype=torch.int32, device=dev)
+            self.sh_h = torch.empty((T, d_ff), dtype=store, device=dev)
+            self.sh_h_s = (torch.empty((T, d_ff // MOE_FP8_TILE), dtype=torch.float32, device=dev)
+                           if self.dtype == MOE_E4M3 else None)
+            self.ysh = torch.empty((T, d), dtype=act, device=dev)
+            if self.dtype == MOE_E4M3:
+                self.sh_xq = torch.empty((T, d), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((T, d), dtype=torch.float32 if self.local else act, device=dev)
+
+    def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                marks: Optional[Sequence[torch.cuda.Event]] = None) -> torch.Tensor:
+        """One layer forward.  `marks`: optional 7 events recorded on the current
+        stream around the six stages (STAGES)."""
+        def mark(i):
+            if marks is not None:
+                marks[i].record()
+
+        sh = self.sh
+        mark(0)
+        route(sh, x, self.w_prep, self.bias, self.logit_offset, logits=self.logits, idx=self.idx,
+              w=self.topk_w, block_counts=self.block_counts)
+        mark(1)
+        self.dbufs = dispatch(sh, self.idx, self.block_counts, x, self.e_begin, self.e_end,
+                              out_dtype=self.dtype if self.dtype == MOE_E4M3 else None,
+                              bufs=self.dbufs)
+        b = self.dbufs
+        mark(2)
+        expert_ffn(b["offsets"], self.max_rows, b["xp"], self.w13, self.w2, self.dtype,
+                   xp_scale=b["xp_scale"], w13_scale=self.w13_s, w2_scale=self.w2_s, h=self.h,
+                   h_scale=self.h_s, yp=self.yp, stages=MOE_FFN_UP)
+        mark(3)
+        expert_ffn(b["offsets"], self.max_rows, b["xp"], self.w13, self.w2, self.dtype,
+                   xp_scale=b["xp_scale"], w13_scale=self.w13_s, w2_scale=self.w2_s, h=self.h,
+                   h_scale=self.h_s, yp=self.yp, stages=MOE_FFN_DOWN)
+        mark(4)
+        ysh = None
+        if self.has_shared:
+            xs, xs_scale = x, None
+            if self.dtype == MOE_E4M3:
+                xs, xs_scale = self._shared_quant_input(x)
+            expert_ffn(self.sh_offsets, self.T, xs, self.sh_w13, self.sh_w2, self.dtype,
+                       xp_scale=xs_scale, w13_scale=self.sh_w13_s, w2_scale=self.sh_w2_s,
+                       h=self.sh_h, h_scale=self.sh_h_s, yp=self.ysh, stages=MOE_FFN_ALL)
+            ysh = self.ysh
+        mark(5)
+        out = self.out if out is None else out
+        combine(sh, b["dest"], self.topk_w, self.yp, ysh, out=out, accumulate=self.local)
+        mark(6)
+        return out
+
+    def _shared_quant_input(self, x):
+        raise NotImplementedError("fp8 shared expert input quantisation")

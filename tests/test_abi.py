@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/moe.h declares, its constants match the header, and bad arguments are
+rejected on the host before anything is launched."""
+import ctypes
+import re
+
+import pytest
+
+from moe_expert_routing_sqrt_amd import _lib
+
+L = _lib.load()
+
+
+def test_exports_every_declared_function():
+    names = _lib.header_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in _lib.SIGNATURES, f"binding lacks a signature for {n}"
+    assert sorted(_lib.SIGNATURES) == names
+
+
+def test_constants_match_header():
+    text = open(_lib.HEADER).read()
+    defs = dict(re.findall(r"#define\s+(MOE_\w+)\s+\(?(-?\d+)\)?", text))
+    for name, val in defs.items():
+        if hasattr(_lib, name):
+            assert getattr(_lib, name) == int(val), name
+    assert L.moe_abi_version() == int(defs["MOE_ABI_VERSION"])
+
+
+def test_shape_struct_layout():
+    assert ctypes.sizeof(_lib.MoeShape) == 8 + 7 * 4 + 4  # int64 + 7 int32, padded to 8
+    assert _lib.MoeShape.d.offset == 8
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4):
+        assert L.moe_status_str(st)
+    assert L.moe_status_str(99) == b"unknown status"
+
+
+def _sh(T=16, d=64, E=16, G=4, M=2, k=4, gk=2, d_ff=32):
+    return _lib.MoeShape(T, d, E, G, M, k, gk, d_ff)
+
+
+FAKE = 0x1000  # never dereferenced: every case below fails its host-side check
+
+
+@pytest.mark.parametrize("bad", [
+    dict(E=15), dict(G=0), dict(M=5), dict(k=9), dict(gk=5), dict(T=-1), dict(d=0), dict(d_ff=0),
+    dict(E=16, G=4, M=1, k=5),
+])
+def test_route_rejects_bad_shapes(bad):
+    sh = _sh(**bad)
+    st = L.moe_route(ctypes.byref(sh), FAKE, _lib.MOE_BF16, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None)
+    assert st == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_route_rejects_null_and_flags():
+    sh = _sh()
+    assert L.moe_route(None, FAKE, 1, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
+    assert L.moe_route(ctypes.byref(sh), FAKE, 1, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
+    assert L.moe_route(ctypes.byref(sh), None, 1, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
+    assert L.moe_route(ctypes.byref(sh), FAKE, 1, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, None) == -1
+    assert L.moe_route(ctypes.byref(sh), FAKE, 7, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
+
+
+def test_route_unsupported_and_empty():
+    sh = _sh(E=320, G=5, M=2, k=4, gk=2)
+    assert L.moe_route(ctypes.byref(sh), FAKE, 1, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == -2
+    sh0 = _sh(T=0)
+    assert L.moe_route(ctypes.byref(sh0), FAKE, 1, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == 0
+
+
+def test_dispatch_checks():
+    sh = _sh()
+    ws = L.moe_dispatch_workspace_size(ctypes.byref(sh), 0, 16)
+    assert ws == 1 * 16 * 4
+    assert L.moe_dispatch_workspace_size(ctypes.byref(sh), 4, 2) == 0
+    args = lambda eb, ee, xdt, odt, scale, wsb: (ctypes.byref(sh), FAKE, FAKE, eb, ee, FAKE, xdt, odt, FAKE,
+                                                FAKE, FAKE, FAKE, FAKE, scale, FAKE, wsb, None)
+    assert L.moe_dispatch(*args(0, 17, 1, 1, None, ws)) == -1
+    assert L.moe_dispatch(*args(3, 3, 1, 1, None, ws)) == -1
+    assert L.moe_dispatch(*args(0, 16, 1, 1, None, ws - 1)) == -3
+    assert L.moe_dispatch(*args(0, 16, 1, 2, None, ws)) == -1          # e4m3 needs scales
+    assert L.moe_dispatch(*args(0, 16, 0, 2, FAKE, ws)) == -2          # e4m3 from f32 x
+    assert L.moe_dispatch(*args(0, 16, 1, 0, None, ws)) == -2          # bf16 -> f32 repack
+    sh0 = _sh(T=0)
+    assert L.moe_dispatch(ctypes.byref(sh0), FAKE, FAKE, 0, 16, FAKE, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                          None, FAKE, 0, None) == 0
+
+
+def test_expert_ffn_checks():
+    f = L.moe_expert_ffn
+    assert f(0, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3, None) == -1
+    assert f(2000, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3, None) == -1
+    assert f(4, None, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3, None) == -1
+    assert f(4, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 0, None) == -1
+    assert f(4, FAKE, 10, 64, 32, 1, None, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 1, None) == -1
+    assert f(4, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, None, None, FAKE, None, FAKE, 2, None) == -1
+    assert f(4, FAKE, 10, 256, 128, 2, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3, None) == -1
+    assert f(4, FAKE, 10, 200, 128, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, None) == -2
+    assert f(4, FAKE, 0, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3, None) == 0
+
+
+def test_combine_checks():
+    sh = _sh()
+    c = L.moe_combine
+    assert c(ctypes.byref(sh), None, FAKE, FAKE, 1, None, FAKE, 1, 0, None) == -1
+    assert c(ctypes.byref(sh), FAKE, FAKE, FAKE, 2, None, FAKE, 1, 0, None) == -1
+    assert c(ctypes.byref(sh), FAKE, FAKE, FAKE, 1, None, FAKE, 1, 1, None) == -2   # += needs f32 out
+    assert c(ctypes.byref(sh), FAKE, FAKE, FAKE, 1, None, FAKE, 0, 2, None) == -1
+    sh0 = _sh(T=0)
+    assert c(ctypes.byref(sh0), FAKE, FAKE, FAKE, 1, None, FAKE, 1, 0, None) == 0
+
+
+def test_prep_checks():
+    assert L.moe_gate_prepare(0, 16, FAKE, FAKE, None) == -1
+    assert L.moe_gate_prepare(64, 16, None, FAKE, None) == -1
+    assert L.moe_quantize_blocks_e4m3(1, 100, 128, FAKE, FAKE, FAKE, None) == -2
+    assert L.moe_quantize_blocks_e4m3(1, 128, 128, None, FAKE, FAKE, None) == -1
+    assert L.moe_quantize_blocks_e4m3(0, 128, 128, FAKE, FAKE, FAKE, None) == 0
