@@ -8,8 +8,10 @@
 // 32x32 accumulators fed by v_mfma_f32_32x32x16_bf16 (fp32 accumulate).
 // Operands stage through LDS in 128-byte rows (64 bf16 of K) whose 16-byte
 // chunks are XOR-swizzled by row, so the 32 rows a wave reads for one MFMA
-// operand spread over all banks.  Global loads for step k+1 are issued before
-// the MFMAs of step k (register prefetch, one LDS buffer, two barriers/step).
+// operand spread over all banks.  Tiles reach LDS by direct-to-LDS DMA
+// (global_load_lds_dwordx4, no register staging) through a three-stage ring:
+// the loads for step k+2 are in flight while step k computes, with one
+// barrier per step.
 //
 // Epilogues
 //   SWIGLU  (up projection of the SwiGLU expert, mastering-deepseek-v4 Exp08,
@@ -52,19 +54,77 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
+// left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Work-group barrier without the memory fence __syncthreads() carries: the
+// fence would wait for every outstanding global load, including the LDS DMA of
+// later pipeline stages.  Callers wait for exactly what they need first.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// N 16-byte LDS reads in one asm block that also waits for them: the LDS reads
+// are then invisible to the compiler's memory-counter bookkeeping, which would
+// otherwise treat every in-flight DMA of later stages as a possible writer of
+// the stage being read and wait for all of them.  The wait inside the block
+// means no output register is handed back while its load is still in flight.
+template <int N>
+__device__ __forceinline__ void lds_read(uint4 (&v)[N], const uint32_t (&a)[N]) {
+  if constexpr (N == 2) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]) : "v"(a[0]), "v"(a[1]) : "memory");
+  } else if constexpr (N == 3) {
+    asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]) : "v"(a[0]), "v"(a[1]), "v"(a[2]) : "memory");
+  } else if constexpr (N == 4) {
+    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
+                 "ds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]) : "memory");
+  } else if constexpr (N == 6) {
+    asm volatile("ds_read_b128 %0, %6\n\tds_read_b128 %1, %7\n\tds_read_b128 %2, %8\n\t"
+                 "ds_read_b128 %3, %9\n\tds_read_b128 %4, %10\n\tds_read_b128 %5, %11\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]) : "memory");
+  } else {
+    static_assert(N == 2, "unsupported fragment count");
+  }
+}
+
 template <int BM, int BN, int WAVES_M, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(const GemmArgs p) {
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
   constexpr int RM = TM / 32, RN = TN / 32;
-  constexpr int AC = BM * 8 / kThreads;  // 16-byte chunks per thread per K step
-  constexpr int BC = BN * 8 / kThreads;
+  constexpr int ADMA = BM / 32;  // 1 KB (8-row) LDS blocks per wave per K step
+  constexpr int BDMA = BN / 32;
+  constexpr int DMA_PER_STEP = ADMA + BDMA;
   constexpr int PLANES = MODE == MODE_GATE3 ? 3 : 1;
-  static_assert(RM >= 1 && RN >= 1 && AC >= 1 && BC >= 1, "tile too small");
+  static_assert(RM >= 1 && RN >= 1 && ADMA >= 1 && BDMA >= 1, "tile too small");
   static_assert(MODE != MODE_SWIGLU || RN % 2 == 0, "gate/up blocks come in pairs");
 
-  __shared__ uint4 sA[BM * 8];
-  __shared__ uint4 sB[BN * 8];
+  // three pipeline stages, each its own LDS object so the compiler can tell the
+  // DMA into one stage from the reads of another
+  __shared__ uint4 sA0[BM * 8], sA1[BM * 8], sA2[BM * 8];
+  __shared__ uint4 sB0[BN * 8], sB1[BN * 8], sB2[BN * 8];
   __shared__ int s_pre[kMaxExperts + 1];
 
   TileInfo ti;
@@ -75,16 +135,26 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(const GemmArgs p
   const int wave = tid >> 6;
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
-  const int r0 = tid >> 3;  // first tile row this thread loads
-  const int ch = tid & 7;   // 16-byte chunk within the 128-byte K slice
 
-  // global source rows of this thread's chunks (row r0 + 32*c)
-  const uint16_t* a_src = p.A + (int64_t)ti.row0 * p.lda + ch * 8;
-  const uint16_t* b_src[BC];
-  const uint16_t* bg = p.B + (int64_t)ti.group * p.b_group_stride + ch * 8;
+  // Direct-to-LDS loads: one instruction moves 64 lanes x 16 B into 1 KB of
+  // LDS at lane*16, i.e. 8 rows of 128 B.  The LDS layout is row-major with the
+  // 16-byte chunks of a row XOR-swizzled by (row & 7); since the LDS slot of a
+  // lane is fixed, the swizzle is applied to the global address instead: the
+  // lane filling physical chunk pc of row r fetches logical chunk pc ^ (r & 7).
+  const int lrow = lane >> 3;                  // row within the 8-row block
+  const int lch = (lane & 7) ^ (lrow & 7);     // logical chunk this lane fetches
+  const uint16_t* a_src[ADMA];
+  const uint16_t* b_src[BDMA];
 #pragma unroll
-  for (int c = 0; c < BC; ++c) {
-    const int r = r0 + 32 * c;
+  for (int i = 0; i < ADMA; ++i) {
+    const int r = (wave + 4 * i) * 8 + lrow;
+    const int rc = r < ti.rows ? r : ti.rows - 1;  // padding rows: any valid row
+    a_src[i] = p.A + (int64_t)(ti.row0 + rc) * p.lda + lch * 8;
+  }
+  const uint16_t* bg = p.B + (int64_t)ti.group * p.b_group_stride + lch * 8;
+#pragma unroll
+  for (int i = 0; i < BDMA; ++i) {
+    const int r = (wave + 4 * i) * 8 + lrow;
     int grow;
     if constexpr (MODE == MODE_SWIGLU) {
       const int part = r / TN, within = r % TN;
@@ -93,33 +163,22 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(const GemmArgs p
     } else {
       grow = ti.n_tile * BN + r;
     }
-    b_src[c] = bg + (int64_t)grow * p.K;
+    b_src[i] = bg + (int64_t)grow * p.K;
   }
 
-  uint4 ra[AC], rb[BC];
   const int nkp = p.K / BK;
   const int nsteps = PLANES * nkp;
 
-  auto gload = [&](int kt) {
+  auto issue = [&](int kt, uint4* sa, uint4* sb) {
     const int plane = PLANES == 1 ? 0 : kt / nkp;
     const int k0 = (kt - plane * nkp) * BK;
 #pragma unroll
-    for (int c = 0; c < AC; ++c) {
-      const int r = r0 + 32 * c;
-      if (r < ti.rows)
-        ra[c] = *reinterpret_cast<const uint4*>(a_src + (int64_t)(32 * c) * p.lda + k0);
-      else
-        ra[c] = make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < ADMA; ++i)
+      __builtin_amdgcn_global_load_lds(a_src[i] + k0, (lds_ptr_t)(sa + (wave + 4 * i) * 64), 16, 0, 0);
+    const int64_t boff = (int64_t)plane * p.b_plane_stride + k0;
 #pragma unroll
-    for (int c = 0; c < BC; ++c)
-      rb[c] = *reinterpret_cast<const uint4*>(b_src[c] + (int64_t)plane * p.b_plane_stride + k0);
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int c = 0; c < AC; ++c) sA[swz(r0 + 32 * c, ch)] = ra[c];
-#pragma unroll
-    for (int c = 0; c < BC; ++c) sB[swz(r0 + 32 * c, ch)] = rb[c];
+    for (int i = 0; i < BDMA; ++i)
+      __builtin_amdgcn_global_load_lds(b_src[i] + boff, (lds_ptr_t)(sb + (wave + 4 * i) * 64), 16, 0, 0);
   };
 
   f32x16 acc[RM][RN];
@@ -130,30 +189,62 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(const GemmArgs p
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  gload(0);
-  sstore();
-  __syncthreads();
-  for (int kt = 0; kt < nsteps; ++kt) {
-    if (kt + 1 < nsteps) gload(kt + 1);
+  // Fragment addresses: row r of an operand tile is 128 bytes, chunk c of it
+  // sits at (c ^ (r & 7)) * 16; rows used by a lane are lane%32 plus multiples
+  // of 8, so the swizzle term depends on the lane only.
+  constexpr int NF = RM + RN;
+  uint32_t frag_off[NF];
+#pragma unroll
+  for (int i = 0; i < RM; ++i) frag_off[i] = (wm * TM + i * 32 + (lane & 31)) * 128;
+#pragma unroll
+  for (int j = 0; j < RN; ++j) frag_off[RM + j] = (wn * TN + j * 32 + (lane & 31)) * 128;
+  const int sw = lane & 7, khalf = lane >> 5;
+
+  auto compute = [&](const uint4* sa, const uint4* sb) {
+    const uint32_t a_base = lds_addr(sa), b_base = lds_addr(sb);
+    uint4 fr[2][NF];
+    auto read = [&](uint4 (&f)[NF], int s) {
+      const uint32_t co = ((2 * s + khalf) ^ sw) * 16;
+      uint32_t ad[NF];
+#pragma unroll
+      for (int i = 0; i < RM; ++i) ad[i] = a_base + frag_off[i] + co;
+#pragma unroll
+      for (int j = 0; j < RN; ++j) ad[RM + j] = b_base + frag_off[RM + j] + co;
+      lds_read<NF>(f, ad);
+    };
+    read(fr[0], 0);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
-      const int kc = 2 * s + (lane >> 5);
-      bf16x8 af[RM], bfr[RN];
-#pragma unroll
-      for (int i = 0; i < RM; ++i) af[i] = as_bf16x8(sA[swz(wm * TM + i * 32 + (lane & 31), kc)]);
-#pragma unroll
-      for (int j = 0; j < RN; ++j) bfr[j] = as_bf16x8(sB[swz(wn * TN + j * 32 + (lane & 31), kc)]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < RM; ++i)
 #pragma unroll
         for (int j = 0; j < RN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fr[s & 1][i]),
+                                                               as_bf16x8(fr[s & 1][RM + j]),
+                                                               acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < BK / 16) read(fr[(s + 1) & 1], s + 1);
     }
-    __syncthreads();
-    if (kt + 1 < nsteps) {
-      sstore();
-      __syncthreads();
-    }
+  };
+
+  // Step kt consumes stage kt % 3.  Before reading it, this wave waits for its
+  // own DMA of step kt (the DMA of step kt+1 may stay in flight), then the
+  // barrier makes every wave's part visible and guarantees that all waves are
+  // done with the stage the next DMA (step kt+2) overwrites.
+  auto step = [&](int kt, uint4* sa, uint4* sb, uint4* na, uint4* nb) {
+    if (kt + 1 < nsteps) wait_vmcnt<DMA_PER_STEP>(); else wait_vmcnt<0>();
+    barrier_only();
+    if (kt + 2 < nsteps) issue(kt + 2, na, nb);
+    compute(sa, sb);
+  };
+
+  issue(0, sA0, sB0);
+  if (nsteps > 1) issue(1, sA1, sB1);
+  for (int kt = 0; kt < nsteps; kt += 3) {
+    step(kt, sA0, sB0, sA2, sB2);
+    if (kt + 1 < nsteps) step(kt + 1, sA1, sB1, sA0, sB0);
+    if (kt + 2 < nsteps) step(kt + 2, sA2, sB2, sA1, sB1);
   }
 
   // epilogue: accumulator (i, j) register v holds row 8*(v/4) + 4*(lane/32) + v%4
@@ -187,6 +278,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(const GemmArgs p
       }
     }
   }
+#endif
 }
 
 template <int BM, int BN, int WAVES_M, int MODE>
