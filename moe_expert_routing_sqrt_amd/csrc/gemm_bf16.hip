@@ -50,11 +50,13 @@ struct GemmArgs {
   int d_ff;                // SWIGLU: first up-projection row of w13
 };
 
-__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+// LDS operand rows are 128 bytes (8 chunks of 16 B).  gfx950's LDS serves 16
+// lanes x 16 B per clock over 64 banks, so the 16 rows read together must land
+// on distinct bank groups: even rows use banks 0-31, odd rows 32-63, and within
+// each parity the chunk is XORed with (r >> 1) & 7.
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Wait until at most n vector-memory operations of this wave are outstanding
 // (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
@@ -78,34 +80,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
 }
 
-// N 16-byte LDS reads in one asm block that also waits for them: the LDS reads
-// are then invisible to the compiler's memory-counter bookkeeping, which would
-// otherwise treat every in-flight DMA of later stages as a possible writer of
-// the stage being read and wait for all of them.  The wait inside the block
-// means no output register is handed back while its load is still in flight.
-template <int N>
-__device__ __forceinline__ void lds_read(uint4 (&v)[N], const uint32_t (&a)[N]) {
-  if constexpr (N == 2) {
-    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&v"(v[0]), "=&v"(v[1]) : "v"(a[0]), "v"(a[1]) : "memory");
-  } else if constexpr (N == 3) {
-    asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\t"
-                 "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]) : "v"(a[0]), "v"(a[1]), "v"(a[2]) : "memory");
-  } else if constexpr (N == 4) {
-    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
-                 "ds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]) : "memory");
-  } else if constexpr (N == 6) {
-    asm volatile("ds_read_b128 %0, %6\n\tds_read_b128 %1, %7\n\tds_read_b128 %2, %8\n\t"
-                 "ds_read_b128 %3, %9\n\tds_read_b128 %4, %10\n\tds_read_b128 %5, %11\n\t"
-                 "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5])
-                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]) : "memory");
-  } else {
-    static_assert(N == 2, "unsupported fragment count");
-  }
+// 64 lanes x 16 bytes from global memory straight into 1 KB of LDS at
+// lds + lane*16 (global_load_lds_dwordx4; M0 holds the wave-uniform LDS
+// base, one wait state after writing it).  Issued from asm so the compiler's
+// memory-counter bookkeeping does not see an LDS writer: it would otherwise
+// make every later LDS read wait for all DMA in flight.  There is no output
+// register; completion is waited for explicitly (wait_vmcnt) before the
+// barrier that publishes a stage.
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(gaddr) : "memory", "m0");
 }
 
 template <int BM, int BN, int WAVES_M, int MODE>
@@ -132,17 +116,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs p
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
 
   // Direct-to-LDS loads: one instruction moves 64 lanes x 16 B into 1 KB of
-  // LDS at lane*16, i.e. 8 rows of 128 B.  The LDS layout is row-major with the
-  // 16-byte chunks of a row XOR-swizzled by (row & 7); since the LDS slot of a
-  // lane is fixed, the swizzle is applied to the global address instead: the
-  // lane filling physical chunk pc of row r fetches logical chunk pc ^ (r & 7).
-  const int lrow = lane >> 3;                  // row within the 8-row block
-  const int lch = (lane & 7) ^ (lrow & 7);     // logical chunk this lane fetches
+  // LDS at lane*16, i.e. 8 rows of 128 B.  The LDS slot of a lane is fixed, so
+  // the swizzle is applied to the global address instead: the lane filling
+  // physical chunk pc of row r fetches logical chunk pc ^ ((r >> 1) & 7).
+  // Block j covers rows 8j..8j+7 and this wave only fills blocks j = wave + 4i,
+  // so (r >> 1) & 7 = 4*(wave & 1) + (lane >> 4) for every row it fills.
+  const int lrow = lane >> 3;  // row within the 8-row block
+  const int lch = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);  // logical chunk fetched
   const uint16_t* a_src[ADMA];
   const uint16_t* b_src[BDMA];
 #pragma unroll
@@ -169,17 +154,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs p
   const int nkp = p.K / BK;
   const int nsteps = PLANES * nkp;
 
-  auto issue = [&](int kt, uint4* sa, uint4* sb) {
+  // DMA of one K step, split into parts so they can be spread between MFMA
+  // groups (issuing all at once stalls the wave on address back-pressure).
+  constexpr int NDMA = ADMA + BDMA;
+  auto issue_part = [&](int kt, uint4* sa, uint4* sb, int q0, int q1) {
     const int plane = PLANES == 1 ? 0 : kt / nkp;
     const int k0 = (kt - plane * nkp) * BK;
-#pragma unroll
-    for (int i = 0; i < ADMA; ++i)
-      __builtin_amdgcn_global_load_lds(a_src[i] + k0, (lds_ptr_t)(sa + (wave + 4 * i) * 64), 16, 0, 0);
+    const uint32_t la = lds_addr(sa), lb = lds_addr(sb);
     const int64_t boff = (int64_t)plane * p.b_plane_stride + k0;
 #pragma unroll
-    for (int i = 0; i < BDMA; ++i)
-      __builtin_amdgcn_global_load_lds(b_src[i] + boff, (lds_ptr_t)(sb + (wave + 4 * i) * 64), 16, 0, 0);
+    for (int q = 0; q < NDMA; ++q) {
+      if (q < q0 || q >= q1) continue;
+      if (q < ADMA) dma16(a_src[q] + k0, la + (wave + 4 * q) * 1024);
+      else dma16(b_src[q - ADMA] + boff, lb + (wave + 4 * (q - ADMA)) * 1024);
+    }
   };
+  auto issue = [&](int kt, uint4* sa, uint4* sb) { issue_part(kt, sa, sb, 0, NDMA); };
 
   f32x16 acc[RM][RN];
 #pragma unroll
@@ -189,42 +179,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs p
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // Fragment addresses: row r of an operand tile is 128 bytes, chunk c of it
-  // sits at (c ^ (r & 7)) * 16; rows used by a lane are lane%32 plus multiples
-  // of 8, so the swizzle term depends on the lane only.
-  constexpr int NF = RM + RN;
-  uint32_t frag_off[NF];
+  // Fragment reads: row r of an operand tile is 128 bytes and chunk c of it
+  // sits at (c ^ (r & 7)) * 16.  Slice s+1 is read while the MFMAs of slice s
+  // run.
+  auto compute = [&](const uint4* sa, const uint4* sb, int kn, uint4* na, uint4* nb) {
+    bf16x8 fa[2][RM], fb[2][RN];
+    auto read = [&](int buf, int s) {
+      const int kc = 2 * s + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < RM; ++i) frag_off[i] = (wm * TM + i * 32 + (lane & 31)) * 128;
+      for (int i = 0; i < RM; ++i) fa[buf][i] = as_bf16x8(sa[swz(wm * TM + i * 32 + (lane & 31), kc)]);
 #pragma unroll
-  for (int j = 0; j < RN; ++j) frag_off[RM + j] = (wn * TN + j * 32 + (lane & 31)) * 128;
-  const int sw = lane & 7, khalf = lane >> 5;
-
-  auto compute = [&](const uint4* sa, const uint4* sb) {
-    const uint32_t a_base = lds_addr(sa), b_base = lds_addr(sb);
-    uint4 fr[2][NF];
-    auto read = [&](uint4 (&f)[NF], int s) {
-      const uint32_t co = ((2 * s + khalf) ^ sw) * 16;
-      uint32_t ad[NF];
-#pragma unroll
-      for (int i = 0; i < RM; ++i) ad[i] = a_base + frag_off[i] + co;
-#pragma unroll
-      for (int j = 0; j < RN; ++j) ad[RM + j] = b_base + frag_off[RM + j] + co;
-      lds_read<NF>(f, ad);
+      for (int j = 0; j < RN; ++j) fb[buf][j] = as_bf16x8(sb[swz(wn * TN + j * 32 + (lane & 31), kc)]);
     };
-    read(fr[0], 0);
+    constexpr int NS = BK / 16;
+    read(0, 0);
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      __builtin_amdgcn_sched_barrier(0);
+    for (int s = 0; s < NS; ++s) {
+      if (s + 1 < NS) read((s + 1) & 1, s + 1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads of slice s+1 ahead of these MFMAs
 #pragma unroll
       for (int i = 0; i < RM; ++i)
 #pragma unroll
         for (int j = 0; j < RN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fr[s & 1][i]),
-                                                               as_bf16x8(fr[s & 1][RM + j]),
-                                                               acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j], acc[i][j], 0, 0, 0);
+      // a share of the next stage's DMA goes out while these MFMAs run
+      if (kn >= 0 && s < NS - 1) {
+        constexpr int per = (NDMA + NS - 2) / (NS - 1);
+        issue_part(kn, na, nb, s * per, (s + 1) * per);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      if (s + 1 < BK / 16) read(fr[(s + 1) & 1], s + 1);
     }
   };
 
@@ -235,8 +218,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs p
   auto step = [&](int kt, uint4* sa, uint4* sb, uint4* na, uint4* nb) {
     if (kt + 1 < nsteps) wait_vmcnt<DMA_PER_STEP>(); else wait_vmcnt<0>();
     barrier_only();
-    if (kt + 2 < nsteps) issue(kt + 2, na, nb);
-    compute(sa, sb);
+    compute(sa, sb, kt + 2 < nsteps ? kt + 2 : -1, na, nb);
   };
 
   issue(0, sA0, sB0);
