@@ -53,10 +53,12 @@ def algorithmic(cfg):
     T, d, E, k, d_ff = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
     P = T * k if not cfg.local else None
     act = 4 if cfg.dtype == "f32" else 2
+    # packed-row bytes: e4m3 codes plus one fp32 scale per 128 columns for fp8
+    packed = d + 4 * (d // 128) if cfg.dtype == "fp8" else d * act
     return {
         "route_flops": 2 * T * d * E,
         "route_select_bytes": T * E * 4 + E * 4 + T * k * 8 + ((T + 63) // 64) * E * 4,
-        "dispatch_bytes": lambda rows: T * d * act + rows * (d * act) + 12 * T * k,
+        "dispatch_bytes": lambda rows: T * d * act + rows * packed + 12 * T * k,
         "ffn_up_flops": lambda rows: 4 * d * d_ff * rows,
         "ffn_down_flops": lambda rows: 2 * d * d_ff * rows,
         "shared_flops": 6 * d * d_ff * T,

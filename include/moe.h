@@ -211,6 +211,15 @@ int moe_combine(const moe_shape* shape, const int32_t* dest, const float* topk_w
                 moe_stream_t stream);
 
 /*
+ * moe_quantize_rows_e4m3 - bf16 [rows, cols] -> e4m3 codes [rows, cols] with
+ * one fp32 scale per 1 x 128 tile of a row [rows, cols/128] (the same rule as
+ * moe_dispatch's MOE_E4M3 output).  For the shared expert of the fp8 workload,
+ * whose input is the unpermuted token rows.  cols must be a multiple of 128.
+ */
+int moe_quantize_rows_e4m3(int64_t rows, int32_t cols, const void* x, uint8_t* q, float* scale,
+                           moe_stream_t stream);
+
+/*
  * moe_quantize_blocks_e4m3 - fp32 [n, rows, cols] -> e4m3 codes
  * [n, rows, cols] with one fp32 scale per 128 x 128 block
  * [n, rows/128, cols/128] (scale = amax/448, or 1 for an all-zero block;

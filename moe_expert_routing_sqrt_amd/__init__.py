@@ -23,7 +23,7 @@ from ._lib import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN, MOE_F
                    MOE_FP8_TILE, MOE_ROUTE_BLOCK, MOE_ROUTE_LOGITS_IN, MoeError, MoeShape)
 
 __all__ = ["shape", "gate_prepare", "route", "dispatch", "expert_ffn", "combine",
-           "quantize_blocks_e4m3", "MoELayer", "MoeError", "lib"]
+           "quantize_blocks_e4m3", "quantize_rows_e4m3", "MoELayer", "MoeError", "lib"]
 
 
 def lib():
@@ -210,6 +210,22 @@ def combine(sh: MoeShape, dest: torch.Tensor, topk_w: torch.Tensor, yp: torch.Te
                            _ptr(out), out_dtype, 1 if accumulate else 0, _stream())
     _lib.check("moe_combine", st)
     return out
+
+
+def quantize_rows_e4m3(x: torch.Tensor, q=None, scale=None):
+    """bf16 [rows, cols] -> e4m3 codes (uint8) + fp32 scales per 1x128 row tile."""
+    rows, cols = x.shape
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bf16")
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((rows, cols // MOE_FP8_TILE), dtype=torch.float32, device=x.device)
+    _need(q, rows * cols, "q")
+    _need(scale, rows * (cols // MOE_FP8_TILE), "scale")
+    st = lib().moe_quantize_rows_e4m3(rows, cols, _ptr(x), _ptr(q), _ptr(scale), _stream())
+    _lib.check("moe_quantize_rows_e4m3", st)
+    return q, scale
 
 
 def quantize_blocks_e4m3(w: torch.Tensor, q=None, scale=None):

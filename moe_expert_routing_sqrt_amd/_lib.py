@@ -52,6 +52,7 @@ SIGNATURES = {
                               _INT, _P]),
     "moe_combine": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _P, _INT, _P, _P, _INT, _INT, _P]),
     "moe_quantize_blocks_e4m3": (_INT, [_I64, _I32, _I32, _P, _P, _P, _P]),
+    "moe_quantize_rows_e4m3": (_INT, [_I64, _I32, _P, _P, _P, _P]),
 }
 
 _lib = None

@@ -139,14 +139,17 @@ int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int3
         (down && w2_scale == nullptr))
       return MOE_ERR_INVALID_ARG;
     if (d % 256 != 0 || d_ff % 128 != 0) return MOE_ERR_UNSUPPORTED;
-    return MOE_ERR_UNSUPPORTED;  // e4m3 expert GEMM not built yet
   }
   if (max_rows == 0) return MOE_OK;
   hipStream_t s = as_stream(stream);
   const bool mfma = dtype == MOE_BF16 && d % 256 == 0 && d_ff % 128 == 0;
   if (up) {
     hipError_t e;
-    if (mfma)
+    if (dtype == MOE_E4M3)
+      e = launch_ffn_up_fp8(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint8_t*>(xp),
+                            xp_scale, static_cast<const uint8_t*>(w13), w13_scale,
+                            static_cast<uint8_t*>(h), h_scale, s);
+    else if (mfma)
       e = launch_ffn_up_bf16(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint16_t*>(xp),
                              static_cast<const uint16_t*>(w13), static_cast<uint16_t*>(h), s);
     else
@@ -155,7 +158,11 @@ int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int3
   }
   if (down) {
     hipError_t e;
-    if (mfma)
+    if (dtype == MOE_E4M3)
+      e = launch_ffn_down_fp8(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint8_t*>(h),
+                              h_scale, static_cast<const uint8_t*>(w2), w2_scale,
+                              static_cast<uint16_t*>(yp), s);
+    else if (mfma)
       e = launch_ffn_down_bf16(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint16_t*>(h),
                                static_cast<const uint16_t*>(w2), static_cast<uint16_t*>(yp), s);
     else
@@ -180,6 +187,15 @@ int moe_combine(const moe_shape* shape, const int32_t* dest, const float* topk_w
   if (shape->T == 0) return MOE_OK;
   return hip_status(launch_combine(shape->T, shape->k, shape->d, dest, topk_w, yp, y_dtype, ysh, out,
                                    out_dtype, accumulate, as_stream(stream)));
+}
+
+int moe_quantize_rows_e4m3(int64_t rows, int32_t cols, const void* x, uint8_t* q, float* scale,
+                           moe_stream_t stream) {
+  if (rows < 0 || cols <= 0 || x == nullptr || q == nullptr || scale == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (cols % MOE_FP8_TILE != 0) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_quantize_rows(rows, cols, static_cast<const uint16_t*>(x), q, scale,
+                                         as_stream(stream)));
 }
 
 int moe_quantize_blocks_e4m3(int64_t n, int32_t rows, int32_t cols, const float* w, uint8_t* q,

@@ -53,6 +53,8 @@ hipError_t launch_combine(int64_t T, int k, int d, const int32_t* dest, const fl
 // weight preparation
 hipError_t launch_gate_prepare(int d, int E, const float* w_gate, uint16_t* w_prep,
                                hipStream_t s);
+hipError_t launch_quantize_rows(int64_t rows, int cols, const uint16_t* x, uint8_t* q, float* scale,
+                                hipStream_t s);
 hipError_t launch_quantize_blocks(int64_t n, int rows, int cols, const float* w, uint8_t* q,
                                   float* scale, hipStream_t s);
 

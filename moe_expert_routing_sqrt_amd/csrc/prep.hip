@@ -9,6 +9,9 @@
 //                   iteration loop").
 //  quantize_blocks  fp32 [n, R, C] -> e4m3 codes with one fp32 scale per
 //                   128 x 128 block (the fp8 workload's weight format).
+//  quantize_rows    bf16 [rows, C] -> e4m3 codes with one fp32 scale per
+//                   1 x 128 tile of a row (the shared expert's input in the fp8
+//                   workload; routed rows are quantised inside dispatch).
 #pragma clang fp contract(off)
 
 #include "common.h"
@@ -70,7 +73,50 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(int rows, int cols
   }
 }
 
+// 16 threads per 128-wide tile, 8 elements each; 16 tiles per work-group.
+__global__ __launch_bounds__(256) void quantize_rows_kernel(int64_t ntiles, int cols,
+                                                            const uint16_t* __restrict__ x,
+                                                            uint8_t* __restrict__ q,
+                                                            float* __restrict__ scale) {
+  const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // tile index
+  if (t >= ntiles) return;                                          // whole 16-lane groups
+  const int sub = threadIdx.x & 15;
+  const int tiles_per_row = cols / kBlk;
+  const int64_t row = t / tiles_per_row;
+  const int64_t col = (t % tiles_per_row) * kBlk + sub * 8;
+  const uint4 v = *reinterpret_cast<const uint4*>(x + row * cols + col);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_to_f32(static_cast<uint16_t>(w[i] & 0xFFFFu));
+    f[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+  const float sc = e4m3_tile_scale(amax);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(f[i] / sc) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(f[4 + i] / sc) << (8 * i);
+  *reinterpret_cast<uint2*>(q + row * cols + col) = make_uint2(lo, hi);
+  if (sub == 0) scale[t] = sc;
+}
+
 }  // namespace
+
+hipError_t launch_quantize_rows(int64_t rows, int cols, const uint16_t* x, uint8_t* q, float* scale,
+                                hipStream_t s) {
+  const int64_t ntiles = rows * (cols / kBlk);
+  if (ntiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)((ntiles + 15) / 16)), dim3(256), 0, s, ntiles,
+                     cols, x, q, scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_gate_prepare(int d, int E, const float* w_gate, uint16_t* w_prep,
                                hipStream_t s) {

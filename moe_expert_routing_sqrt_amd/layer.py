@@ -11,8 +11,8 @@ from typing import Optional, Sequence
 import torch
 
 from . import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN, MOE_FFN_UP, MOE_FP8_TILE,
-               combine, dispatch, expert_ffn, gate_prepare, n_blocks, quantize_blocks_e4m3, route,
-               shape)
+               combine, dispatch, expert_ffn, gate_prepare, n_blocks, quantize_blocks_e4m3,
+               quantize_rows_e4m3, route, shape)
 
 STAGES = ("route", "dispatch", "ffn_up", "ffn_down", "shared", "combine")
 
@@ -67,6 +67,7 @@ class MoELayer:
             self.ysh = torch.empty((T, d), dtype=act, device=dev)
             if self.dtype == MOE_E4M3:
                 self.sh_xq = torch.empty((T, d), dtype=torch.uint8, device=dev)
+                self.sh_xs = torch.empty((T, d // MOE_FP8_TILE), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, d), dtype=torch.float32 if self.local else act, device=dev)
 
     def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
@@ -111,4 +112,4 @@ class MoELayer:
         return out
 
     def _shared_quant_input(self, x):
-        raise NotImplementedError("fp8 shared expert input quantisation")
+        return quantize_rows_e4m3(x, self.sh_xq, self.sh_xs)
