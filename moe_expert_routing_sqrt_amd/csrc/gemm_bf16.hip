@@ -23,6 +23,8 @@
 //   GATE3   (router gate): B is three bf16 planes whose sum is the fp32 gate
 //           weight exactly; the K loop runs over the three planes into one
 //           fp32 accumulator, stored as fp32 logits.
+#include <type_traits>
+
 #include "common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -64,11 +66,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs p
   static_assert(RM >= 1 && RN >= 1 && ADMA >= 1 && BDMA >= 1, "tile too small");
   static_assert(MODE != MODE_SWIGLU || RN % 2 == 0, "gate/up blocks come in pairs");
 
-  // three pipeline stages, each its own LDS object so the compiler can tell the
-  // DMA into one stage from the reads of another
-  __shared__ uint4 sA0[BM * 8], sA1[BM * 8], sA2[BM * 8];
-  __shared__ uint4 sB0[BN * 8], sB1[BN * 8], sB2[BN * 8];
+  // three pipeline stages of (A tile, B tile); after the K loop the same LDS
+  // stages the output tile so it leaves in 16-byte row chunks
+  constexpr int STAGE = (BM + BN) * 8;  // uint4 per stage
+  __shared__ uint4 smem[3 * STAGE];
   __shared__ int s_pre[kMaxExperts + 1];
+  uint4* const sA0 = smem;
+  uint4* const sB0 = smem + BM * 8;
+  uint4* const sA1 = smem + STAGE;
+  uint4* const sB1 = smem + STAGE + BM * 8;
+  uint4* const sA2 = smem + 2 * STAGE;
+  uint4* const sB2 = smem + 2 * STAGE + BM * 8;
 
   TileInfo ti;
   if (!map_tile(p.offsets, p.n_exp, p.rows_total, BM, p.n_tiles, s_pre, ti)) return;
@@ -188,36 +196,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs p
     if (kt + 2 < nsteps) step(kt + 2, sA2, sB2, sA1, sB1);
   }
 
-  // epilogue: accumulator (i, j) register v holds row 8*(v/4) + 4*(lane/32) + v%4
-  // and column lane%32 of its 32x32 block
+  // Epilogue.  Accumulator (i, j) register v holds row 8*(v/4) + 4*(lane/32) +
+  // v%4 and column lane%32 of its 32x32 block: each lane owns one column, so
+  // direct stores would be 2-byte scatters.  The tile is written to LDS first
+  // (row pitch padded by 16 bytes), then streamed out as 16-byte row chunks.
+  using OutT = std::conditional_t<MODE == MODE_GATE3, float, uint16_t>;
+  constexpr int OUT_COLS = MODE == MODE_SWIGLU ? BN / 2 : BN;
+  constexpr int ROW_BYTES = OUT_COLS * (int)sizeof(OutT);
+  constexpr int PITCH = ROW_BYTES + 16;
+  static_assert(BM * PITCH <= 3 * STAGE * 16, "output tile must fit the LDS ring");
+  char* const stage = reinterpret_cast<char*>(smem);
+  barrier_only();  // every wave is done with the last stage (its DMA was waited for)
 #pragma unroll
   for (int i = 0; i < RM; ++i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int lr = wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (lr >= ti.rows) continue;
-      const int64_t grow = ti.row0 + lr;
+      OutT* row = reinterpret_cast<OutT*>(stage + lr * PITCH);
       if constexpr (MODE == MODE_SWIGLU) {
-        uint16_t* out = static_cast<uint16_t*>(p.C) + grow * p.ldc;
 #pragma unroll
         for (int jj = 0; jj < RN / 2; ++jj) {
           const float g = acc[i][jj][v];
           const float u = acc[i][jj + RN / 2][v];
-          const float hval = g / (1.0f + __expf(-g)) * u;
-          const int col = ti.n_tile * (BN / 2) + wn * (TN / 2) + jj * 32 + (lane & 31);
-          out[col] = f32_to_bf16(hval);
+          row[wn * (TN / 2) + jj * 32 + (lane & 31)] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
         }
       } else if constexpr (MODE == MODE_STORE) {
-        uint16_t* out = static_cast<uint16_t*>(p.C) + grow * p.ldc;
 #pragma unroll
-        for (int j = 0; j < RN; ++j)
-          out[ti.n_tile * BN + wn * TN + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][v]);
+        for (int j = 0; j < RN; ++j) row[wn * TN + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][v]);
       } else {
-        float* out = static_cast<float*>(p.C) + grow * p.ldc;
 #pragma unroll
-        for (int j = 0; j < RN; ++j) out[ti.n_tile * BN + wn * TN + j * 32 + (lane & 31)] = acc[i][j][v];
+        for (int j = 0; j < RN; ++j) row[wn * TN + j * 32 + (lane & 31)] = acc[i][j][v];
       }
     }
+  }
+  __syncthreads();
+  constexpr int CPR = ROW_BYTES / 16;  // 16-byte chunks per row
+  const int64_t col0 = (int64_t)ti.n_tile * OUT_COLS;
+  for (int q = tid; q < ti.rows * CPR; q += kThreads) {
+    const int r = q / CPR, c = q % CPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(stage + r * PITCH + c * 16);
+    char* dst = reinterpret_cast<char*>(static_cast<OutT*>(p.C) + (ti.row0 + r) * p.ldc + col0) + c * 16;
+    *reinterpret_cast<uint4*>(dst) = v;
   }
 #endif
 }
