@@ -5,7 +5,8 @@
 //
 // A gather, not a scatter: each work-group owns a few tokens and pulls their k
 // expert rows in 16-byte chunks, so every output element is written once,
-// without atomics, and the fp32 sum runs in slot order (deterministic).
+// without atomics, and the fp32 sum runs in slot order (deterministic).  Every
+// byte is touched once, so accesses are nontemporal.
 #include "common.h"
 #include "launch.h"
 
@@ -31,7 +32,7 @@ template <typename TY>
 __device__ __forceinline__ void load8(const TY* p, float (&f)[8]);
 template <>
 __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&f)[8]) {
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint4 v = ld_stream(p);
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -41,23 +42,22 @@ __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&f)[8]
 }
 template <>
 __device__ __forceinline__ void load8<float>(const float* p, float (&f)[8]) {
-  const float4 a = reinterpret_cast<const float4*>(p)[0];
-  const float4 b = reinterpret_cast<const float4*>(p)[1];
-  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  const uint4 a = ld_stream(p), b = ld_stream(p + 4);
+  f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y); f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
+  f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y); f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
 }
 
 template <typename TO>
 __device__ __forceinline__ void store8(TO* p, const float (&f)[8]);
 template <>
 __device__ __forceinline__ void store8<uint16_t>(uint16_t* p, const float (&f)[8]) {
-  *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                                            pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+  st_stream(p, make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                          pack_bf16x2(f[6], f[7])));
 }
 template <>
 __device__ __forceinline__ void store8<float>(float* p, const float (&f)[8]) {
-  reinterpret_cast<float4*>(p)[0] = make_float4(f[0], f[1], f[2], f[3]);
-  reinterpret_cast<float4*>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
+  st_stream(p, make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])));
+  st_stream(p + 4, make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]), __float_as_uint(f[7])));
 }
 
 template <typename TY, typename TO, bool ACC>

@@ -72,6 +72,21 @@ __device__ __forceinline__ float e4m3_tile_scale(float amax) {
   return amax == 0.0f ? 1.0f : amax / 448.0f;
 }
 
+// ---------------------------------------------------------------- streaming accesses
+// 16-byte loads/stores marked nontemporal: data read or written once per pass
+// streams through the caches instead of displacing reused lines.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ void st_stream(void* p, uint4 v) {
+  u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, static_cast<u32x4*>(p));
+}
+
 // ---------------------------------------------------------------- wave reductions
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {

@@ -157,8 +157,7 @@ __global__ __launch_bounds__(kPermThreads) void dispatch_permute_kernel(const Pe
     if constexpr (!FP8) {
       for (int j = 0; j < k; ++j) {
         const int r = s_dest[tt * kMaxK + j];
-        if (r >= 0)
-          reinterpret_cast<uint4*>(static_cast<char*>(p.xp) + (int64_t)r * p.d * ELEM)[c] = v;
+        if (r >= 0) st_stream(static_cast<char*>(p.xp) + ((int64_t)r * p.d * ELEM + (int64_t)c * 16), v);
       }
     } else {
       // 8 bf16 per chunk; a 128-wide tile is 16 consecutive chunks = 16 lanes
