@@ -12,6 +12,7 @@ timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,14 +26,34 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 
+# HBM traffic of the routed up-projection launch, per launch, from two
+# rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over
+#   python3 bench.py --steps 2 --warmup 1 --cpu-sample 0 --copy-probe
+# Each counter is scaled by what it reads for the copy probe (a plain 2 GiB
+# elementwise copy run in the same process): on gfx950 FETCH_SIZE reports half
+# of the bytes a full-line read moves, WRITE_SIZE reports them exactly.  The
+# record holds only for the kernel sources it was taken from: any change to them
+# turns the reported traffic into null until the passes are taken again.
+TRAFFIC_SOURCES = ("moe_expert_routing_sqrt_amd/csrc/gemm_bf16.hip",
+                   "moe_expert_routing_sqrt_amd/csrc/gemm_common.h",
+                   "moe_expert_routing_sqrt_amd/csrc/common.h",
+                   "moe_expert_routing_sqrt_amd/build.py")
+TRAFFIC = {
+    "v3": {"sources_sha256": "d589d8f5caac35cf8d5e1ca06a52efc16749c92ec7d2286e7d513456078c6a16",
+           "fetch_kib": 11647986.1, "fetch_scale": 1.99997,
+           "write_kib": 524288.0, "write_scale": 1.0},
+}
+
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3")
     ap.add_argument("--cpu-sample", type=int, default=512, help="tokens the CPU oracle runs (0: skip)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run a plain 2 GiB copy (counter calibration for --pmc passes)")
     return ap.parse_args()
 
 
@@ -55,17 +76,54 @@ def algorithmic(cfg):
     act = 4 if cfg.dtype == "f32" else 2
     # packed-row bytes: e4m3 codes plus one fp32 scale per 128 columns for fp8
     packed = d + 4 * (d // 128) if cfg.dtype == "fp8" else d * act
+    wbytes = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.dtype]
     return {
         "route_flops": 2 * T * d * E,
         "route_select_bytes": T * E * 4 + E * 4 + T * k * 8 + ((T + 63) // 64) * E * 4,
         "dispatch_bytes": lambda rows: T * d * act + rows * packed + 12 * T * k,
         "ffn_up_flops": lambda rows: 4 * d * d_ff * rows,
+        # packed rows in, the local experts' W1/W3 once, h out (+ scales for fp8)
+        "ffn_up_bytes": lambda rows: rows * packed + (cfg.e_end - cfg.e_begin) * 2 * d_ff * d * wbytes
+        + rows * (d_ff + 4 * (d_ff // 128) if cfg.dtype == "fp8" else d_ff * act)
+        + ((cfg.e_end - cfg.e_begin) * 2 * d_ff * d // (128 * 128) * 4 if cfg.dtype == "fp8" else 0),
         "ffn_down_flops": lambda rows: 2 * d * d_ff * rows,
         "shared_flops": 6 * d * d_ff * T,
         "combine_bytes": lambda rows: rows * d * act + 8 * T * k + (T * d * act if not cfg.local else 0)
         + T * d * (4 * 2 if cfg.local else act),
         "pairs": P,
     }
+
+
+def sources_digest() -> str:
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic(cfg, up_bytes):
+    """Counter-measured HBM bytes per routed up-projection launch, or None."""
+    rec = TRAFFIC.get(cfg.name)
+    if rec is None or rec["sources_sha256"] != sources_digest():
+        return None
+    fetch = rec["fetch_kib"] * 1024 * rec["fetch_scale"]
+    write = rec["write_kib"] * 1024 * rec["write_scale"]
+    return {"bytes": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
+            "vs_algorithmic_bytes": (fetch + write) / up_bytes}
+
+
+def copy_probe(torch, dev):
+    """A plain elementwise copy of known size: 2 GiB read, 2 GiB written per launch."""
+    n = (2 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print("copy probe: 3 launches of a 2 GiB fp32 negation", file=sys.stderr, flush=True)
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def cpu_baseline(cfg, inp, ex, S):
@@ -119,6 +177,8 @@ def main():
 
     cfg = C.get(a.workload)
     dev = torch.device("cuda:0")
+    if a.copy_probe:
+        copy_probe(torch, dev)
     t_setup = time.perf_counter()
     inp = gen.make_router(cfg, device=dev)
     ex = gen.make_experts(cfg, device=dev)
@@ -147,6 +207,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = start.elapsed_time(end) / a.steps
+    per_step = sorted(m[0].elapsed_time(m[6]) for m in marks)
+    median_ms = per_step[len(per_step) // 2]
     print(f"timed {a.steps} steps: {ms_per_step:.3f} ms/step (host wall {wall / a.steps * 1e3:.3f})",
           file=sys.stderr, flush=True)
 
@@ -173,6 +235,7 @@ def main():
     gemm_ms = st_ms["ffn_up"] + st_ms["ffn_down"] + st_ms["shared"]
     gemm_flops = alg["ffn_up_flops"](rows) + alg["ffn_down_flops"](rows) + (alg["shared_flops"] if layer.has_shared else 0)
     up = stages["ffn_up"]
+    up_traffic = traffic(cfg, alg["ffn_up_bytes"](rows))
     result = {
         "metric": METRIC,
         "value": cfg.T / (ms_per_step * 1e-3),
@@ -181,6 +244,7 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_median": median_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -190,8 +254,11 @@ def main():
                    "k": cfg.k, "M": cfg.M, "d_ff": cfg.d_ff, "routed_rows": rows},
         "roofline": {"kernel": "routed up-projection GEMM + SwiGLU (moe_expert_ffn MOE_FFN_UP)",
                      "bound": "mfma", "achieved": up["tflops"], "peak": peak_mm, "unit": "TFLOP/s",
-                     "frac": up["tflops"] / peak_mm, "traffic": None,
-                     "avg_ms": up["ms"], "flops_per_launch": alg["ffn_up_flops"](rows)},
+                     "frac": up["tflops"] / peak_mm,
+                     "traffic": None if up_traffic is None else up_traffic["bytes"],
+                     "traffic_detail": up_traffic,
+                     "avg_ms": up["ms"], "flops_per_launch": alg["ffn_up_flops"](rows),
+                     "algorithmic_bytes_per_launch": alg["ffn_up_bytes"](rows)},
         "gemm_mfma_frac": tf(gemm_flops, gemm_ms) / peak_mm,
         "stages": stages,
     }
