@@ -34,7 +34,7 @@ PEAK_HBM_GBS = 8000.0
 # of the bytes a full-line read moves, WRITE_SIZE reports them exactly.  The
 # record holds only for the kernel sources it was taken from: any change to them
 # turns the reported traffic into null until the passes are taken again.
-TRAFFIC_SOURCES = ("moe_expert_routing_sqrt_amd/csrc/gemm_bf16.hip",
+TRAFFIC_SOURCES = ("moe_expert_routing_sqrt_amd/csrc/ffn_bf16.hip",
                    "moe_expert_routing_sqrt_amd/csrc/gemm_common.h",
                    "moe_expert_routing_sqrt_amd/csrc/common.h",
                    "moe_expert_routing_sqrt_amd/build.py")
@@ -97,7 +97,10 @@ def algorithmic(cfg):
 def sources_digest() -> str:
     h = hashlib.sha256()
     for rel in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
+        path = os.path.join(ROOT, rel)
+        if not os.path.exists(path):
+            return ""
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 

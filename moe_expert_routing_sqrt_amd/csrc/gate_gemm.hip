@@ -1,7 +1,10 @@
-// Grouped bf16 GEMM on gfx950 matrix cores: the expert FFN products and the
-// fp32-accurate gate product.
+// Router gate product on gfx950 matrix cores, fp32-accurate:
 //
-//   C[m][n] = sum_k A[m][k] * B[n][k]       (A: activations, B: weights [out, in])
+//   logits[t][e] = sum_k x[t][k] * W_g[k][e]
+//
+// x is bf16 (exact); the fp32 gate weight is split into three bf16 planes whose
+// sum is exact (prepared once by moe_gate_prepare), and the K loop runs over the
+// three planes into one fp32 accumulator.
 //
 // Work-group tile BM x BN x 64 (K), 256 threads = 4 wave64s laid out
 // WAVES_M x WAVES_N; each wave owns a (BM/WAVES_M) x (BN/WAVES_N) block of
@@ -13,18 +16,6 @@
 // the loads for step k+2 are in flight while step k computes, with one
 // barrier per step.
 //
-// Epilogues
-//   SWIGLU  (up projection of the SwiGLU expert, mastering-deepseek-v4 Exp08,
-//           Implemented):  the BN weight rows of a tile are BN/2 gate rows
-//           (W1) and the matching BN/2 up rows (W3); each wave holds the gate
-//           and up accumulators of the same features, so
-//           h = silu(gate) * up is formed in registers and stored as bf16.
-//   STORE   (down projection): bf16 store.
-//   GATE3   (router gate): B is three bf16 planes whose sum is the fp32 gate
-//           weight exactly; the K loop runs over the three planes into one
-//           fp32 accumulator, stored as fp32 logits.
-#include <type_traits>
-
 #include "common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -34,27 +25,22 @@ namespace {
 
 constexpr int BK = 64;
 constexpr int kThreads = 256;
+constexpr int PLANES = 3;
 
-enum { MODE_SWIGLU = 0, MODE_STORE = 1, MODE_GATE3 = 2 };
-
-struct GemmArgs {
-  const uint16_t* A;
+struct GateArgs {
+  const uint16_t* A;       // x [T, d] bf16
   int64_t lda;
-  const uint16_t* B;
-  int64_t b_group_stride;  // elements between consecutive groups' weights
-  int64_t b_plane_stride;  // GATE3: elements between planes
-  void* C;
+  const uint16_t* B;       // three planes [E, d] bf16
+  int64_t b_plane_stride;  // elements between planes
+  float* C;                // logits [T, E]
   int64_t ldc;
-  const int* offsets;      // [n_exp + 1] or nullptr (one group of rows_total rows)
-  int n_exp;
-  int64_t rows_total;
-  int K;                   // reduction length (per plane)
-  int n_tiles;
-  int d_ff;                // SWIGLU: first up-projection row of w13
+  int64_t rows_total;      // T
+  int K;                   // d
+  int n_tiles;             // E / BN
 };
 
-template <int BM, int BN, int WAVES_M, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs p) {
+template <int BM, int BN, int WAVES_M>
+__global__ __launch_bounds__(kThreads, 1) void gate_gemm_kernel(const GateArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
@@ -62,9 +48,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs p
   constexpr int ADMA = BM / 32;  // 1 KB (8-row) LDS blocks per wave per K step
   constexpr int BDMA = BN / 32;
   constexpr int DMA_PER_STEP = ADMA + BDMA;
-  constexpr int PLANES = MODE == MODE_GATE3 ? 3 : 1;
   static_assert(RM >= 1 && RN >= 1 && ADMA >= 1 && BDMA >= 1, "tile too small");
-  static_assert(MODE != MODE_SWIGLU || RN % 2 == 0, "gate/up blocks come in pairs");
 
   // three pipeline stages of (A tile, B tile); after the K loop the same LDS
   // stages the output tile so it leaves in 16-byte row chunks
@@ -79,7 +63,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs p
   uint4* const sB2 = smem + 2 * STAGE + BM * 8;
 
   TileInfo ti;
-  if (!map_tile(p.offsets, p.n_exp, p.rows_total, BM, p.n_tiles, s_pre, ti)) return;
+  if (!map_tile(nullptr, 1, p.rows_total, BM, p.n_tiles, s_pre, ti)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,19 +87,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs p
     const int rc = r < ti.rows ? r : ti.rows - 1;  // padding rows: any valid row
     a_src[i] = p.A + (int64_t)(ti.row0 + rc) * p.lda + lch * 8;
   }
-  const uint16_t* bg = p.B + (int64_t)ti.group * p.b_group_stride + lch * 8;
 #pragma unroll
   for (int i = 0; i < BDMA; ++i) {
     const int r = (wave + 4 * i) * 8 + lrow;
-    int grow;
-    if constexpr (MODE == MODE_SWIGLU) {
-      const int part = r / TN, within = r % TN;
-      const int h0 = ti.n_tile * (BN / 2) + part * (TN / 2);
-      grow = within < TN / 2 ? h0 + within : p.d_ff + h0 + (within - TN / 2);
-    } else {
-      grow = ti.n_tile * BN + r;
-    }
-    b_src[i] = bg + (int64_t)grow * p.K;
+    b_src[i] = p.B + (int64_t)(ti.n_tile * BN + r) * p.K + lch * 8;
   }
 
   const int nkp = p.K / BK;
@@ -125,7 +100,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs p
   // groups (issuing all at once stalls the wave on address back-pressure).
   constexpr int NDMA = ADMA + BDMA;
   auto issue_part = [&](int kt, uint4* sa, uint4* sb, int q0, int q1) {
-    const int plane = PLANES == 1 ? 0 : kt / nkp;
+    const int plane = kt / nkp;
     const int k0 = (kt - plane * nkp) * BK;
     const uint32_t la = lds_addr(sa), lb = lds_addr(sb);
     const int64_t boff = (int64_t)plane * p.b_plane_stride + k0;
@@ -200,9 +175,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs p
   // v%4 and column lane%32 of its 32x32 block: each lane owns one column, so
   // direct stores would be 2-byte scatters.  The tile is written to LDS first
   // (row pitch padded by 16 bytes), then streamed out as 16-byte row chunks.
-  using OutT = std::conditional_t<MODE == MODE_GATE3, float, uint16_t>;
-  constexpr int OUT_COLS = MODE == MODE_SWIGLU ? BN / 2 : BN;
-  constexpr int ROW_BYTES = OUT_COLS * (int)sizeof(OutT);
+  constexpr int ROW_BYTES = BN * 4;
   constexpr int PITCH = ROW_BYTES + 16;
   static_assert(BM * PITCH <= 3 * STAGE * 16, "output tile must fit the LDS ring");
   char* const stage = reinterpret_cast<char*>(smem);
@@ -212,42 +185,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs p
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int lr = wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      OutT* row = reinterpret_cast<OutT*>(stage + lr * PITCH);
-      if constexpr (MODE == MODE_SWIGLU) {
+      float* row = reinterpret_cast<float*>(stage + lr * PITCH);
 #pragma unroll
-        for (int jj = 0; jj < RN / 2; ++jj) {
-          const float g = acc[i][jj][v];
-          const float u = acc[i][jj + RN / 2][v];
-          row[wn * (TN / 2) + jj * 32 + (lane & 31)] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
-        }
-      } else if constexpr (MODE == MODE_STORE) {
-#pragma unroll
-        for (int j = 0; j < RN; ++j) row[wn * TN + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][v]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < RN; ++j) row[wn * TN + j * 32 + (lane & 31)] = acc[i][j][v];
-      }
+      for (int j = 0; j < RN; ++j) row[wn * TN + j * 32 + (lane & 31)] = acc[i][j][v];
     }
   }
   __syncthreads();
   constexpr int CPR = ROW_BYTES / 16;  // 16-byte chunks per row
-  const int64_t col0 = (int64_t)ti.n_tile * OUT_COLS;
+  const int64_t col0 = (int64_t)ti.n_tile * BN;
   for (int q = tid; q < ti.rows * CPR; q += kThreads) {
     const int r = q / CPR, c = q % CPR;
     const uint4 v = *reinterpret_cast<const uint4*>(stage + r * PITCH + c * 16);
-    char* dst = reinterpret_cast<char*>(static_cast<OutT*>(p.C) + (ti.row0 + r) * p.ldc + col0) + c * 16;
+    char* dst = reinterpret_cast<char*>(p.C + (ti.row0 + r) * p.ldc + col0) + c * 16;
     *reinterpret_cast<uint4*>(dst) = v;
   }
 #endif
 }
 
-template <int BM, int BN, int WAVES_M, int MODE>
-hipError_t launch(const GemmArgs& a, int64_t max_rows, hipStream_t s) {
-  const int64_t mt = max_row_tiles(max_rows, a.offsets == nullptr ? 1 : a.n_exp, BM);
+template <int BM, int BN, int WAVES_M>
+hipError_t launch(const GateArgs& a, hipStream_t s) {
+  const int64_t mt = (a.rows_total + BM - 1) / BM;
   const int64_t grid = (mt * a.n_tiles + kXcds - 1) / kXcds * kXcds;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WAVES_M, MODE>), dim3((unsigned)grid), dim3(kThreads),
-                     0, s, a);
+  hipLaunchKernelGGL((gate_gemm_kernel<BM, BN, WAVES_M>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -257,61 +217,21 @@ bool gate_gemm_bf16_supported(int d, int E) { return d % BK == 0 && E % 64 == 0;
 
 hipError_t launch_gate_gemm_bf16(const uint16_t* x, const uint16_t* w_prep, float* logits,
                                  int64_t T, int d, int E, hipStream_t s) {
-  GemmArgs a{};
+  GateArgs a{};
   a.A = x;
   a.lda = d;
   a.B = w_prep;
-  a.b_group_stride = 0;
   a.b_plane_stride = (int64_t)E * d;
   a.C = logits;
   a.ldc = E;
-  a.offsets = nullptr;
-  a.n_exp = 1;
   a.rows_total = T;
   a.K = d;
   if (E % 128 == 0) {
     a.n_tiles = E / 128;
-    return launch<128, 128, 2, MODE_GATE3>(a, T, s);
+    return launch<128, 128, 2>(a, s);
   }
   a.n_tiles = E / 64;
-  return launch<64, 64, 2, MODE_GATE3>(a, T, s);
-}
-
-hipError_t launch_ffn_up_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
-                              int d_ff, const uint16_t* xp, const uint16_t* w13, uint16_t* h,
-                              hipStream_t s) {
-  GemmArgs a{};
-  a.A = xp;
-  a.lda = d;
-  a.B = w13;
-  a.b_group_stride = (int64_t)2 * d_ff * d;
-  a.C = h;
-  a.ldc = d_ff;
-  a.offsets = offsets;
-  a.n_exp = n_exp;
-  a.rows_total = max_rows;
-  a.K = d;
-  a.n_tiles = d_ff / 128;
-  a.d_ff = d_ff;
-  return launch<128, 256, 2, MODE_SWIGLU>(a, max_rows, s);
-}
-
-hipError_t launch_ffn_down_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
-                                int d_ff, const uint16_t* h, const uint16_t* w2, uint16_t* yp,
-                                hipStream_t s) {
-  GemmArgs a{};
-  a.A = h;
-  a.lda = d_ff;
-  a.B = w2;
-  a.b_group_stride = (int64_t)d * d_ff;
-  a.C = yp;
-  a.ldc = d;
-  a.offsets = offsets;
-  a.n_exp = n_exp;
-  a.rows_total = max_rows;
-  a.K = d_ff;
-  a.n_tiles = d / 256;
-  return launch<128, 256, 2, MODE_STORE>(a, max_rows, s);
+  return launch<64, 64, 2>(a, s);
 }
 
 }  // namespace moe

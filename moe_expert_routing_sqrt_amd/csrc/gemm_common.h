@@ -37,21 +37,22 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // 64 lanes x 16 bytes from global memory straight into 1 KB of LDS at
 // lds + lane*16 (global_load_lds_dwordx4; M0 holds the wave-uniform LDS
-// base, one wait state after writing it).  Issued from asm so the compiler's
+// base, one wait state after writing it; lds must be wave-uniform, and
+// readfirstlane keeps it in a scalar register whatever the compiler inferred).  Issued from asm so the compiler's
 // memory-counter bookkeeping does not see an LDS writer: it would otherwise
 // make every later LDS read wait for all DMA in flight.  There is no output
 // register; completion is waited for explicitly (wait_vmcnt) before the
 // barrier that publishes a stage.
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds), "v"(gaddr) : "memory", "m0");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(gaddr) : "memory", "m0");
 }
 
 // 64 lanes x 4 bytes from global memory into 256 contiguous LDS bytes at
 // lds + lane*4 (global_load_lds_dword), for per-row scale columns.
 __device__ __forceinline__ void dma4(const void* gaddr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(lds), "v"(gaddr) : "memory", "m0");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(gaddr) : "memory", "m0");
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
