@@ -39,8 +39,8 @@ TRAFFIC_SOURCES = ("moe_expert_routing_sqrt_amd/csrc/ffn_bf16.hip",
                    "moe_expert_routing_sqrt_amd/csrc/common.h",
                    "moe_expert_routing_sqrt_amd/build.py")
 TRAFFIC = {
-    "v3": {"sources_sha256": "d589d8f5caac35cf8d5e1ca06a52efc16749c92ec7d2286e7d513456078c6a16",
-           "fetch_kib": 11647986.1, "fetch_scale": 1.99997,
+    "v3": {"sources_sha256": "ba7a4f7cbfe7db1a83ea1e48c0ec4667e8ab3bf452e6be37ff238f17f94355fc",
+           "fetch_kib": 16543786.5, "fetch_scale": 1.99997,
            "write_kib": 524288.0, "write_scale": 1.0},
 }
 
