@@ -17,6 +17,9 @@ Stages (pages cited by title and section):
               Implemented: 6*d*d_ff flops per token-expert pair)
   combine   - gate-weighted sum back in token order (deepmox ch.5)
   fp8       - e4m3 block quantisation for the fp8 workload
+  balance   - per-expert bias update from the batch's expert load
+              (auxiliary-loss-free balancing; mastering-deepseek-v4, Implemented
+              and Measured)
 
 Parity pinned by tests/test_oracle_*.py; see each module's header for the pins
 and for the functions whose parity the pages leave unpinned.
