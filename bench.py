@@ -215,6 +215,20 @@ def main():
     print(f"timed {a.steps} steps: {ms_per_step:.3f} ms/step (host wall {wall / a.steps * 1e3:.3f})",
           file=sys.stderr, flush=True)
 
+    # the balancing step that follows a forward (moe_bias_update on the route's
+    # block counts); gamma = 0 keeps the workload fixed across repetitions
+    bu0, bu1 = ev(), ev()
+    reps = 50
+    load_buf = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    bu0.record()
+    for _ in range(reps):
+        M.bias_update(layer.block_counts, layer.bias, 0.0, load_buf)
+    bu1.record()
+    torch.cuda.synchronize()
+    bu_us = bu0.elapsed_time(bu1) / reps * 1e3
+    nblk = layer.block_counts.shape[0]
+    bu_bytes = nblk * cfg.E * 4 + cfg.E * 4 * 3
+
     names = ("route", "dispatch", "ffn_up", "ffn_down", "shared", "combine")
     st_ms = {n: sum(m[i].elapsed_time(m[i + 1]) for m in marks) / a.steps for i, n in enumerate(names)}
     rows = int(layer.dbufs["offsets"][-1].item())
@@ -264,6 +278,8 @@ def main():
                      "algorithmic_bytes_per_launch": alg["ffn_up_bytes"](rows)},
         "gemm_mfma_frac": tf(gemm_flops, gemm_ms) / peak_mm,
         "stages": stages,
+        "after_step": {"bias_update": {"us": bu_us, "bytes": bu_bytes, "gb_s": bu_bytes / (bu_us * 1e-6) / 1e9,
+                                       "bound": "latency (one work-group)"}},
     }
     if a.cpu_sample > 0:
         print("cpu baseline ...", file=sys.stderr, flush=True)

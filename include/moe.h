@@ -229,6 +229,29 @@ int moe_quantize_rows_e4m3(int64_t rows, int32_t cols, const void* x, uint8_t* q
 int moe_quantize_blocks_e4m3(int64_t n, int32_t rows, int32_t cols, const float* w, uint8_t* q,
                              float* scale, moe_stream_t stream);
 
+/*
+ * moe_bias_update - auxiliary-loss-free load balancing (mastering-deepseek-v4
+ * "MoE + Expert-Parallel Overlap (Exp08)", Implemented and Measured: a
+ * per-expert bias, updated from the observed expert load, replaces an
+ * auxiliary balancing loss).  The pages do not print the rule; this is the
+ * plainest reading:
+ *     load[e] = sum over r of counts[r, e]
+ *     bias[e] += gamma * sign(sum(load) / E - load[e])      (sign(0) = 0)
+ * The comparison is exact (integer: sum(load) against E * load[e]); the update
+ * is one fp32 addition of +gamma or -gamma, or none.
+ *   n_rows, counts  [n_rows, E] int32 device, row-major: moe_route's
+ *                   block_counts (n_rows = ceil(T/MOE_ROUTE_BLOCK)), a single
+ *                   load vector (n_rows = 1, e.g. after an all-reduce over
+ *                   data-parallel ranks), or one row per rank
+ *   gamma   update step (finite)
+ *   bias    [E] fp32 device, updated in place
+ *   load    [E] int32 device, receives load[e]; may be NULL
+ * 1 <= E <= 1024.  n_rows = 0 is a no-op returning MOE_OK (nothing written).
+ * Ordered on the stream; overlapping calls on the same bias race.
+ */
+int moe_bias_update(int64_t n_rows, int32_t E, const int32_t* counts, float gamma, float* bias,
+                    int32_t* load, moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,6 +9,7 @@ library is missing, or a tensor is not on the GPU, calls raise.
     dispatch(shape, topk_idx, block_counts, x) -> counts, offsets, dest, src, xp, xp_scale
     expert_ffn(offsets, max_rows, xp, w13, w2) -> yp
     combine(shape, dest, topk_w, yp, ysh)    -> out
+    bias_update(block_counts, bias, gamma)   -> load (bias updated in place)
     MoELayer                                 weights + buffers, forward(x) = the four calls
 """
 from __future__ import annotations
@@ -23,7 +24,7 @@ from ._lib import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN, MOE_F
                    MOE_FP8_TILE, MOE_ROUTE_BLOCK, MOE_ROUTE_LOGITS_IN, MoeError, MoeShape)
 
 __all__ = ["shape", "gate_prepare", "route", "dispatch", "expert_ffn", "combine",
-           "quantize_blocks_e4m3", "quantize_rows_e4m3", "MoELayer", "MoeError", "lib"]
+           "quantize_blocks_e4m3", "quantize_rows_e4m3", "bias_update", "MoELayer", "MoeError", "lib"]
 
 
 def lib():
@@ -242,6 +243,26 @@ def quantize_blocks_e4m3(w: torch.Tensor, q=None, scale=None):
     st = lib().moe_quantize_blocks_e4m3(n, rows, cols, _ptr(w), _ptr(q), _ptr(scale), _stream())
     _lib.check("moe_quantize_blocks_e4m3", st)
     return q, scale
+
+
+def bias_update(counts: torch.Tensor, bias: torch.Tensor, gamma: float,
+                load: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bias[e] += gamma * sign(mean load - load[e]) in place, with load[e] the
+    column sums of counts [n_rows, E] (moe_route's block counts, or one load
+    vector).  Returns load [E] int32 (allocated when not given)."""
+    E = bias.numel()
+    if bias.dtype != torch.float32 or counts.dtype != torch.int32:
+        raise TypeError("bias must be float32 and counts int32")
+    if not (bias.is_contiguous() and counts.is_contiguous()):
+        raise ValueError("bias and counts must be contiguous")
+    n_rows = counts.numel() // E if E else 0
+    if load is None:
+        load = torch.empty(E, dtype=torch.int32, device=bias.device)
+    _need(counts, n_rows * E, "counts")
+    _need(load, E, "load")
+    st = lib().moe_bias_update(n_rows, E, _ptr(counts), float(gamma), _ptr(bias), _ptr(load), _stream())
+    _lib.check("moe_bias_update", st)
+    return load
 
 
 from .layer import MoELayer  # noqa: E402

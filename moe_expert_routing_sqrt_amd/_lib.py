@@ -35,6 +35,7 @@ class MoeError(RuntimeError):
 
 
 _P = ctypes.c_void_p
+_F32 = ctypes.c_float
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
@@ -53,6 +54,7 @@ SIGNATURES = {
     "moe_combine": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _P, _INT, _P, _P, _INT, _INT, _P]),
     "moe_quantize_blocks_e4m3": (_INT, [_I64, _I32, _I32, _P, _P, _P, _P]),
     "moe_quantize_rows_e4m3": (_INT, [_I64, _I32, _P, _P, _P, _P]),
+    "moe_bias_update": (_INT, [_I64, _I32, _P, _F32, _P, _P, _P]),
 }
 
 _lib = None

@@ -3,6 +3,8 @@
 // allocates, frees or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "common.h"
 #include "launch.h"
 #include "moe.h"
@@ -204,6 +206,14 @@ int moe_quantize_blocks_e4m3(int64_t n, int32_t rows, int32_t cols, const float*
     return MOE_ERR_INVALID_ARG;
   if (rows % MOE_FP8_TILE != 0 || cols % MOE_FP8_TILE != 0) return MOE_ERR_UNSUPPORTED;
   return hip_status(launch_quantize_blocks(n, rows, cols, w, q, scale, as_stream(stream)));
+}
+
+int moe_bias_update(int64_t n_rows, int32_t E, const int32_t* counts, float gamma, float* bias,
+                    int32_t* load, moe_stream_t stream) {
+  if (n_rows < 0 || E < 1 || E > kMaxExperts || !std::isfinite(gamma)) return MOE_ERR_INVALID_ARG;
+  if (n_rows == 0) return MOE_OK;
+  if (counts == nullptr || bias == nullptr) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_bias_update(n_rows, E, counts, gamma, bias, load, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -11,8 +11,8 @@ from typing import Optional, Sequence
 import torch
 
 from . import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN, MOE_FFN_UP, MOE_FP8_TILE,
-               combine, dispatch, expert_ffn, gate_prepare, n_blocks, quantize_blocks_e4m3,
-               quantize_rows_e4m3, route, shape)
+               bias_update, combine, dispatch, expert_ffn, gate_prepare, n_blocks,
+               quantize_blocks_e4m3, quantize_rows_e4m3, route, shape)
 
 STAGES = ("route", "dispatch", "ffn_up", "ffn_down", "shared", "combine")
 
@@ -69,6 +69,15 @@ class MoELayer:
                 self.sh_xq = torch.empty((T, d), dtype=torch.uint8, device=dev)
                 self.sh_xs = torch.empty((T, d // MOE_FP8_TILE), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, d), dtype=torch.float32 if self.local else act, device=dev)
+
+    def update_bias(self, gamma: float) -> torch.Tensor:
+        """Auxiliary-loss-free balancing step after a forward: moves each
+        expert's routing bias by gamma towards the mean load of the last
+        batch (moe_bias_update on the route's block counts).  Returns the
+        per-expert load [E]."""
+        if not hasattr(self, "load"):
+            self.load = torch.empty(self.E, dtype=torch.int32, device=self.bias.device)
+        return bias_update(self.block_counts, self.bias, gamma, self.load)
 
     def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
                 marks: Optional[Sequence[torch.cuda.Event]] = None) -> torch.Tensor:

@@ -121,3 +121,15 @@ def test_prep_checks():
     assert L.moe_quantize_blocks_e4m3(1, 100, 128, FAKE, FAKE, FAKE, None) == -2
     assert L.moe_quantize_blocks_e4m3(1, 128, 128, None, FAKE, FAKE, None) == -1
     assert L.moe_quantize_blocks_e4m3(0, 128, 128, FAKE, FAKE, FAKE, None) == 0
+
+
+def test_bias_update_checks():
+    bad = ctypes.c_void_p(16)  # never dereferenced: every case below fails on the host
+    assert L.moe_bias_update(0, 16, None, 0.01, None, None, None) == _lib.MOE_OK  # no rows: no-op
+    assert L.moe_bias_update(-1, 16, bad, 0.01, bad, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_bias_update(4, 0, bad, 0.01, bad, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_bias_update(4, 1025, bad, 0.01, bad, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_bias_update(4, 16, None, 0.01, bad, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_bias_update(4, 16, bad, 0.01, None, None, None) == _lib.MOE_ERR_INVALID_ARG
+    for g in (float("inf"), float("nan")):
+        assert L.moe_bias_update(4, 16, bad, g, bad, None, None) == _lib.MOE_ERR_INVALID_ARG
