@@ -17,6 +17,8 @@ Stages (pages cited by title and section):
               Implemented: 6*d*d_ff flops per token-expert pair)
   combine   - gate-weighted sum back in token order (deepmox ch.5)
   fp8       - e4m3 block quantisation for the fp8 workload
+  hash_route - hash router: experts fixed by a Philox hash of the token id
+              (mastering-deepseek-v4, Implemented: hash router for early layers)
   balance   - per-expert bias update from the batch's expert load
               (auxiliary-loss-free balancing; mastering-deepseek-v4, Implemented
               and Measured)
