@@ -25,6 +25,7 @@ METRIC = "MoE-layer fwd tokens/sec on 1 MI355X; GEMM MFMA % peak; route/permute 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
+HASH_SEED = 7
 
 # HBM traffic of the routed up-projection launch, per launch, from two
 # rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over
@@ -52,14 +53,18 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3")
     ap.add_argument("--cpu-sample", type=int, default=512, help="tokens the CPU oracle runs (0: skip)")
+    ap.add_argument("--router", default="topk", choices=("topk", "hash"),
+                    help="topk: the affinity router; hash: experts from a hash of synthetic token ids")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 2 GiB copy (counter calibration for --pmc passes)")
     return ap.parse_args()
 
 
-def workload_name(cfg) -> str:
+def workload_name(cfg, router="topk") -> str:
     s = (f"{cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} G={cfg.G} k={cfg.k} M={cfg.M} d_ff={cfg.d_ff} "
          f"{cfg.dtype}")
+    if router == "hash":
+        s += ", hash router (Philox of Zipf(1.1) token ids over 65536)"
     if cfg.local:
         s += f" experts [{cfg.e_begin},{cfg.e_end}) only"
     else:
@@ -129,12 +134,12 @@ def copy_probe(torch, dev):
     torch.cuda.empty_cache()
 
 
-def cpu_baseline(cfg, inp, ex, S):
+def cpu_baseline(cfg, inp, ex, S, ids=None):
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
 
-    from oracle import combine as OC, dispatch as OD, ffn as OF, route as OR
+    from oracle import combine as OC, dispatch as OD, ffn as OF, hash_route as OH, route as OR
 
     S = min(S, cfg.T)
     x = inp["x"][:S].float().cpu().numpy()
@@ -149,7 +154,10 @@ def cpu_baseline(cfg, inp, ex, S):
     sh2 = ex["sh_w2"][0].cpu()
     f = lambda t: t.float().numpy()
     t0 = time.perf_counter()
-    L, idx, w = OR.route(x, wg, bias, cfg.G, cfg.M, cfg.k, cfg.gk, off)
+    if ids is None:
+        L, idx, w = OR.route(x, wg, bias, cfg.G, cfg.M, cfg.k, cfg.gk, off)
+    else:
+        idx, w = OH.hash_route(ids[:S], cfg.E, cfg.k, HASH_SEED)
     counts, offsets, dest, src = OD.dispatch(idx, cfg.E, cfg.e_begin, cfg.e_end)
     yp, _ = OF.grouped_ffn(OD.pack(x, src), offsets, None, None,
                            weight_fn=lambda i: (f(w13_h[i]), f(w2_h[i])))
@@ -188,13 +196,14 @@ def main():
     layer = M.MoELayer(cfg.T, cfg.d, cfg.E, cfg.G, cfg.M, cfg.k, cfg.d_ff, cfg.dtype, inp["w_gate"],
                        inp["bias"], ex["w13"], ex["w2"], ex["sh_w13"], ex["sh_w2"],
                        logit_offset=inp["logit_offset"], e_begin=cfg.e_begin, e_end=cfg.e_end,
-                       group_topk=cfg.gk)
+                       group_topk=cfg.gk, router=a.router, hash_seed=HASH_SEED)
     x = inp["x"]
+    ids = gen.token_ids(cfg, device=dev) if a.router == "hash" else None
     torch.cuda.synchronize()
-    print(f"setup {time.perf_counter() - t_setup:.1f}s: {workload_name(cfg)}", file=sys.stderr, flush=True)
+    print(f"setup {time.perf_counter() - t_setup:.1f}s: {workload_name(cfg, a.router)}", file=sys.stderr, flush=True)
 
     for _ in range(a.warmup):
-        layer.forward(x)
+        layer.forward(x, token_ids=ids)
     torch.cuda.synchronize()
     print(f"warmup {a.warmup} done", file=sys.stderr, flush=True)
 
@@ -205,7 +214,7 @@ def main():
     wall0 = time.perf_counter()
     start.record()
     for i in range(a.steps):
-        layer.forward(x, marks=marks[i])
+        layer.forward(x, marks=marks[i], token_ids=ids)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -237,7 +246,10 @@ def main():
     tf = lambda flops, ms: flops / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
     gbs = lambda byts, ms: byts / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
     stages = {
-        "route": {"ms": st_ms["route"], "gate_tflops": tf(alg["route_flops"], st_ms["route"])},
+        "route": ({"ms": st_ms["route"], "gate_tflops": tf(alg["route_flops"], st_ms["route"])}
+                  if a.router == "topk" else
+                  {"ms": st_ms["route"], "kind": "hash router",
+                   "bytes": cfg.T * 4 + cfg.T * cfg.k * 8 + ((cfg.T + 63) // 64) * cfg.E * 4}),
         "dispatch": {"ms": st_ms["dispatch"], "gb_s": gbs(alg["dispatch_bytes"](rows), st_ms["dispatch"])},
         "ffn_up": {"ms": st_ms["ffn_up"], "tflops": tf(alg["ffn_up_flops"](rows), st_ms["ffn_up"])},
         "ffn_down": {"ms": st_ms["ffn_down"], "tflops": tf(alg["ffn_down_flops"](rows), st_ms["ffn_down"])},
@@ -267,7 +279,7 @@ def main():
         "vs_baseline": None,
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "e4m3"}[cfg.dtype],
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02^2) weights, U(-0.1,0.1) bias)",
-        "config": {"workload": workload_name(cfg), "T": cfg.T, "d": cfg.d, "E": cfg.E, "G": cfg.G,
+        "config": {"workload": workload_name(cfg, a.router), "router": a.router, "T": cfg.T, "d": cfg.d, "E": cfg.E, "G": cfg.G,
                    "k": cfg.k, "M": cfg.M, "d_ff": cfg.d_ff, "routed_rows": rows},
         "roofline": {"kernel": "routed up-projection GEMM + SwiGLU (moe_expert_ffn MOE_FFN_UP)",
                      "bound": "mfma", "achieved": up["tflops"], "peak": peak_mm, "unit": "TFLOP/s",
@@ -283,7 +295,8 @@ def main():
     }
     if a.cpu_sample > 0:
         print("cpu baseline ...", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, ex, a.cpu_sample)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, ex, a.cpu_sample,
+                                              None if ids is None else ids.cpu().numpy())
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result))

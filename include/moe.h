@@ -230,6 +230,29 @@ int moe_quantize_blocks_e4m3(int64_t n, int32_t rows, int32_t cols, const float*
                              float* scale, moe_stream_t stream);
 
 /*
+ * moe_route_hash - hash router (mastering-deepseek-v4 "MoE + Expert-Parallel
+ * Overlap (Exp08)", Implemented: a hash router emulates the early layers; a
+ * token's experts follow from its token id).  Replaces moe_route; dispatch,
+ * the expert FFN and combine are unchanged.  The pages do not give the hash;
+ * this library uses Philox4x64-10 (Salmon et al., SC'11) keyed by (seed, 0)
+ * with counter (token_ids[t] as uint32, block, 0, 0): each 64-bit word u of a
+ * block picks expert floor(u * E / 2^64), repeats are skipped, the first k
+ * distinct experts are listed in draw order; after 256 blocks any empty slot
+ * takes the smallest unused experts.  Groups (G, M) play no part.
+ *   shape      uses T, E, k (1 <= k <= min(E, 16), E <= 1024)
+ *   token_ids  [T] int32 device (vocabulary ids; equal ids get equal experts)
+ *   seed       key of the hash (one per layer)
+ *   logits     [T, E] fp32 device or NULL.  NULL: topk_w = 1/k.  Otherwise
+ *              topk_w[t,j] = s_j / (s_0 + ... + s_{k-1}) (left to right) with
+ *              s = sqrt(softplus(logit)) by the same fp32 sequence as moe_route
+ *   topk_idx   [T, k] int32, topk_w [T, k] fp32, block_counts as moe_route
+ * T = 0 is a no-op returning MOE_OK.
+ */
+int moe_route_hash(const moe_shape* shape, const int32_t* token_ids, uint64_t seed,
+                   const float* logits, int32_t* topk_idx, float* topk_w, int32_t* block_counts,
+                   moe_stream_t stream);
+
+/*
  * moe_bias_update - auxiliary-loss-free load balancing (mastering-deepseek-v4
  * "MoE + Expert-Parallel Overlap (Exp08)", Implemented and Measured: a
  * per-expert bias, updated from the observed expert load, replaces an

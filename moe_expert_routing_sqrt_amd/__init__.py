@@ -6,6 +6,7 @@ runs in the library's HIP kernels.  There is no CPU or PyTorch fallback: if the
 library is missing, or a tensor is not on the GPU, calls raise.
 
     route(shape, x, w_prep, bias)            -> logits, topk_idx, topk_w, block_counts
+    route_hash(shape, token_ids, seed)       -> topk_idx, topk_w, block_counts
     dispatch(shape, topk_idx, block_counts, x) -> counts, offsets, dest, src, xp, xp_scale
     expert_ffn(offsets, max_rows, xp, w13, w2) -> yp
     combine(shape, dest, topk_w, yp, ysh)    -> out
@@ -23,7 +24,7 @@ from . import _lib
 from ._lib import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN, MOE_FFN_UP,  # noqa: F401
                    MOE_FP8_TILE, MOE_ROUTE_BLOCK, MOE_ROUTE_LOGITS_IN, MoeError, MoeShape)
 
-__all__ = ["shape", "gate_prepare", "route", "dispatch", "expert_ffn", "combine",
+__all__ = ["shape", "gate_prepare", "route", "route_hash", "dispatch", "expert_ffn", "combine",
            "quantize_blocks_e4m3", "quantize_rows_e4m3", "bias_update", "MoELayer", "MoeError", "lib"]
 
 
@@ -113,6 +114,30 @@ def route(sh: MoeShape, x: Optional[torch.Tensor], w_prep: Optional[torch.Tensor
                          MOE_ROUTE_LOGITS_IN if logits_in else 0, _stream())
     _lib.check("moe_route", st)
     return logits, idx, w, block_counts
+
+
+def route_hash(sh: MoeShape, token_ids: torch.Tensor, seed: int, logits: Optional[torch.Tensor] = None,
+               idx=None, w=None, block_counts=None):
+    """Hash router: each token's k experts from a Philox hash of its token id
+    (int32 [T]); weights 1/k, or the renormalised affinities of those experts
+    when logits [T, E] are given."""
+    T, E, k = sh.T, sh.E, sh.k
+    dev = token_ids.device
+    if token_ids.dtype != torch.int32:
+        raise TypeError("token_ids must be int32")
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev) if idx is None else idx
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
+    if block_counts is None:
+        block_counts = torch.empty((n_blocks(T), E), dtype=torch.int32, device=dev)
+    _need(token_ids, T, "token_ids")
+    _need(idx, T * k, "topk_idx")
+    _need(w, T * k, "topk_w")
+    _need(block_counts, n_blocks(T) * E, "block_counts")
+    _need(logits, T * E, "logits")
+    st = lib().moe_route_hash(ctypes.byref(sh), _ptr(token_ids), int(seed) & ((1 << 64) - 1), _ptr(logits),
+                              _ptr(idx), _ptr(w), _ptr(block_counts), _stream())
+    _lib.check("moe_route_hash", st)
+    return idx, w, block_counts
 
 
 def dispatch_workspace_bytes(sh: MoeShape, e_begin=0, e_end=None) -> int:

@@ -55,6 +55,7 @@ SIGNATURES = {
     "moe_quantize_blocks_e4m3": (_INT, [_I64, _I32, _I32, _P, _P, _P, _P]),
     "moe_quantize_rows_e4m3": (_INT, [_I64, _I32, _P, _P, _P, _P]),
     "moe_bias_update": (_INT, [_I64, _I32, _P, _F32, _P, _P, _P]),
+    "moe_route_hash": (_INT, [ctypes.POINTER(MoeShape), _P, ctypes.c_uint64, _P, _P, _P, _P, _P]),
 }
 
 _lib = None

@@ -208,6 +208,19 @@ int moe_quantize_blocks_e4m3(int64_t n, int32_t rows, int32_t cols, const float*
   return hip_status(launch_quantize_blocks(n, rows, cols, w, q, scale, as_stream(stream)));
 }
 
+int moe_route_hash(const moe_shape* shape, const int32_t* token_ids, uint64_t seed,
+                   const float* logits, int32_t* topk_idx, float* topk_w, int32_t* block_counts,
+                   moe_stream_t stream) {
+  if (shape == nullptr) return MOE_ERR_INVALID_ARG;
+  if (shape->T < 0 || shape->E < 1 || shape->k < 1 || shape->k > shape->E) return MOE_ERR_INVALID_ARG;
+  if (shape->E > kMaxExperts || shape->k > 16) return MOE_ERR_UNSUPPORTED;
+  if (shape->T == 0) return MOE_OK;
+  if (token_ids == nullptr || topk_idx == nullptr || topk_w == nullptr || block_counts == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_hash_route(token_ids, shape->T, shape->E, shape->k, seed, logits, topk_idx,
+                                      topk_w, block_counts, as_stream(stream)));
+}
+
 int moe_bias_update(int64_t n_rows, int32_t E, const int32_t* counts, float gamma, float* bias,
                     int32_t* load, moe_stream_t stream) {
   if (n_rows < 0 || E < 1 || E > kMaxExperts || !std::isfinite(gamma)) return MOE_ERR_INVALID_ARG;

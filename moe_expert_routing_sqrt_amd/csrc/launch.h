@@ -58,6 +58,11 @@ hipError_t launch_quantize_rows(int64_t rows, int cols, const uint16_t* x, uint8
 hipError_t launch_quantize_blocks(int64_t n, int rows, int cols, const float* w, uint8_t* q,
                                   float* scale, hipStream_t s);
 
+// hash router
+hipError_t launch_hash_route(const int32_t* ids, int64_t T, int E, int k, uint64_t seed,
+                             const float* logits, int32_t* idx, float* w, int32_t* block_counts,
+                             hipStream_t s);
+
 // load balancing
 hipError_t launch_bias_update(int64_t n_rows, int E, const int32_t* counts, float gamma, float* bias,
                               int32_t* load, hipStream_t s);

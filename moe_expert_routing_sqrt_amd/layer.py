@@ -12,7 +12,7 @@ import torch
 
 from . import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN, MOE_FFN_UP, MOE_FP8_TILE,
                bias_update, combine, dispatch, expert_ffn, gate_prepare, n_blocks,
-               quantize_blocks_e4m3, quantize_rows_e4m3, route, shape)
+               quantize_blocks_e4m3, quantize_rows_e4m3, route, route_hash, shape)
 
 STAGES = ("route", "dispatch", "ffn_up", "ffn_down", "shared", "combine")
 
@@ -22,7 +22,8 @@ class MoELayer:
                  w_gate: torch.Tensor, bias: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor,
                  sh_w13: Optional[torch.Tensor] = None, sh_w2: Optional[torch.Tensor] = None,
                  logit_offset: Optional[torch.Tensor] = None, e_begin: int = 0,
-                 e_end: Optional[int] = None, group_topk: Optional[int] = None):
+                 e_end: Optional[int] = None, group_topk: Optional[int] = None,
+                 router: str = "topk", hash_seed: int = 0):
         dev = bias.device
         self.sh = shape(T, d, E, G, M, k, d_ff, group_topk)
         self.T, self.d, self.E, self.k, self.d_ff = T, d, E, k, d_ff
@@ -31,6 +32,9 @@ class MoELayer:
         self.dtype = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_E4M3}[dtype]
         self.bias = bias
         self.logit_offset = logit_offset
+        if router not in ("topk", "hash"):
+            raise ValueError("router must be 'topk' or 'hash'")
+        self.router, self.hash_seed = router, hash_seed
         self.w_prep = gate_prepare(w_gate)
 
         # expert weights in the compute format (fp8: e4m3 codes + 128x128 block scales)
@@ -80,17 +84,25 @@ class MoELayer:
         return bias_update(self.block_counts, self.bias, gamma, self.load)
 
     def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
-                marks: Optional[Sequence[torch.cuda.Event]] = None) -> torch.Tensor:
+                marks: Optional[Sequence[torch.cuda.Event]] = None,
+                token_ids: Optional[torch.Tensor] = None) -> torch.Tensor:
         """One layer forward.  `marks`: optional 7 events recorded on the current
-        stream around the six stages (STAGES)."""
+        stream around the six stages (STAGES).  With router="hash" the experts
+        come from `token_ids` (int32 [T]) and the gate weights are 1/k."""
         def mark(i):
             if marks is not None:
                 marks[i].record()
 
         sh = self.sh
         mark(0)
-        route(sh, x, self.w_prep, self.bias, self.logit_offset, logits=self.logits, idx=self.idx,
-              w=self.topk_w, block_counts=self.block_counts)
+        if self.router == "hash":
+            if token_ids is None:
+                raise ValueError("the hash router needs token_ids")
+            route_hash(sh, token_ids, self.hash_seed, idx=self.idx, w=self.topk_w,
+                       block_counts=self.block_counts)
+        else:
+            route(sh, x, self.w_prep, self.bias, self.logit_offset, logits=self.logits, idx=self.idx,
+                  w=self.topk_w, block_counts=self.block_counts)
         mark(1)
         self.dbufs = dispatch(sh, self.idx, self.block_counts, x, self.e_begin, self.e_end,
                               out_dtype=self.dtype if self.dtype == MOE_E4M3 else None,

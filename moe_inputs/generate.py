@@ -22,13 +22,15 @@ import torch
 from .configs import MoEConfig
 
 # stream ids
-X, W_GATE, BIAS, W1, W3, W2, SH_W1, SH_W3, SH_W2 = range(9)
+X, W_GATE, BIAS, W1, W3, W2, SH_W1, SH_W3, SH_W2, TOKEN_IDS = range(10)
 
 X_STD = 1.0
 W_STD = 0.02
 BIAS_HALF_WIDTH = 0.1
 ZIPF_S = 1.2
 ZIPF_SPAN = 2.0
+VOCAB = 65536          # token-id range for the hash-router workload
+TOKEN_ZIPF_S = 1.1     # token frequency ~ rank^-1.1 (text-like: few ids very common)
 
 
 def _gen(device, seed: int, tensor_id: int, expert: int = 0) -> torch.Generator:
@@ -115,3 +117,18 @@ def make_experts(cfg: MoEConfig, device="cpu", experts=None, dtype=None):
         sh13[i].copy_(a)
         sh2[i].copy_(b)
     return {"w13": w13, "w2": w2, "sh_w13": sh13, "sh_w2": sh2, "experts": experts}
+
+
+def token_ids(cfg: MoEConfig, device="cpu") -> torch.Tensor:
+    """int32 [T] token ids for the hash router: ranks drawn with probability
+    proportional to r^-TOKEN_ZIPF_S over r = 1..VOCAB, then mapped through a
+    fixed seeded permutation of the vocabulary (so common ids are not the
+    small ones)."""
+    ss = np.random.SeedSequence([cfg.seed, TOKEN_IDS])
+    rng = np.random.default_rng(ss)
+    r = np.arange(1, VOCAB + 1, dtype=np.float64)
+    p = r ** (-TOKEN_ZIPF_S)
+    p /= p.sum()
+    ranks = rng.choice(VOCAB, size=cfg.T, p=p)
+    perm = rng.permutation(VOCAB)
+    return torch.from_numpy(perm[ranks].astype(np.int32)).to(device)

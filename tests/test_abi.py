@@ -133,3 +133,21 @@ def test_bias_update_checks():
     assert L.moe_bias_update(4, 16, bad, 0.01, None, None, None) == _lib.MOE_ERR_INVALID_ARG
     for g in (float("inf"), float("nan")):
         assert L.moe_bias_update(4, 16, bad, g, bad, None, None) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_route_hash_checks():
+    bad = ctypes.c_void_p(16)  # never dereferenced: every case below fails on the host
+    def sh(T, E, k):
+        return ctypes.byref(_lib.MoeShape(T, 64, E, 1, 1, k, 1, 32))
+    assert L.moe_route_hash(sh(0, 16, 4), None, 1, None, None, None, None, None) == _lib.MOE_OK
+    assert L.moe_route_hash(None, bad, 1, None, bad, bad, bad, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_hash(sh(-1, 16, 4), bad, 1, None, bad, bad, bad, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_hash(sh(8, 4, 5), bad, 1, None, bad, bad, bad, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_hash(sh(8, 16, 0), bad, 1, None, bad, bad, bad, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_hash(sh(8, 2048, 4), bad, 1, None, bad, bad, bad, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_route_hash(sh(8, 64, 17), bad, 1, None, bad, bad, bad, None) == _lib.MOE_ERR_UNSUPPORTED
+    for i in range(4):
+        ptrs = [bad, bad, bad, bad]
+        ptrs[i] = None
+        assert L.moe_route_hash(sh(8, 16, 4), ptrs[0], 1, None, ptrs[1], ptrs[2], ptrs[3],
+                                None) == _lib.MOE_ERR_INVALID_ARG
