@@ -293,6 +293,25 @@ def main():
         "after_step": {"bias_update": {"us": bu_us, "bytes": bu_bytes, "gb_s": bu_bytes / (bu_us * 1e-6) / 1e9,
                                        "bound": "latency (one work-group)"}},
     }
+    # the page's exposed/hidden communication model, instantiated with this
+    # run's measured routed-expert throughput and MI355X xGMI link figures
+    from moe_expert_routing_sqrt_amd import overlap as OV
+    if not cfg.local:
+        C_meas = (alg["ffn_up_flops"](rows) + alg["ffn_down_flops"](rows)) / ((st_ms["ffn_up"] + st_ms["ffn_down"]) * 1e-3)
+        pts = {"ib_50GBs": 50e9, "one_xgmi_link": OV.XGMI_LINK_GBS * 1e9, "ep4_xgmi": OV.ep_bandwidth(4),
+               "ep8_xgmi": OV.ep_bandwidth(8)}
+        sw = {}
+        for name, B in pts.items():
+            r = OV.model(C_meas, B, cfg.d, cfg.d_ff, pairs=rows)
+            sw[name] = {"B_GBs": B / 1e9, "t_comp_ms": r["t_comp"] * 1e3, "t_comm_ms": r["t_comm"] * 1e3,
+                        "exposed_ms": r["exposed"] * 1e3, "utilization": r["utilization"],
+                        "speedup_vs_serial": r["speedup"]}
+        result["overlap_model"] = {
+            "C_measured_tflops": C_meas / 1e12, "pairs_per_gpu": rows,
+            "crossover_flops_per_byte": OV.crossover_intensity(cfg.d, cfg.d_ff),
+            "crossover_bandwidth_GBs": OV.crossover_bandwidth(C_meas, cfg.d, cfg.d_ff) / 1e9,
+            "points": sw,
+            "one_gpu_local_exchange_ms": st_ms["dispatch"] + st_ms["combine"]}
     if a.cpu_sample > 0:
         print("cpu baseline ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, inp, ex, a.cpu_sample,
