@@ -19,6 +19,9 @@ Stages (pages cited by title and section):
   fp8       - e4m3 block quantisation for the fp8 workload
   hash_route - hash router: experts fixed by a Philox hash of the token id
               (mastering-deepseek-v4, Implemented: hash router for early layers)
+  backward  - the layer's backward: combine, expert dgrad/wgrad, dispatch and
+              gate gradients (deepmox ch.5: the backward splits into input and
+              weight gradients and carries its own exchanges)
   balance   - per-expert bias update from the batch's expert load
               (auxiliary-loss-free balancing; mastering-deepseek-v4, Implemented
               and Measured)
