@@ -230,6 +230,73 @@ int moe_quantize_blocks_e4m3(int64_t n, int32_t rows, int32_t cols, const float*
                              float* scale, moe_stream_t stream);
 
 /*
+ * ---------------------------------------------------------------- backward
+ * The layer's backward (deepmox ch.5 "The network becomes part of the forward
+ * pass": the backward carries its own communication and splits into the
+ * gradient for the input and the gradient for the weights).  The pages give
+ * no formulas; these are the exact derivatives of the forward above with the
+ * expert selection held fixed (it is piecewise constant) and no gradient for
+ * the routing bias (it steers selection and follows moe_bias_update).  Call
+ * order for g = d loss / d out:
+ *   moe_combine_backward     -> d_yp, d_topk_w          (d_ysh = g)
+ *   moe_expert_ffn_backward  routed experts (d_yp) and the shared expert (g)
+ *   moe_dispatch_backward    dx = shared-expert dx + sum over a token's rows
+ *   moe_route_backward       dx += gate path, dW_g
+ */
+
+/*
+ * moe_combine_backward - for out[t] = ysh[t] + sum_j w[t,j] yp[dest[t,j]]:
+ *   d_yp[dest[t,j]] = topk_w[t,j] * grad_out[t]       bf16 [rows, d]
+ *   d_topk_w[t,j]   = <grad_out[t], yp[dest[t,j]]>     fp32 [T, k] (0 for dest = -1)
+ * yp in y_dtype, grad_out in g_dtype (MOE_BF16 or MOE_F32).  Rows of d_yp that
+ * no slot points at are not written.  The dot products are reduced in a fixed
+ * order (deterministic).
+ */
+int moe_combine_backward(const moe_shape* shape, const int32_t* dest, const float* topk_w, const void* yp,
+                         int y_dtype, const void* grad_out, int g_dtype, void* d_yp, float* d_topk_w,
+                         moe_stream_t stream);
+
+/*
+ * moe_expert_ffn_backward - backward of the grouped SwiGLU experts
+ * (y = (silu(x W1^T) * (x W3^T)) W2^T per group), bf16 products on the matrix
+ * cores with fp32 accumulation:
+ *   d_xp [max_rows, d]  bf16   d_yp W2 -> d_h; SwiGLU derivative; [da|du] W13
+ *   dw13 [n_exp, 2*d_ff, d] fp32   [da|du]^T xp   (over each group's rows)
+ *   dw2  [n_exp, d, d_ff]   fp32   d_yp^T h
+ * Workspaces (caller-owned, bf16): au [max_rows, 2*d_ff] (the up-projection
+ * is recomputed into it), h [max_rows, d_ff] (d_h, then h), d_au
+ * [max_rows, 2*d_ff].  offsets as moe_expert_ffn (device, [n_exp+1]); NULL with
+ * n_exp = 1 means one group of max_rows rows (the shared expert on x).  Weight
+ * gradients are written (not accumulated); a group with no rows gets zeros.
+ * dtype must be MOE_BF16; d and d_ff multiples of 256.
+ */
+int moe_expert_ffn_backward(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int32_t d, int32_t d_ff,
+                            int dtype, const void* xp, const void* w13, const void* w2, const void* d_yp,
+                            void* au, void* h, void* d_au, void* d_xp, float* dw13, float* dw2,
+                            moe_stream_t stream);
+
+/*
+ * moe_dispatch_backward - dx[t] (+)= d_extra[t] + sum_j d_xp[dest[t,j]] (slots
+ * with dest = -1 skipped), fp32 [T, d].  d_xp [rows, d] and d_extra [T, d] (or
+ * NULL) in xp_dtype (MOE_BF16 or MOE_F32).  accumulate = 1 adds into dx.
+ */
+int moe_dispatch_backward(const moe_shape* shape, const int32_t* dest, const void* d_xp, int xp_dtype,
+                          const void* d_extra, float* dx, int accumulate, moe_stream_t stream);
+
+/*
+ * moe_route_backward - gate path.  With l = logits + logit_offset (as routed),
+ * s = sqrt(softplus(l)) and w_j = s_j / S over a token's k experts:
+ *   dlogits[t, idx_j] = (d_topk_w_j - sum_i w_i d_topk_w_i) / S * sig(l_j) / (2 s_j),
+ *   zero elsewhere (fp32 [T, E], written);
+ *   dx [T, d] fp32 += dlogits W_g^T;   dw_gate [d, E] fp32 = x^T dlogits.
+ * x [T, d] in x_dtype; w_gate [d, E] fp32; logits [T, E] as moe_route wrote
+ * them (without the offset); logit_offset [E] or NULL.
+ */
+int moe_route_backward(const moe_shape* shape, const void* x, int x_dtype, const float* w_gate,
+                       const float* logit_offset, const float* logits, const int32_t* topk_idx,
+                       const float* d_topk_w, float* dlogits, float* dx, float* dw_gate, moe_stream_t stream);
+
+/*
  * moe_route_hash - hash router (mastering-deepseek-v4 "MoE + Expert-Parallel
  * Overlap (Exp08)", Implemented: a hash router emulates the early layers; a
  * token's experts follow from its token id).  Replaces moe_route; dispatch,

@@ -11,6 +11,8 @@ library is missing, or a tensor is not on the GPU, calls raise.
     expert_ffn(offsets, max_rows, xp, w13, w2) -> yp
     combine(shape, dest, topk_w, yp, ysh)    -> out
     bias_update(block_counts, bias, gamma)   -> load (bias updated in place)
+    combine_backward / expert_ffn_backward / dispatch_backward / route_backward
+                                             the layer's backward, stage by stage
     MoELayer                                 weights + buffers, forward(x) = the four calls
 """
 from __future__ import annotations
@@ -24,7 +26,8 @@ from . import _lib
 from ._lib import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN, MOE_FFN_UP,  # noqa: F401
                    MOE_FP8_TILE, MOE_ROUTE_BLOCK, MOE_ROUTE_LOGITS_IN, MoeError, MoeShape)
 
-__all__ = ["shape", "gate_prepare", "route", "route_hash", "dispatch", "expert_ffn", "combine",
+__all__ = ["shape", "gate_prepare", "route", "route_hash", "dispatch", "combine_backward",
+           "expert_ffn_backward", "dispatch_backward", "route_backward", "expert_ffn", "combine",
            "quantize_blocks_e4m3", "quantize_rows_e4m3", "bias_update", "MoELayer", "MoeError", "lib"]
 
 
@@ -268,6 +271,99 @@ def quantize_blocks_e4m3(w: torch.Tensor, q=None, scale=None):
     st = lib().moe_quantize_blocks_e4m3(n, rows, cols, _ptr(w), _ptr(q), _ptr(scale), _stream())
     _lib.check("moe_quantize_blocks_e4m3", st)
     return q, scale
+
+
+def combine_backward(sh: MoeShape, dest, topk_w, yp, grad_out, d_yp=None, d_w=None):
+    """d_yp [rows, d] bf16 and d_topk_w [T, k] fp32 of the combine."""
+    T, k, d = sh.T, sh.k, sh.d
+    rows = yp.shape[0]
+    if d_yp is None:
+        d_yp = torch.empty((rows, d), dtype=torch.bfloat16, device=yp.device)
+    if d_w is None:
+        d_w = torch.empty((T, k), dtype=torch.float32, device=yp.device)
+    if d_yp.dtype != torch.bfloat16 or d_w.dtype != torch.float32:
+        raise TypeError("d_yp must be bf16 and d_w fp32")
+    _need(dest, T * k, "dest")
+    _need(topk_w, T * k, "topk_w")
+    _need(grad_out, T * d, "grad_out")
+    _need(d_w, T * k, "d_topk_w")
+    st = lib().moe_combine_backward(ctypes.byref(sh), _ptr(dest), _ptr(topk_w), _ptr(yp), _dt(yp), _ptr(grad_out),
+                                    _dt(grad_out), _ptr(d_yp), _ptr(d_w), _stream())
+    _lib.check("moe_combine_backward", st)
+    return d_yp, d_w
+
+
+def expert_ffn_backward(offsets: Optional[torch.Tensor], max_rows: int, xp, w13, w2, d_yp, ws: Optional[dict] = None):
+    """Grouped SwiGLU backward: returns dict with d_xp [max_rows, d] bf16, dw13
+    [n, 2*d_ff, d] fp32, dw2 [n, d, d_ff] fp32 (and the bf16 workspaces)."""
+    n_exp = 1 if offsets is None else offsets.numel() - 1
+    d_ff, d = w13.shape[-2] // 2, w13.shape[-1]
+    dev = xp.device
+    b = {} if ws is None else ws
+    bf = torch.bfloat16
+    if "au" not in b:
+        b["au"] = torch.empty((max_rows, 2 * d_ff), dtype=bf, device=dev)
+        b["h"] = torch.empty((max_rows, d_ff), dtype=bf, device=dev)
+        b["d_au"] = torch.empty((max_rows, 2 * d_ff), dtype=bf, device=dev)
+        b["d_xp"] = torch.empty((max_rows, d), dtype=bf, device=dev)
+        b["dw13"] = torch.empty((n_exp, 2 * d_ff, d), dtype=torch.float32, device=dev)
+        b["dw2"] = torch.empty((n_exp, d, d_ff), dtype=torch.float32, device=dev)
+    _need(xp, max_rows * d, "xp")
+    _need(d_yp, max_rows * d, "d_yp")
+    _need(w13, n_exp * 2 * d_ff * d, "w13")
+    _need(w2, n_exp * d * d_ff, "w2")
+    for n, need in (("au", max_rows * 2 * d_ff), ("h", max_rows * d_ff), ("d_au", max_rows * 2 * d_ff),
+                    ("d_xp", max_rows * d), ("dw13", n_exp * 2 * d_ff * d), ("dw2", n_exp * d * d_ff)):
+        _need(b[n], need, n)
+    st = lib().moe_expert_ffn_backward(n_exp, _ptr(offsets), max_rows, d, d_ff, _dt(xp), _ptr(xp), _ptr(w13),
+                                       _ptr(w2), _ptr(d_yp), _ptr(b["au"]), _ptr(b["h"]), _ptr(b["d_au"]),
+                                       _ptr(b["d_xp"]), _ptr(b["dw13"]), _ptr(b["dw2"]), _stream())
+    _lib.check("moe_expert_ffn_backward", st)
+    return b
+
+
+def dispatch_backward(sh: MoeShape, dest, d_xp, d_extra=None, dx=None, accumulate: bool = False):
+    """dx [T, d] fp32 (+)= d_extra + sum_j d_xp[dest[t, j]]."""
+    T, d = sh.T, sh.d
+    if dx is None:
+        dx = torch.empty((T, d), dtype=torch.float32, device=d_xp.device)
+    if dx.dtype != torch.float32:
+        raise TypeError("dx must be fp32")
+    if d_extra is not None and d_extra.dtype != d_xp.dtype:
+        raise TypeError("d_extra must have d_xp's dtype")
+    _need(dest, T * sh.k, "dest")
+    _need(d_extra, T * d, "d_extra")
+    _need(dx, T * d, "dx")
+    st = lib().moe_dispatch_backward(ctypes.byref(sh), _ptr(dest), _ptr(d_xp), _dt(d_xp), _ptr(d_extra), _ptr(dx),
+                                     1 if accumulate else 0, _stream())
+    _lib.check("moe_dispatch_backward", st)
+    return dx
+
+
+def route_backward(sh: MoeShape, x, w_gate, logits, idx, d_w, dx, logit_offset=None, dlogits=None,
+                   dw_gate=None):
+    """Gate path: dlogits [T, E] (written), dx += dlogits W_g^T, dw_gate = x^T dlogits."""
+    T, E, d = sh.T, sh.E, sh.d
+    dev = x.device
+    if dlogits is None:
+        dlogits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if dw_gate is None:
+        dw_gate = torch.empty((d, E), dtype=torch.float32, device=dev)
+    if w_gate.dtype != torch.float32 or dx.dtype != torch.float32:
+        raise TypeError("w_gate and dx must be fp32")
+    _need(x, T * d, "x")
+    _need(w_gate, d * E, "w_gate")
+    _need(logits, T * E, "logits")
+    _need(idx, T * sh.k, "topk_idx")
+    _need(d_w, T * sh.k, "d_topk_w")
+    _need(dlogits, T * E, "dlogits")
+    _need(dx, T * d, "dx")
+    _need(dw_gate, d * E, "dw_gate")
+    _need(logit_offset, E, "logit_offset")
+    st = lib().moe_route_backward(ctypes.byref(sh), _ptr(x), _dt(x), _ptr(w_gate), _ptr(logit_offset), _ptr(logits),
+                                  _ptr(idx), _ptr(d_w), _ptr(dlogits), _ptr(dx), _ptr(dw_gate), _stream())
+    _lib.check("moe_route_backward", st)
+    return dlogits, dw_gate
 
 
 def bias_update(counts: torch.Tensor, bias: torch.Tensor, gamma: float,

@@ -56,6 +56,11 @@ SIGNATURES = {
     "moe_quantize_rows_e4m3": (_INT, [_I64, _I32, _P, _P, _P, _P]),
     "moe_bias_update": (_INT, [_I64, _I32, _P, _F32, _P, _P, _P]),
     "moe_route_hash": (_INT, [ctypes.POINTER(MoeShape), _P, ctypes.c_uint64, _P, _P, _P, _P, _P]),
+    "moe_combine_backward": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _P, _INT, _P, _INT, _P, _P, _P]),
+    "moe_expert_ffn_backward": (_INT, [_I32, _P, _I64, _I32, _I32, _INT, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       _P, _P]),
+    "moe_dispatch_backward": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _INT, _P, _P, _INT, _P]),
+    "moe_route_backward": (_INT, [ctypes.POINTER(MoeShape), _P, _INT, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 _lib = None

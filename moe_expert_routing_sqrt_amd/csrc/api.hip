@@ -208,6 +208,84 @@ int moe_quantize_blocks_e4m3(int64_t n, int32_t rows, int32_t cols, const float*
   return hip_status(launch_quantize_blocks(n, rows, cols, w, q, scale, as_stream(stream)));
 }
 
+int moe_combine_backward(const moe_shape* shape, const int32_t* dest, const float* topk_w, const void* yp,
+                         int y_dtype, const void* grad_out, int g_dtype, void* d_yp, float* d_topk_w,
+                         moe_stream_t stream) {
+  if (shape == nullptr || shape->T < 0 || shape->k < 1 || shape->d < 1) return MOE_ERR_INVALID_ARG;
+  if ((y_dtype != MOE_F32 && y_dtype != MOE_BF16) || (g_dtype != MOE_F32 && g_dtype != MOE_BF16))
+    return MOE_ERR_INVALID_ARG;
+  if (shape->k > 16 || shape->d % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (shape->T == 0) return MOE_OK;
+  if (dest == nullptr || topk_w == nullptr || yp == nullptr || grad_out == nullptr || d_yp == nullptr ||
+      d_topk_w == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine_bwd(shape->T, shape->k, shape->d, dest, topk_w, yp, y_dtype, grad_out,
+                                       g_dtype, static_cast<uint16_t*>(d_yp), d_topk_w, as_stream(stream)));
+}
+
+int moe_expert_ffn_backward(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int32_t d, int32_t d_ff,
+                            int dtype, const void* xp, const void* w13, const void* w2, const void* d_yp,
+                            void* au, void* h, void* d_au, void* d_xp, float* dw13, float* dw2,
+                            moe_stream_t stream) {
+  if (n_exp < 1 || n_exp > kMaxExperts || max_rows < 0 || d < 1 || d_ff < 1) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16 || !ffn_bwd_bf16_supported(d, d_ff)) return MOE_ERR_UNSUPPORTED;
+  if (offsets == nullptr && n_exp != 1) return MOE_ERR_INVALID_ARG;
+  if (xp == nullptr || w13 == nullptr || w2 == nullptr || d_yp == nullptr || au == nullptr || h == nullptr ||
+      d_au == nullptr || d_xp == nullptr || dw13 == nullptr || dw2 == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  const hipStream_t s = as_stream(stream);
+  const auto* X = static_cast<const uint16_t*>(xp);
+  const auto* W13 = static_cast<const uint16_t*>(w13);
+  const auto* W2 = static_cast<const uint16_t*>(w2);
+  const auto* DY = static_cast<const uint16_t*>(d_yp);
+  auto* AU = static_cast<uint16_t*>(au);
+  auto* H = static_cast<uint16_t*>(h);
+  auto* DAU = static_cast<uint16_t*>(d_au);
+  hipError_t e;
+  // [a | u] again (recomputed), d_h = d_y W2, then SwiGLU's derivative (h on the side)
+  if ((e = launch_ffn_store_bf16(n_exp, offsets, max_rows, d, 2 * d_ff, X, W13, AU, s)) != hipSuccess)
+    return hip_status(e);
+  if ((e = launch_ffn_dgrad_bf16(n_exp, offsets, max_rows, d, d_ff, DY, W2, H, s)) != hipSuccess)
+    return hip_status(e);
+  if ((e = launch_swiglu_bwd(offsets == nullptr ? nullptr : offsets + n_exp, max_rows, d_ff, AU, H, DAU, s)) !=
+      hipSuccess)
+    return hip_status(e);
+  // d_x = [da | du] W13, dW2 = d_y^T h, dW13 = [da | du]^T x
+  if ((e = launch_ffn_dgrad_bf16(n_exp, offsets, max_rows, 2 * d_ff, d, DAU, W13, static_cast<uint16_t*>(d_xp),
+                                 s)) != hipSuccess)
+    return hip_status(e);
+  if ((e = launch_ffn_wgrad_bf16(n_exp, offsets, max_rows, d, d_ff, DY, H, dw2, s)) != hipSuccess)
+    return hip_status(e);
+  return hip_status(launch_ffn_wgrad_bf16(n_exp, offsets, max_rows, 2 * d_ff, d, DAU, X, dw13, s));
+}
+
+int moe_dispatch_backward(const moe_shape* shape, const int32_t* dest, const void* d_xp, int xp_dtype,
+                          const void* d_extra, float* dx, int accumulate, moe_stream_t stream) {
+  if (shape == nullptr || shape->T < 0 || shape->k < 1 || shape->d < 1) return MOE_ERR_INVALID_ARG;
+  if ((xp_dtype != MOE_F32 && xp_dtype != MOE_BF16) || (accumulate != 0 && accumulate != 1))
+    return MOE_ERR_INVALID_ARG;
+  if (shape->k > 16 || shape->d % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (shape->T == 0) return MOE_OK;
+  if (dest == nullptr || d_xp == nullptr || dx == nullptr) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(shape->T, shape->k, shape->d, dest, nullptr, d_xp, xp_dtype, d_extra, dx,
+                                   MOE_F32, accumulate, as_stream(stream)));
+}
+
+int moe_route_backward(const moe_shape* shape, const void* x, int x_dtype, const float* w_gate,
+                       const float* logit_offset, const float* logits, const int32_t* topk_idx,
+                       const float* d_topk_w, float* dlogits, float* dx, float* dw_gate, moe_stream_t stream) {
+  if (shape == nullptr || shape->T < 0 || shape->E < 1 || shape->k < 1 || shape->k > shape->E || shape->d < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (shape->k > 16 || shape->E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (shape->T == 0) return MOE_OK;
+  if (x == nullptr || w_gate == nullptr || logits == nullptr || topk_idx == nullptr || d_topk_w == nullptr ||
+      dlogits == nullptr || dx == nullptr || dw_gate == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_gate_bwd(shape->T, shape->d, shape->E, shape->k, x, x_dtype, w_gate, logits,
+                                    logit_offset, topk_idx, d_topk_w, dlogits, dx, dw_gate, as_stream(stream)));
+}
+
 int moe_route_hash(const moe_shape* shape, const int32_t* token_ids, uint64_t seed,
                    const float* logits, int32_t* topk_idx, float* topk_w, int32_t* block_counts,
                    moe_stream_t stream) {

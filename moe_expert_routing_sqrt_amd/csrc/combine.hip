@@ -1,4 +1,5 @@
 // Combine on gfx950: out[t] = ysh[t] + sum_j w[t,j] * yp[dest[t,j]]
+// (w = nullptr: unit weights, which is also the backward of dispatch)
 // (deepmox ch.5 "The network becomes part of the forward pass": the forward
 // chunk ends by combining the expert outputs; zenaique "Why all to all
 // dominates": combine brings FFN outputs back to the token's owner).
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombArgs p) {
   for (int q = tid; q < ntok * p.k; q += kThreads) {
     const int tt = q / p.k, j = q % p.k;
     s_dest[tt * kMaxK + j] = p.dest[(t0 + tt) * p.k + j];
-    s_w[tt * kMaxK + j] = p.w[(t0 + tt) * p.k + j];
+    s_w[tt * kMaxK + j] = p.w == nullptr ? 1.0f : p.w[(t0 + tt) * p.k + j];
   }
   __syncthreads();
   const int nch = p.d / kVec;

@@ -323,22 +323,27 @@ hipError_t launch_ffn_up_bf16(int n_exp, const int32_t* offsets, int64_t max_row
   return launch<MODE_SWIGLU>(a, max_rows, s);
 }
 
-hipError_t launch_ffn_down_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
-                                int d_ff, const uint16_t* h, const uint16_t* w2, uint16_t* yp,
-                                hipStream_t s) {
+hipError_t launch_ffn_store_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int K, int N,
+                                 const uint16_t* A, const uint16_t* B, uint16_t* C, hipStream_t s) {
   FfnArgs a{};
-  a.A = h;
-  a.lda = d_ff;
-  a.B = w2;
-  a.b_group_stride = (int64_t)d * d_ff;
-  a.C = yp;
-  a.ldc = d;
+  a.A = A;
+  a.lda = K;
+  a.B = B;
+  a.b_group_stride = (int64_t)N * K;
+  a.C = C;
+  a.ldc = N;
   a.offsets = offsets;
   a.n_exp = n_exp;
   a.rows_total = max_rows;
-  a.K = d_ff;
-  a.n_tiles = d / BN;
+  a.K = K;
+  a.n_tiles = N / BN;
   return launch<MODE_STORE>(a, max_rows, s);
+}
+
+hipError_t launch_ffn_down_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
+                                int d_ff, const uint16_t* h, const uint16_t* w2, uint16_t* yp,
+                                hipStream_t s) {
+  return launch_ffn_store_bf16(n_exp, offsets, max_rows, d_ff, d, h, w2, yp, s);
 }
 
 }  // namespace moe

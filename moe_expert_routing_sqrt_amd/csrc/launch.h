@@ -34,6 +34,15 @@ hipError_t launch_ffn_up_bf16(int n_exp, const int32_t* offsets, int64_t max_row
 hipError_t launch_ffn_down_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
                                 int d_ff, const uint16_t* h, const uint16_t* w2, uint16_t* yp,
                                 hipStream_t s);
+// C [rows, N] = A [rows, K] x B_g^T with B_g [N, K] per group (plain bf16 store)
+hipError_t launch_ffn_store_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int K, int N,
+                                 const uint16_t* A, const uint16_t* B, uint16_t* C, hipStream_t s);
+// backward products (ffn_bwd_bf16.hip)
+bool ffn_bwd_bf16_supported(int d, int d_ff);
+hipError_t launch_ffn_dgrad_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int K, int N,
+                                 const uint16_t* A, const uint16_t* W, uint16_t* C, hipStream_t s);
+hipError_t launch_ffn_wgrad_bf16(int n_exp, const int32_t* offsets, int64_t rows_total, int M, int N,
+                                 const uint16_t* A, const uint16_t* B, float* C, hipStream_t s);
 hipError_t launch_ffn_simt(int stage, int n_exp, const int32_t* offsets, int64_t max_rows, int d,
                            int d_ff, int dtype, const void* in, const void* w, void* out,
                            hipStream_t s);
@@ -62,6 +71,16 @@ hipError_t launch_quantize_blocks(int64_t n, int rows, int cols, const float* w,
 hipError_t launch_hash_route(const int32_t* ids, int64_t T, int E, int k, uint64_t seed,
                              const float* logits, int32_t* idx, float* w, int32_t* block_counts,
                              hipStream_t s);
+
+// backward (backward.hip)
+hipError_t launch_combine_bwd(int64_t T, int k, int d, const int32_t* dest, const float* w, const void* yp,
+                              int y_dtype, const void* g, int g_dtype, uint16_t* d_yp, float* d_w,
+                              hipStream_t s);
+hipError_t launch_swiglu_bwd(const int32_t* rows_dev, int64_t max_rows, int d_ff, const uint16_t* au,
+                             uint16_t* dh, uint16_t* d_au, hipStream_t s);
+hipError_t launch_gate_bwd(int64_t T, int d, int E, int k, const void* x, int x_dtype, const float* w_gate,
+                           const float* logits, const float* offset, const int32_t* idx, const float* d_w,
+                           float* dL, float* dx, float* dw_gate, hipStream_t s);
 
 // load balancing
 hipError_t launch_bias_update(int64_t n_rows, int E, const int32_t* counts, float gamma, float* bias,

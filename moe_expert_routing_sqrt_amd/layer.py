@@ -11,8 +11,9 @@ from typing import Optional, Sequence
 import torch
 
 from . import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN, MOE_FFN_UP, MOE_FP8_TILE,
-               bias_update, combine, dispatch, expert_ffn, gate_prepare, n_blocks,
-               quantize_blocks_e4m3, quantize_rows_e4m3, route, route_hash, shape)
+               bias_update, combine, combine_backward, dispatch, dispatch_backward, expert_ffn,
+               expert_ffn_backward, gate_prepare, n_blocks, quantize_blocks_e4m3, quantize_rows_e4m3, route,
+               route_backward, route_hash, shape)
 
 STAGES = ("route", "dispatch", "ffn_up", "ffn_down", "shared", "combine")
 
@@ -31,6 +32,7 @@ class MoELayer:
         self.local = (self.e_begin, self.e_end) != (0, E)
         self.dtype = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_E4M3}[dtype]
         self.bias = bias
+        self.w_gate = w_gate
         self.logit_offset = logit_offset
         if router not in ("topk", "hash"):
             raise ValueError("router must be 'topk' or 'hash'")
@@ -130,6 +132,52 @@ class MoELayer:
         out = self.out if out is None else out
         combine(sh, b["dest"], self.topk_w, self.yp, ysh, out=out, accumulate=self.local)
         mark(6)
+        return out
+
+    def backward(self, x: torch.Tensor, grad_out: torch.Tensor,
+                 marks: Optional[Sequence[torch.cuda.Event]] = None) -> dict:
+        """Gradients of the last forward(x) for grad_out = d loss / d out (bf16
+        [T, d]): dx [T, d] fp32, dw_gate [d, E] fp32, dw13 / dw2 of the routed
+        experts and dsh_w13 / dsh_w2 of the shared expert (fp32).  The expert
+        selection of the forward is held fixed; the routing bias gets no
+        gradient.  `marks`: optional 5 events around the four stages
+        (combine, routed experts, shared expert, dispatch + gate)."""
+        if self.dtype != MOE_BF16 or self.local or self.router != "topk":
+            raise ValueError("backward covers the bf16 top-k layer with all experts local")
+        if grad_out.dtype != torch.bfloat16:
+            raise TypeError("grad_out must be bf16")
+
+        def mark(i):
+            if marks is not None:
+                marks[i].record()
+
+        sh, b, dev = self.sh, self.dbufs, x.device
+        if not hasattr(self, "bws"):
+            self.bws = {"routed": {}, "shared": {},
+                        "d_yp": torch.empty((self.max_rows, self.d), dtype=torch.bfloat16, device=dev),
+                        "d_w": torch.empty((self.T, self.k), dtype=torch.float32, device=dev),
+                        "dx": torch.empty((self.T, self.d), dtype=torch.float32, device=dev),
+                        "dlogits": torch.empty((self.T, self.E), dtype=torch.float32, device=dev),
+                        "dw_gate": torch.empty((self.d, self.E), dtype=torch.float32, device=dev)}
+        w = self.bws
+        mark(0)
+        combine_backward(sh, b["dest"], self.topk_w, self.yp, grad_out, w["d_yp"], w["d_w"])
+        mark(1)
+        r = expert_ffn_backward(b["offsets"], self.max_rows, b["xp"], self.w13, self.w2, w["d_yp"], w["routed"])
+        mark(2)
+        sx = None
+        if self.has_shared:
+            s_ = expert_ffn_backward(None, self.T, x, self.sh_w13, self.sh_w2, grad_out, w["shared"])
+            sx = s_["d_xp"]
+        mark(3)
+        dispatch_backward(sh, b["dest"], r["d_xp"], d_extra=sx, dx=w["dx"])
+        route_backward(sh, x, self.w_gate, self.logits, self.idx, w["d_w"], w["dx"],
+                       logit_offset=self.logit_offset, dlogits=w["dlogits"], dw_gate=w["dw_gate"])
+        mark(4)
+        out = {"dx": w["dx"], "dw_gate": w["dw_gate"], "dw13": r["dw13"], "dw2": r["dw2"],
+               "d_topk_w": w["d_w"]}
+        if self.has_shared:
+            out["dsh_w13"], out["dsh_w2"] = w["shared"]["dw13"], w["shared"]["dw2"]
         return out
 
     def _shared_quant_input(self, x):

@@ -151,3 +151,40 @@ def test_route_hash_checks():
         ptrs[i] = None
         assert L.moe_route_hash(sh(8, 16, 4), ptrs[0], 1, None, ptrs[1], ptrs[2], ptrs[3],
                                 None) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_backward_checks():
+    bad = ctypes.c_void_p(16)  # never dereferenced: every case below fails on the host
+    sh = lambda T=8, d=256, E=16, k=4: ctypes.byref(_lib.MoeShape(T, d, E, 4, 2, k, 2, 256))
+    BF, F = _lib.MOE_BF16, _lib.MOE_F32
+    # combine backward
+    assert L.moe_combine_backward(sh(0), None, None, None, BF, None, BF, None, None, None) == _lib.MOE_OK
+    assert L.moe_combine_backward(None, bad, bad, bad, BF, bad, BF, bad, bad, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_combine_backward(sh(), bad, bad, bad, 7, bad, BF, bad, bad, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_combine_backward(sh(k=17), bad, bad, bad, BF, bad, BF, bad, bad, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine_backward(sh(), None, bad, bad, BF, bad, BF, bad, bad, None) == _lib.MOE_ERR_INVALID_ARG
+    # expert FFN backward
+    args = [bad] * 10
+    assert L.moe_expert_ffn_backward(0, bad, 8, 256, 256, BF, *args, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn_backward(2, None, 8, 256, 256, BF, *args, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn_backward(1, None, 8, 256, 256, F, *args, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_ffn_backward(1, None, 8, 256, 128, BF, *args, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_ffn_backward(1, None, 8, 200, 256, BF, *args, None) == _lib.MOE_ERR_UNSUPPORTED
+    for i in range(10):
+        a = list(args)
+        a[i] = None
+        assert L.moe_expert_ffn_backward(1, None, 8, 256, 256, BF, *a, None) == _lib.MOE_ERR_INVALID_ARG
+    # dispatch backward
+    assert L.moe_dispatch_backward(sh(0), None, None, BF, None, None, 0, None) == _lib.MOE_OK
+    assert L.moe_dispatch_backward(sh(), bad, bad, BF, None, bad, 2, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch_backward(sh(), None, bad, BF, None, bad, 0, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch_backward(sh(d=12), bad, bad, BF, None, bad, 0, None) == _lib.MOE_ERR_UNSUPPORTED
+    # route backward
+    assert L.moe_route_backward(sh(0), None, BF, None, None, None, None, None, None, None, None,
+                                None) == _lib.MOE_OK
+    assert L.moe_route_backward(sh(k=20), bad, BF, bad, None, bad, bad, bad, bad, bad, bad,
+                                None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_backward(sh(), bad, 9, bad, None, bad, bad, bad, bad, bad, bad,
+                                None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_backward(sh(), bad, BF, None, None, bad, bad, bad, bad, bad, bad,
+                                None) == _lib.MOE_ERR_INVALID_ARG
