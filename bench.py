@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=512, help="tokens the CPU oracle runs (0: skip)")
     ap.add_argument("--router", default="topk", choices=("topk", "hash"),
                     help="topk: the affinity router; hash: experts from a hash of synthetic token ids")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time forward+backward steps (bf16 top-k workload) and report the backward")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 2 GiB copy (counter calibration for --pmc passes)")
     return ap.parse_args()
@@ -132,6 +134,41 @@ def copy_probe(torch, dev):
     print("copy probe: 3 launches of a 2 GiB fp32 negation", file=sys.stderr, flush=True)
     del src, dst
     torch.cuda.empty_cache()
+
+
+def backward_bench(a, cfg, layer, x, ev, torch, alg, rows):
+    """Forward + backward steps of the bf16 top-k layer; the backward's stages
+    timed with events (combine, routed experts, shared expert, dispatch + gate)."""
+    g = torch.randn((cfg.T, cfg.d), device=x.device, dtype=torch.float32).to(torch.bfloat16)
+    for _ in range(max(1, a.warmup)):
+        layer.forward(x)
+        layer.backward(x, g)
+    torch.cuda.synchronize()
+    steps = max(5, a.steps // 5)
+    fm = [[ev() for _ in range(7)] for _ in range(steps)]
+    bm = [[ev() for _ in range(5)] for _ in range(steps)]
+    s0, s1 = ev(), ev()
+    s0.record()
+    for i in range(steps):
+        layer.forward(x, marks=fm[i])
+        layer.backward(x, g, marks=bm[i])
+    s1.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / steps
+    names = ("combine_bwd", "routed_experts_bwd", "shared_expert_bwd", "dispatch_gate_bwd")
+    st = {n: sum(m[i].elapsed_time(m[i + 1]) for m in bm) / steps for i, n in enumerate(names)}
+    bwd_ms = sum(st.values())
+    # expert backward products: the recomputed up-projection (4 d d_ff per row),
+    # d_h (2), d_x (4), dW2 (2), dW13 (4) = 16 d d_ff per row
+    fl = 16 * cfg.d * cfg.d_ff
+    peak = PEAK_BF16_TFLOPS
+    tf = lambda flops, t: flops / (t * 1e-3) / 1e12
+    return {"steps": steps, "fwd_bwd_ms_per_step": ms, "fwd_bwd_tokens_per_s": cfg.T / (ms * 1e-3),
+            "bwd_ms": bwd_ms, "stages_ms": st,
+            "routed_experts_tflops": tf(fl * rows, st["routed_experts_bwd"]),
+            "routed_experts_frac_mfma": tf(fl * rows, st["routed_experts_bwd"]) / peak,
+            "shared_expert_tflops": tf(fl * cfg.T, st["shared_expert_bwd"]),
+            "flops_note": "16*d*d_ff per row: recomputed up-projection + d_h + d_x + dW2 + dW13"}
 
 
 def cpu_baseline(cfg, inp, ex, S, ids=None):
@@ -293,6 +330,9 @@ def main():
         "after_step": {"bias_update": {"us": bu_us, "bytes": bu_bytes, "gb_s": bu_bytes / (bu_us * 1e-6) / 1e9,
                                        "bound": "latency (one work-group)"}},
     }
+    if a.backward:
+        result["backward"] = backward_bench(a, cfg, layer, x, ev, torch, alg, rows)
+
     # the page's exposed/hidden communication model, instantiated with this
     # run's measured routed-expert throughput and MI355X xGMI link figures
     from moe_expert_routing_sqrt_amd import overlap as OV

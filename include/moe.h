@@ -290,11 +290,15 @@ int moe_dispatch_backward(const moe_shape* shape, const int32_t* dest, const voi
  *   zero elsewhere (fp32 [T, E], written);
  *   dx [T, d] fp32 += dlogits W_g^T;   dw_gate [d, E] fp32 = x^T dlogits.
  * x [T, d] in x_dtype; w_gate [d, E] fp32; logits [T, E] as moe_route wrote
- * them (without the offset); logit_offset [E] or NULL.
+ * them (without the offset); logit_offset [E] or NULL.  dw_gate sums over the
+ * T tokens in up to 16 K-parts held in ws (moe_route_backward_workspace_size
+ * bytes; MOE_ERR_WORKSPACE if smaller), added in part order (deterministic).
  */
+size_t moe_route_backward_workspace_size(const moe_shape* shape);
 int moe_route_backward(const moe_shape* shape, const void* x, int x_dtype, const float* w_gate,
                        const float* logit_offset, const float* logits, const int32_t* topk_idx,
-                       const float* d_topk_w, float* dlogits, float* dx, float* dw_gate, moe_stream_t stream);
+                       const float* d_topk_w, float* dlogits, float* dx, float* dw_gate, void* ws,
+                       size_t ws_bytes, moe_stream_t stream);
 
 /*
  * moe_route_hash - hash router (mastering-deepseek-v4 "MoE + Expert-Parallel

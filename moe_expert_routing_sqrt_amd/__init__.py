@@ -341,7 +341,7 @@ def dispatch_backward(sh: MoeShape, dest, d_xp, d_extra=None, dx=None, accumulat
 
 
 def route_backward(sh: MoeShape, x, w_gate, logits, idx, d_w, dx, logit_offset=None, dlogits=None,
-                   dw_gate=None):
+                   dw_gate=None, ws=None):
     """Gate path: dlogits [T, E] (written), dx += dlogits W_g^T, dw_gate = x^T dlogits."""
     T, E, d = sh.T, sh.E, sh.d
     dev = x.device
@@ -360,8 +360,12 @@ def route_backward(sh: MoeShape, x, w_gate, logits, idx, d_w, dx, logit_offset=N
     _need(dx, T * d, "dx")
     _need(dw_gate, d * E, "dw_gate")
     _need(logit_offset, E, "logit_offset")
+    wsb = lib().moe_route_backward_workspace_size(ctypes.byref(sh))
+    if ws is None and wsb > 0:
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     st = lib().moe_route_backward(ctypes.byref(sh), _ptr(x), _dt(x), _ptr(w_gate), _ptr(logit_offset), _ptr(logits),
-                                  _ptr(idx), _ptr(d_w), _ptr(dlogits), _ptr(dx), _ptr(dw_gate), _stream())
+                                  _ptr(idx), _ptr(d_w), _ptr(dlogits), _ptr(dx), _ptr(dw_gate), _ptr(ws),
+                                  0 if ws is None else ws.numel() * ws.element_size(), _stream())
     _lib.check("moe_route_backward", st)
     return dlogits, dw_gate
 

@@ -60,7 +60,9 @@ SIGNATURES = {
     "moe_expert_ffn_backward": (_INT, [_I32, _P, _I64, _I32, _I32, _INT, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, _P]),
     "moe_dispatch_backward": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _INT, _P, _P, _INT, _P]),
-    "moe_route_backward": (_INT, [ctypes.POINTER(MoeShape), _P, _INT, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_route_backward": (_INT, [ctypes.POINTER(MoeShape), _P, _INT, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                  ctypes.c_size_t, _P]),
+    "moe_route_backward_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MoeShape)]),
 }
 
 _lib = None

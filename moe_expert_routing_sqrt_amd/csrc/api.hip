@@ -271,9 +271,15 @@ int moe_dispatch_backward(const moe_shape* shape, const int32_t* dest, const voi
                                    MOE_F32, accumulate, as_stream(stream)));
 }
 
+size_t moe_route_backward_workspace_size(const moe_shape* shape) {
+  if (shape == nullptr || shape->T <= 0 || shape->d < 1 || shape->E < 1) return 0;
+  return gate_bwd_workspace_bytes(shape->T, shape->d, shape->E);
+}
+
 int moe_route_backward(const moe_shape* shape, const void* x, int x_dtype, const float* w_gate,
                        const float* logit_offset, const float* logits, const int32_t* topk_idx,
-                       const float* d_topk_w, float* dlogits, float* dx, float* dw_gate, moe_stream_t stream) {
+                       const float* d_topk_w, float* dlogits, float* dx, float* dw_gate, void* ws,
+                       size_t ws_bytes, moe_stream_t stream) {
   if (shape == nullptr || shape->T < 0 || shape->E < 1 || shape->k < 1 || shape->k > shape->E || shape->d < 1)
     return MOE_ERR_INVALID_ARG;
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
@@ -282,8 +288,11 @@ int moe_route_backward(const moe_shape* shape, const void* x, int x_dtype, const
   if (x == nullptr || w_gate == nullptr || logits == nullptr || topk_idx == nullptr || d_topk_w == nullptr ||
       dlogits == nullptr || dx == nullptr || dw_gate == nullptr)
     return MOE_ERR_INVALID_ARG;
+  const size_t need = gate_bwd_workspace_bytes(shape->T, shape->d, shape->E);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   return hip_status(launch_gate_bwd(shape->T, shape->d, shape->E, shape->k, x, x_dtype, w_gate, logits,
-                                    logit_offset, topk_idx, d_topk_w, dlogits, dx, dw_gate, as_stream(stream)));
+                                    logit_offset, topk_idx, d_topk_w, dlogits, dx, dw_gate,
+                                    static_cast<float*>(ws), as_stream(stream)));
 }
 
 int moe_route_hash(const moe_shape* shape, const int32_t* token_ids, uint64_t seed,

@@ -191,6 +191,8 @@ struct F32Args {
   int64_t ldc;
   int M, N, K;
   int accumulate;
+  int64_t split_stride;  // split-K: part z writes C + z * split_stride over its K range
+  int k_per_split;
 };
 
 template <typename TA>
@@ -201,14 +203,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const F32Args p) {
   const TA* A = static_cast<const TA*>(p.A);
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int m0 = blockIdx.y * BT, n0 = blockIdx.x * BT;
+  const int kb = blockIdx.z * p.k_per_split;
+  const int ke = min(p.K, kb + p.k_per_split);
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < p.K; k0 += BKs) {
+  for (int k0 = kb; k0 < ke; k0 += BKs) {
     for (int e = tid; e < BT * BKs; e += 256) {
       // contiguous index innermost across threads
       int r, kk;
       if (p.sam == 1) { r = e % BT; kk = e / BT; } else { kk = e % BKs; r = e / BKs; }
       float v = 0.0f;
-      if (m0 + r < p.M && k0 + kk < p.K) {
+      if (m0 + r < p.M && k0 + kk < ke) {
         const int64_t off = (int64_t)(m0 + r) * p.sam + (int64_t)(k0 + kk) * p.sak;
         if constexpr (sizeof(TA) == 2) v = bf16_to_f32(A[off]); else v = A[off];
       }
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const F32Args p) {
       int r, kk;
       if (p.sbn == 1) { r = e % BT; kk = e / BT; } else { kk = e % BKs; r = e / BKs; }
       float v = 0.0f;
-      if (n0 + r < p.N && k0 + kk < p.K) v = p.B[(int64_t)(n0 + r) * p.sbn + (int64_t)(k0 + kk) * p.sbk];
+      if (n0 + r < p.N && k0 + kk < ke) v = p.B[(int64_t)(n0 + r) * p.sbn + (int64_t)(k0 + kk) * p.sbk];
       sB[kk][r] = v;
     }
     __syncthreads();
@@ -244,14 +248,23 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const F32Args p) {
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + tx * 4 + j;
       if (n >= p.N) continue;
-      float* c = p.C + (int64_t)m * p.ldc + n;
+      float* c = p.C + blockIdx.z * p.split_stride + (int64_t)m * p.ldc + n;
       *c = p.accumulate ? *c + acc[i][j] : acc[i][j];
     }
   }
 }
 
-hipError_t launch_f32(const F32Args& a, int a_dtype, hipStream_t s) {
-  const dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
+// sum of the split-K parts in part order: out[i] = ((p0 + p1) + p2) + ...
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* parts, int nparts, int64_t n, float* out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float v = parts[i];
+    for (int z = 1; z < nparts; ++z) v += parts[z * n + i];
+    out[i] = v;
+  }
+}
+
+hipError_t launch_f32(const F32Args& a, int a_dtype, hipStream_t s, int splits = 1) {
+  const dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, splits);
   if (a_dtype == MOE_BF16) hipLaunchKernelGGL(gemm_f32_kernel<uint16_t>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(gemm_f32_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
@@ -284,19 +297,38 @@ hipError_t launch_swiglu_bwd(const int32_t* rows_dev, int64_t max_rows, int d_ff
   return hipGetLastError();
 }
 
+int gate_bwd_splits(int64_t T) {
+  int s = static_cast<int>(T / 1024);
+  return s < 1 ? 1 : (s > 16 ? 16 : s);
+}
+
+size_t gate_bwd_workspace_bytes(int64_t T, int d, int E) {
+  const int s = gate_bwd_splits(T);
+  return s > 1 ? (size_t)s * d * E * sizeof(float) : 0;
+}
+
 hipError_t launch_gate_bwd(int64_t T, int d, int E, int k, const void* x, int x_dtype, const float* w_gate,
                            const float* logits, const float* offset, const int32_t* idx, const float* d_w,
-                           float* dL, float* dx, float* dw_gate, hipStream_t s) {
+                           float* dL, float* dx, float* dw_gate, float* ws, hipStream_t s) {
   hipLaunchKernelGGL(gate_bwd_kernel, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(256), 0, s, T, E, k,
                      logits, offset, idx, d_w, dL);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dx[t][c] += sum_e dL[t][e] W_g[c][e]
-  F32Args a{dL, E, 1, w_gate, E, 1, dx, d, static_cast<int>(T), d, E, 1};
+  F32Args a{dL, E, 1, w_gate, E, 1, dx, d, static_cast<int>(T), d, E, 1, 0, E};
   if ((e = launch_f32(a, MOE_F32, s)) != hipSuccess) return e;
-  // dW_g[c][e] = sum_t x[t][c] dL[t][e]
-  F32Args b{x, 1, d, dL, 1, E, dw_gate, E, d, E, static_cast<int>(T), 0};
-  return launch_f32(b, x_dtype, s);
+  // dW_g[c][e] = sum_t x[t][c] dL[t][e]: K = T split into gate_bwd_splits(T)
+  // parts of the workspace, summed in part order (deterministic)
+  const int splits = gate_bwd_splits(T);
+  const int kps = static_cast<int>((T + splits - 1) / splits + 15) / 16 * 16;
+  F32Args b{x, 1, d, dL, 1, E, splits > 1 ? ws : dw_gate, E, d, E, static_cast<int>(T), 0,
+            (int64_t)d * E, kps};
+  if ((e = launch_f32(b, x_dtype, s, splits)) != hipSuccess || splits == 1) return e;
+  const int64_t n = (int64_t)d * E;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(split_sum_kernel, dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s,
+                     ws, splits, n, dw_gate);
+  return hipGetLastError();
 }
 
 }  // namespace moe

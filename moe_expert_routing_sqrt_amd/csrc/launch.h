@@ -78,9 +78,11 @@ hipError_t launch_combine_bwd(int64_t T, int k, int d, const int32_t* dest, cons
                               hipStream_t s);
 hipError_t launch_swiglu_bwd(const int32_t* rows_dev, int64_t max_rows, int d_ff, const uint16_t* au,
                              uint16_t* dh, uint16_t* d_au, hipStream_t s);
+int gate_bwd_splits(int64_t T);
+size_t gate_bwd_workspace_bytes(int64_t T, int d, int E);
 hipError_t launch_gate_bwd(int64_t T, int d, int E, int k, const void* x, int x_dtype, const float* w_gate,
                            const float* logits, const float* offset, const int32_t* idx, const float* d_w,
-                           float* dL, float* dx, float* dw_gate, hipStream_t s);
+                           float* dL, float* dx, float* dw_gate, float* ws, hipStream_t s);
 
 // load balancing
 hipError_t launch_bias_update(int64_t n_rows, int E, const int32_t* counts, float gamma, float* bias,

@@ -6,14 +6,15 @@ forward(x) = moe_route -> moe_dispatch -> moe_expert_ffn (routed: up, down)
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional, Sequence
 
 import torch
 
 from . import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN, MOE_FFN_UP, MOE_FP8_TILE,
                bias_update, combine, combine_backward, dispatch, dispatch_backward, expert_ffn,
-               expert_ffn_backward, gate_prepare, n_blocks, quantize_blocks_e4m3, quantize_rows_e4m3, route,
-               route_backward, route_hash, shape)
+               expert_ffn_backward, gate_prepare, lib, n_blocks, quantize_blocks_e4m3, quantize_rows_e4m3,
+               route, route_backward, route_hash, shape)
 
 STAGES = ("route", "dispatch", "ffn_up", "ffn_down", "shared", "combine")
 
@@ -159,6 +160,8 @@ class MoELayer:
                         "dx": torch.empty((self.T, self.d), dtype=torch.float32, device=dev),
                         "dlogits": torch.empty((self.T, self.E), dtype=torch.float32, device=dev),
                         "dw_gate": torch.empty((self.d, self.E), dtype=torch.float32, device=dev)}
+            wsb = lib().moe_route_backward_workspace_size(ctypes.byref(sh))
+            self.bws["gate_ws"] = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
         w = self.bws
         mark(0)
         combine_backward(sh, b["dest"], self.topk_w, self.yp, grad_out, w["d_yp"], w["d_w"])
@@ -172,7 +175,8 @@ class MoELayer:
         mark(3)
         dispatch_backward(sh, b["dest"], r["d_xp"], d_extra=sx, dx=w["dx"])
         route_backward(sh, x, self.w_gate, self.logits, self.idx, w["d_w"], w["dx"],
-                       logit_offset=self.logit_offset, dlogits=w["dlogits"], dw_gate=w["dw_gate"])
+                       logit_offset=self.logit_offset, dlogits=w["dlogits"], dw_gate=w["dw_gate"],
+                       ws=w["gate_ws"])
         mark(4)
         out = {"dx": w["dx"], "dw_gate": w["dw_gate"], "dw13": r["dw13"], "dw2": r["dw2"],
                "d_topk_w": w["d_w"]}

@@ -181,10 +181,16 @@ def test_backward_checks():
     assert L.moe_dispatch_backward(sh(d=12), bad, bad, BF, None, bad, 0, None) == _lib.MOE_ERR_UNSUPPORTED
     # route backward
     assert L.moe_route_backward(sh(0), None, BF, None, None, None, None, None, None, None, None,
-                                None) == _lib.MOE_OK
+                                None, 0, None) == _lib.MOE_OK
     assert L.moe_route_backward(sh(k=20), bad, BF, bad, None, bad, bad, bad, bad, bad, bad,
-                                None) == _lib.MOE_ERR_INVALID_ARG
+                                None, 0, None) == _lib.MOE_ERR_INVALID_ARG
     assert L.moe_route_backward(sh(), bad, 9, bad, None, bad, bad, bad, bad, bad, bad,
-                                None) == _lib.MOE_ERR_INVALID_ARG
+                                None, 0, None) == _lib.MOE_ERR_INVALID_ARG
     assert L.moe_route_backward(sh(), bad, BF, None, None, bad, bad, bad, bad, bad, bad,
-                                None) == _lib.MOE_ERR_INVALID_ARG
+                                None, 0, None) == _lib.MOE_ERR_INVALID_ARG
+    big = ctypes.byref(_lib.MoeShape(16384, 7168, 256, 8, 4, 8, 2, 2048))
+    need = L.moe_route_backward_workspace_size(big)
+    assert need == 16 * 7168 * 256 * 4
+    assert L.moe_route_backward(big, bad, BF, bad, None, bad, bad, bad, bad, bad, bad, bad, need - 1,
+                                None) == _lib.MOE_ERR_WORKSPACE
+    assert L.moe_route_backward_workspace_size(sh(T=1000)) == 0

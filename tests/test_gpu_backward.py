@@ -115,11 +115,12 @@ def test_dispatch_backward():
     assert np.abs(host(dx) - (host(base) + OB.dispatch_backward(host(dxp), dest, T))).max() <= 1e-6 * np.abs(ref).max()
 
 
-@pytest.mark.parametrize("with_offset", [False, True])
-def test_route_backward(with_offset):
+@pytest.mark.parametrize("with_offset,T", [(False, 300), (True, 300), (False, 4100)])
+def test_route_backward(with_offset, T):
+    """T = 4100 sums dW_g over four K parts of the workspace (ragged last part)."""
     dev = need_gpu()
-    rng = np.random.default_rng(5 + with_offset)
-    T, E, k, d = 300, 64, 6, 512
+    rng = np.random.default_rng(5 + with_offset + T)
+    E, k, d = 64, 6, 512
     x = _bf16(rng.normal(size=(T, d)), dev)
     wg = (rng.normal(size=(d, E)) * 0.02).astype(np.float32)
     L = (rng.normal(size=(T, E)) * 3).astype(np.float32)
