@@ -141,7 +141,7 @@ def backward_bench(a, cfg, layer, x, ev, torch, alg, rows):
     timed with events (combine, routed experts, shared expert, dispatch + gate)."""
     g = torch.randn((cfg.T, cfg.d), device=x.device, dtype=torch.float32).to(torch.bfloat16)
     for _ in range(max(1, a.warmup)):
-        layer.forward(x)
+        layer.forward(x, save_for_backward=True)
         layer.backward(x, g)
     torch.cuda.synchronize()
     steps = max(5, a.steps // 5)
@@ -150,7 +150,7 @@ def backward_bench(a, cfg, layer, x, ev, torch, alg, rows):
     s0, s1 = ev(), ev()
     s0.record()
     for i in range(steps):
-        layer.forward(x, marks=fm[i])
+        layer.forward(x, marks=fm[i], save_for_backward=True)
         layer.backward(x, g, marks=bm[i])
     s1.record()
     torch.cuda.synchronize()
@@ -158,9 +158,9 @@ def backward_bench(a, cfg, layer, x, ev, torch, alg, rows):
     names = ("combine_bwd", "routed_experts_bwd", "shared_expert_bwd", "dispatch_gate_bwd")
     st = {n: sum(m[i].elapsed_time(m[i + 1]) for m in bm) / steps for i, n in enumerate(names)}
     bwd_ms = sum(st.values())
-    # expert backward products: the recomputed up-projection (4 d d_ff per row),
-    # d_h (2), d_x (4), dW2 (2), dW13 (4) = 16 d d_ff per row
-    fl = 16 * cfg.d * cfg.d_ff
+    # expert backward products (the forward kept [a | u]): d_h (2 d d_ff per
+    # row), d_x (4), dW2 (2), dW13 (4) = 12 d d_ff per row
+    fl = 12 * cfg.d * cfg.d_ff
     peak = PEAK_BF16_TFLOPS
     tf = lambda flops, t: flops / (t * 1e-3) / 1e12
     return {"steps": steps, "fwd_bwd_ms_per_step": ms, "fwd_bwd_tokens_per_s": cfg.T / (ms * 1e-3),
@@ -168,7 +168,8 @@ def backward_bench(a, cfg, layer, x, ev, torch, alg, rows):
             "routed_experts_tflops": tf(fl * rows, st["routed_experts_bwd"]),
             "routed_experts_frac_mfma": tf(fl * rows, st["routed_experts_bwd"]) / peak,
             "shared_expert_tflops": tf(fl * cfg.T, st["shared_expert_bwd"]),
-            "flops_note": "16*d*d_ff per row: recomputed up-projection + d_h + d_x + dW2 + dW13"}
+            "train_forward_ms": sum(m[0].elapsed_time(m[6]) for m in fm) / steps,
+            "flops_note": "12*d*d_ff per row: d_h + d_x + dW2 + dW13 (the training forward keeps [a|u])"}
 
 
 def cpu_baseline(cfg, inp, ex, S, ids=None):

@@ -257,6 +257,20 @@ int moe_combine_backward(const moe_shape* shape, const int32_t* dest, const floa
                          moe_stream_t stream);
 
 /*
+ * moe_expert_ffn_train - moe_expert_ffn (both stages, bf16) that also keeps
+ * the pre-activations [a | u] = [x W1^T | x W3^T] (bf16 [max_rows, 2*d_ff])
+ * for moe_expert_ffn_backward with MOE_BWD_AU_SAVED, which then skips
+ * recomputing them.  h and yp are bit-identical to moe_expert_ffn's.
+ * offsets may be NULL with n_exp = 1 (one group of max_rows rows); d and d_ff
+ * multiples of 256.
+ */
+int moe_expert_ffn_train(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int32_t d, int32_t d_ff,
+                         int dtype, const void* xp, const void* w13, const void* w2, void* h, void* au, void* yp,
+                         moe_stream_t stream);
+
+#define MOE_BWD_AU_SAVED 1  /* moe_expert_ffn_backward: au already holds [a | u] */
+
+/*
  * moe_expert_ffn_backward - backward of the grouped SwiGLU experts
  * (y = (silu(x W1^T) * (x W3^T)) W2^T per group), bf16 products on the matrix
  * cores with fp32 accumulation:
@@ -264,7 +278,8 @@ int moe_combine_backward(const moe_shape* shape, const int32_t* dest, const floa
  *   dw13 [n_exp, 2*d_ff, d] fp32   [da|du]^T xp   (over each group's rows)
  *   dw2  [n_exp, d, d_ff]   fp32   d_yp^T h
  * Workspaces (caller-owned, bf16): au [max_rows, 2*d_ff] (the up-projection
- * is recomputed into it), h [max_rows, d_ff] (d_h, then h), d_au
+ * is recomputed into it, unless flags has MOE_BWD_AU_SAVED and it holds
+ * moe_expert_ffn_train's [a | u]), h [max_rows, d_ff] (d_h, then h), d_au
  * [max_rows, 2*d_ff].  offsets as moe_expert_ffn (device, [n_exp+1]); NULL with
  * n_exp = 1 means one group of max_rows rows (the shared expert on x).  Weight
  * gradients are written (not accumulated); a group with no rows gets zeros.
@@ -272,7 +287,7 @@ int moe_combine_backward(const moe_shape* shape, const int32_t* dest, const floa
  */
 int moe_expert_ffn_backward(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int32_t d, int32_t d_ff,
                             int dtype, const void* xp, const void* w13, const void* w2, const void* d_yp,
-                            void* au, void* h, void* d_au, void* d_xp, float* dw13, float* dw2,
+                            void* au, void* h, void* d_au, void* d_xp, float* dw13, float* dw2, int flags,
                             moe_stream_t stream);
 
 /*

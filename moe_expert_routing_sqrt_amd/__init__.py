@@ -23,10 +23,11 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN, MOE_FFN_UP,  # noqa: F401
+from ._lib import (MOE_BF16, MOE_BWD_AU_SAVED, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN,  # noqa: F401
+                   MOE_FFN_UP,
                    MOE_FP8_TILE, MOE_ROUTE_BLOCK, MOE_ROUTE_LOGITS_IN, MoeError, MoeShape)
 
-__all__ = ["shape", "gate_prepare", "route", "route_hash", "dispatch", "combine_backward",
+__all__ = ["shape", "gate_prepare", "route", "route_hash", "dispatch", "combine_backward", "expert_ffn_train",
            "expert_ffn_backward", "dispatch_backward", "route_backward", "expert_ffn", "combine",
            "quantize_blocks_e4m3", "quantize_rows_e4m3", "bias_update", "MoELayer", "MoeError", "lib"]
 
@@ -293,13 +294,7 @@ def combine_backward(sh: MoeShape, dest, topk_w, yp, grad_out, d_yp=None, d_w=No
     return d_yp, d_w
 
 
-def expert_ffn_backward(offsets: Optional[torch.Tensor], max_rows: int, xp, w13, w2, d_yp, ws: Optional[dict] = None):
-    """Grouped SwiGLU backward: returns dict with d_xp [max_rows, d] bf16, dw13
-    [n, 2*d_ff, d] fp32, dw2 [n, d, d_ff] fp32 (and the bf16 workspaces)."""
-    n_exp = 1 if offsets is None else offsets.numel() - 1
-    d_ff, d = w13.shape[-2] // 2, w13.shape[-1]
-    dev = xp.device
-    b = {} if ws is None else ws
+def _ffn_bwd_ws(b: dict, max_rows: int, n_exp: int, d: int, d_ff: int, dev):
     bf = torch.bfloat16
     if "au" not in b:
         b["au"] = torch.empty((max_rows, 2 * d_ff), dtype=bf, device=dev)
@@ -308,6 +303,36 @@ def expert_ffn_backward(offsets: Optional[torch.Tensor], max_rows: int, xp, w13,
         b["d_xp"] = torch.empty((max_rows, d), dtype=bf, device=dev)
         b["dw13"] = torch.empty((n_exp, 2 * d_ff, d), dtype=torch.float32, device=dev)
         b["dw2"] = torch.empty((n_exp, d, d_ff), dtype=torch.float32, device=dev)
+    return b
+
+
+def expert_ffn_train(offsets: Optional[torch.Tensor], max_rows: int, xp, w13, w2, h, yp, ws: dict):
+    """Grouped SwiGLU forward (bf16) that also keeps [a | u] in ws["au"] for
+    expert_ffn_backward(..., au_saved=True).  h and yp as expert_ffn."""
+    n_exp = 1 if offsets is None else offsets.numel() - 1
+    d_ff, d = w13.shape[-2] // 2, w13.shape[-1]
+    _ffn_bwd_ws(ws, max_rows, n_exp, d, d_ff, xp.device)
+    _need(xp, max_rows * d, "xp")
+    _need(h, max_rows * d_ff, "h")
+    _need(yp, max_rows * d, "yp")
+    st = lib().moe_expert_ffn_train(n_exp, _ptr(offsets), max_rows, d, d_ff, _dt(xp), _ptr(xp), _ptr(w13), _ptr(w2),
+                                    _ptr(h), _ptr(ws["au"]), _ptr(yp), _stream())
+    _lib.check("moe_expert_ffn_train", st)
+    return yp, h
+
+
+def expert_ffn_backward(offsets: Optional[torch.Tensor], max_rows: int, xp, w13, w2, d_yp, ws: Optional[dict] = None,
+                        au_saved: bool = False):
+    """Grouped SwiGLU backward: returns dict with d_xp [max_rows, d] bf16, dw13
+    [n, 2*d_ff, d] fp32, dw2 [n, d, d_ff] fp32 (and the bf16 workspaces).
+    au_saved: ws["au"] holds expert_ffn_train's [a | u] (no recompute)."""
+    n_exp = 1 if offsets is None else offsets.numel() - 1
+    d_ff, d = w13.shape[-2] // 2, w13.shape[-1]
+    dev = xp.device
+    b = {} if ws is None else ws
+    if au_saved and "au" not in b:
+        raise ValueError("au_saved needs ws['au'] from expert_ffn_train")
+    _ffn_bwd_ws(b, max_rows, n_exp, d, d_ff, dev)
     _need(xp, max_rows * d, "xp")
     _need(d_yp, max_rows * d, "d_yp")
     _need(w13, n_exp * 2 * d_ff * d, "w13")
@@ -317,7 +342,8 @@ def expert_ffn_backward(offsets: Optional[torch.Tensor], max_rows: int, xp, w13,
         _need(b[n], need, n)
     st = lib().moe_expert_ffn_backward(n_exp, _ptr(offsets), max_rows, d, d_ff, _dt(xp), _ptr(xp), _ptr(w13),
                                        _ptr(w2), _ptr(d_yp), _ptr(b["au"]), _ptr(b["h"]), _ptr(b["d_au"]),
-                                       _ptr(b["d_xp"]), _ptr(b["dw13"]), _ptr(b["dw2"]), _stream())
+                                       _ptr(b["d_xp"]), _ptr(b["dw13"]), _ptr(b["dw2"]),
+                                       MOE_BWD_AU_SAVED if au_saved else 0, _stream())
     _lib.check("moe_expert_ffn_backward", st)
     return b
 

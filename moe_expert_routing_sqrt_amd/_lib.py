@@ -16,6 +16,7 @@ MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
+MOE_BWD_AU_SAVED = 1
 MOE_ROUTE_LOGITS_IN = 1
 MOE_FFN_UP, MOE_FFN_DOWN, MOE_FFN_ALL = 1, 2, 3
 MOE_ROUTE_BLOCK = 64
@@ -58,7 +59,8 @@ SIGNATURES = {
     "moe_route_hash": (_INT, [ctypes.POINTER(MoeShape), _P, ctypes.c_uint64, _P, _P, _P, _P, _P]),
     "moe_combine_backward": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _P, _INT, _P, _INT, _P, _P, _P]),
     "moe_expert_ffn_backward": (_INT, [_I32, _P, _I64, _I32, _I32, _INT, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                       _P, _P]),
+                                       _P, _INT, _P]),
+    "moe_expert_ffn_train": (_INT, [_I32, _P, _I64, _I32, _I32, _INT, _P, _P, _P, _P, _P, _P, _P]),
     "moe_dispatch_backward": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _INT, _P, _P, _INT, _P]),
     "moe_route_backward": (_INT, [ctypes.POINTER(MoeShape), _P, _INT, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),

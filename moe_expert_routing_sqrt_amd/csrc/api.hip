@@ -223,11 +223,30 @@ int moe_combine_backward(const moe_shape* shape, const int32_t* dest, const floa
                                        g_dtype, static_cast<uint16_t*>(d_yp), d_topk_w, as_stream(stream)));
 }
 
+int moe_expert_ffn_train(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int32_t d, int32_t d_ff,
+                         int dtype, const void* xp, const void* w13, const void* w2, void* h, void* au, void* yp,
+                         moe_stream_t stream) {
+  if (n_exp < 1 || n_exp > kMaxExperts || max_rows < 0 || d < 1 || d_ff < 1) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16 || !ffn_bwd_bf16_supported(d, d_ff)) return MOE_ERR_UNSUPPORTED;
+  if (offsets == nullptr && n_exp != 1) return MOE_ERR_INVALID_ARG;
+  if (xp == nullptr || w13 == nullptr || w2 == nullptr || h == nullptr || au == nullptr || yp == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (max_rows == 0) return MOE_OK;
+  const hipStream_t s = as_stream(stream);
+  hipError_t e = launch_ffn_up_bf16(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint16_t*>(xp),
+                                    static_cast<const uint16_t*>(w13), static_cast<uint16_t*>(h), s,
+                                    static_cast<uint16_t*>(au));
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(launch_ffn_down_bf16(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint16_t*>(h),
+                                         static_cast<const uint16_t*>(w2), static_cast<uint16_t*>(yp), s));
+}
+
 int moe_expert_ffn_backward(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int32_t d, int32_t d_ff,
                             int dtype, const void* xp, const void* w13, const void* w2, const void* d_yp,
-                            void* au, void* h, void* d_au, void* d_xp, float* dw13, float* dw2,
+                            void* au, void* h, void* d_au, void* d_xp, float* dw13, float* dw2, int flags,
                             moe_stream_t stream) {
   if (n_exp < 1 || n_exp > kMaxExperts || max_rows < 0 || d < 1 || d_ff < 1) return MOE_ERR_INVALID_ARG;
+  if ((flags & ~MOE_BWD_AU_SAVED) != 0) return MOE_ERR_INVALID_ARG;
   if (dtype != MOE_BF16 || !ffn_bwd_bf16_supported(d, d_ff)) return MOE_ERR_UNSUPPORTED;
   if (offsets == nullptr && n_exp != 1) return MOE_ERR_INVALID_ARG;
   if (xp == nullptr || w13 == nullptr || w2 == nullptr || d_yp == nullptr || au == nullptr || h == nullptr ||
@@ -242,8 +261,10 @@ int moe_expert_ffn_backward(int32_t n_exp, const int32_t* offsets, int64_t max_r
   auto* H = static_cast<uint16_t*>(h);
   auto* DAU = static_cast<uint16_t*>(d_au);
   hipError_t e;
-  // [a | u] again (recomputed), d_h = d_y W2, then SwiGLU's derivative (h on the side)
-  if ((e = launch_ffn_store_bf16(n_exp, offsets, max_rows, d, 2 * d_ff, X, W13, AU, s)) != hipSuccess)
+  // [a | u] (kept by moe_expert_ffn_train, else recomputed), d_h = d_y W2,
+  // then SwiGLU's derivative (h on the side)
+  if (!(flags & MOE_BWD_AU_SAVED) &&
+      (e = launch_ffn_store_bf16(n_exp, offsets, max_rows, d, 2 * d_ff, X, W13, AU, s)) != hipSuccess)
     return hip_status(e);
   if ((e = launch_ffn_dgrad_bf16(n_exp, offsets, max_rows, d, d_ff, DY, W2, H, s)) != hipSuccess)
     return hip_status(e);

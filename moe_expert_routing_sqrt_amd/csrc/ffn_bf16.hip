@@ -61,7 +61,7 @@ constexpr int DHALF = NDMA / 2;   // DMA issued in the last slice of the step be
 static_assert(NR <= NQ, "one fragment read per MFMA slot");
 static_assert(NW % 2 == 0, "a wave's DMA blocks share the swizzle parity");
 
-enum { MODE_SWIGLU = 0, MODE_STORE = 1 };
+enum { MODE_SWIGLU = 0, MODE_STORE = 1, MODE_SWIGLU_SAVE = 2 };  // SAVE: also [a | u]
 
 struct FfnArgs {
   const uint16_t* A;       // packed rows [rows, K]
@@ -76,17 +76,20 @@ struct FfnArgs {
   int K;
   int n_tiles;             // column tiles per group
   int d_ff;                // SWIGLU: first up-projection row of w13
+  uint16_t* C2;            // SWIGLU_SAVE: [a | u] output [rows, 2*d_ff]
 };
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-  constexpr int OUT_COLS = MODE == MODE_SWIGLU ? BN / 2 : BN;
+  constexpr bool SWI = MODE != MODE_STORE;
+  constexpr int OUT_COLS = SWI ? BN / 2 : BN;
   constexpr int ROW_BYTES = OUT_COLS * 2;
   constexpr int PITCH = ROW_BYTES + 16;  // output staging row pitch
+  constexpr int AU_PITCH = BN * 2 + 16;  // SWIGLU_SAVE: staging of [a | u]
   constexpr int STAGE = (BM + BN) * 8;   // uint4 per stage
   constexpr int RING = 2 * STAGE;
-  constexpr int OUT_U4 = BM * PITCH / 16;
+  constexpr int OUT_U4 = BM * (MODE == MODE_SWIGLU_SAVE ? AU_PITCH : PITCH) / 16;
   __shared__ uint4 smem[RING > OUT_U4 ? RING : OUT_U4];
   __shared__ int s_pre[kMaxExperts + 1];
   uint4* const sA0 = smem;
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
   for (int i = 0; i < BDMA; ++i) {
     const int r = (wave + NW * i) * 8 + lrow;
     int grow;
-    if constexpr (MODE == MODE_SWIGLU) {
+    if constexpr (SWI) {
       // tile rows [part*TN, part*TN + TN/2) are gate rows, the next TN/2 the
       // matching up rows, for features n_tile*BN/2 + part*TN/2 + [0, TN/2)
       const int part = r / TN, within = r % TN;
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
       for (int v = 0; v < 16; ++v) {
         const int lr = wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         uint16_t* row = reinterpret_cast<uint16_t*>(stage + lr * PITCH);
-        if constexpr (MODE == MODE_SWIGLU) {
+        if constexpr (SWI) {
 #pragma unroll
           for (int jj = 0; jj < RN / 2; ++jj) {
             const float g = acc[i][jj][v];
@@ -290,6 +293,36 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
     char* dst = reinterpret_cast<char*>(p.C + (ti.row0 + r) * p.ldc + col0) + c * 16;
     *reinterpret_cast<uint4*>(dst) = v;
   }
+  if constexpr (MODE == MODE_SWIGLU_SAVE) {
+    // the pre-activations for the backward: a (gate) at columns
+    // [n_tile*BN/2, +BN/2) and u (up) at d_ff + the same, bf16
+    __syncthreads();  // every read of the h staging is done
+    if (act) {
+#pragma unroll
+      for (int i = 0; i < RM; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int lr = wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          uint16_t* row = reinterpret_cast<uint16_t*>(stage + lr * AU_PITCH);
+#pragma unroll
+          for (int jj = 0; jj < RN / 2; ++jj) {
+            row[wn * (TN / 2) + jj * 32 + (lane & 31)] = f32_to_bf16(acc[i][jj][v]);
+            row[BN / 2 + wn * (TN / 2) + jj * 32 + (lane & 31)] = f32_to_bf16(acc[i][jj + RN / 2][v]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int HCH = BN / 2 * 2 / 16;  // 16-byte chunks per half row
+    const int64_t ld2 = 2 * (int64_t)p.d_ff;
+    for (int q = tid; q < ti.rows * 2 * HCH; q += kThreads) {
+      const int r = q / (2 * HCH), c = q % (2 * HCH);
+      const int half = c / HCH, cc = c % HCH;
+      const uint4 v = *reinterpret_cast<const uint4*>(stage + r * AU_PITCH + c * 16);
+      uint16_t* dst = p.C2 + (ti.row0 + r) * ld2 + half * p.d_ff + col0 + cc * 8;
+      *reinterpret_cast<uint4*>(dst) = v;
+    }
+  }
 #endif
 }
 
@@ -306,7 +339,7 @@ hipError_t launch(const FfnArgs& a, int64_t max_rows, hipStream_t s) {
 
 hipError_t launch_ffn_up_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
                               int d_ff, const uint16_t* xp, const uint16_t* w13, uint16_t* h,
-                              hipStream_t s) {
+                              hipStream_t s, uint16_t* au) {
   FfnArgs a{};
   a.A = xp;
   a.lda = d;
@@ -320,6 +353,8 @@ hipError_t launch_ffn_up_bf16(int n_exp, const int32_t* offsets, int64_t max_row
   a.K = d;
   a.n_tiles = d_ff / (BN / 2);
   a.d_ff = d_ff;
+  a.C2 = au;
+  if (au != nullptr) return launch<MODE_SWIGLU_SAVE>(a, max_rows, s);
   return launch<MODE_SWIGLU>(a, max_rows, s);
 }
 

@@ -30,7 +30,7 @@ hipError_t launch_dispatch(const int32_t* idx, const int32_t* block_counts, int6
 // grouped expert FFN
 hipError_t launch_ffn_up_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
                               int d_ff, const uint16_t* xp, const uint16_t* w13, uint16_t* h,
-                              hipStream_t s);
+                              hipStream_t s, uint16_t* au = nullptr);
 hipError_t launch_ffn_down_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
                                 int d_ff, const uint16_t* h, const uint16_t* w2, uint16_t* yp,
                                 hipStream_t s);

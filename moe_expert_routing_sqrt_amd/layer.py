@@ -13,7 +13,7 @@ import torch
 
 from . import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN, MOE_FFN_UP, MOE_FP8_TILE,
                bias_update, combine, combine_backward, dispatch, dispatch_backward, expert_ffn,
-               expert_ffn_backward, gate_prepare, lib, n_blocks, quantize_blocks_e4m3, quantize_rows_e4m3,
+               expert_ffn_backward, expert_ffn_train, gate_prepare, lib, n_blocks, quantize_blocks_e4m3, quantize_rows_e4m3,
                route, route_backward, route_hash, shape)
 
 STAGES = ("route", "dispatch", "ffn_up", "ffn_down", "shared", "combine")
@@ -88,10 +88,15 @@ class MoELayer:
 
     def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
                 marks: Optional[Sequence[torch.cuda.Event]] = None,
-                token_ids: Optional[torch.Tensor] = None) -> torch.Tensor:
+                token_ids: Optional[torch.Tensor] = None, save_for_backward: bool = False) -> torch.Tensor:
         """One layer forward.  `marks`: optional 7 events recorded on the current
         stream around the six stages (STAGES).  With router="hash" the experts
-        come from `token_ids` (int32 [T]) and the gate weights are 1/k."""
+        come from `token_ids` (int32 [T]) and the gate weights are 1/k.
+        save_for_backward: the expert FFNs also keep their pre-activations, so
+        backward() does not recompute them (bf16 top-k layer)."""
+        self._saved = save_for_backward
+        if save_for_backward:
+            return self._forward_train(x, marks)
         def mark(i):
             if marks is not None:
                 marks[i].record()
@@ -135,6 +140,46 @@ class MoELayer:
         mark(6)
         return out
 
+    def _bwd_ws(self, dev):
+        if not hasattr(self, "bws"):
+            self.bws = {"routed": {}, "shared": {},
+                        "d_yp": torch.empty((self.max_rows, self.d), dtype=torch.bfloat16, device=dev),
+                        "d_w": torch.empty((self.T, self.k), dtype=torch.float32, device=dev),
+                        "dx": torch.empty((self.T, self.d), dtype=torch.float32, device=dev),
+                        "dlogits": torch.empty((self.T, self.E), dtype=torch.float32, device=dev),
+                        "dw_gate": torch.empty((self.d, self.E), dtype=torch.float32, device=dev)}
+            wsb = lib().moe_route_backward_workspace_size(ctypes.byref(self.sh))
+            self.bws["gate_ws"] = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
+        return self.bws
+
+    def _forward_train(self, x, marks):
+        if self.dtype != MOE_BF16 or self.local or self.router != "topk":
+            raise ValueError("save_for_backward covers the bf16 top-k layer with all experts local")
+
+        def mark(i):
+            if marks is not None:
+                marks[i].record()
+
+        sh, w = self.sh, self._bwd_ws(x.device)
+        mark(0)
+        route(sh, x, self.w_prep, self.bias, self.logit_offset, logits=self.logits, idx=self.idx,
+              w=self.topk_w, block_counts=self.block_counts)
+        mark(1)
+        self.dbufs = dispatch(sh, self.idx, self.block_counts, x, self.e_begin, self.e_end, bufs=self.dbufs)
+        b = self.dbufs
+        mark(2)
+        expert_ffn_train(b["offsets"], self.max_rows, b["xp"], self.w13, self.w2, self.h, self.yp, w["routed"])
+        mark(3)
+        mark(4)
+        ysh = None
+        if self.has_shared:
+            expert_ffn_train(None, self.T, x, self.sh_w13, self.sh_w2, self.sh_h, self.ysh, w["shared"])
+            ysh = self.ysh
+        mark(5)
+        combine(sh, b["dest"], self.topk_w, self.yp, ysh, out=self.out)
+        mark(6)
+        return self.out
+
     def backward(self, x: torch.Tensor, grad_out: torch.Tensor,
                  marks: Optional[Sequence[torch.cuda.Event]] = None) -> dict:
         """Gradients of the last forward(x) for grad_out = d loss / d out (bf16
@@ -153,24 +198,18 @@ class MoELayer:
                 marks[i].record()
 
         sh, b, dev = self.sh, self.dbufs, x.device
-        if not hasattr(self, "bws"):
-            self.bws = {"routed": {}, "shared": {},
-                        "d_yp": torch.empty((self.max_rows, self.d), dtype=torch.bfloat16, device=dev),
-                        "d_w": torch.empty((self.T, self.k), dtype=torch.float32, device=dev),
-                        "dx": torch.empty((self.T, self.d), dtype=torch.float32, device=dev),
-                        "dlogits": torch.empty((self.T, self.E), dtype=torch.float32, device=dev),
-                        "dw_gate": torch.empty((self.d, self.E), dtype=torch.float32, device=dev)}
-            wsb = lib().moe_route_backward_workspace_size(ctypes.byref(sh))
-            self.bws["gate_ws"] = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
-        w = self.bws
+        w = self._bwd_ws(dev)
+        saved = getattr(self, "_saved", False)
         mark(0)
         combine_backward(sh, b["dest"], self.topk_w, self.yp, grad_out, w["d_yp"], w["d_w"])
         mark(1)
-        r = expert_ffn_backward(b["offsets"], self.max_rows, b["xp"], self.w13, self.w2, w["d_yp"], w["routed"])
+        r = expert_ffn_backward(b["offsets"], self.max_rows, b["xp"], self.w13, self.w2, w["d_yp"], w["routed"],
+                                au_saved=saved)
         mark(2)
         sx = None
         if self.has_shared:
-            s_ = expert_ffn_backward(None, self.T, x, self.sh_w13, self.sh_w2, grad_out, w["shared"])
+            s_ = expert_ffn_backward(None, self.T, x, self.sh_w13, self.sh_w2, grad_out, w["shared"],
+                                     au_saved=saved)
             sx = s_["d_xp"]
         mark(3)
         dispatch_backward(sh, b["dest"], r["d_xp"], d_extra=sx, dx=w["dx"])

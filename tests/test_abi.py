@@ -165,15 +165,26 @@ def test_backward_checks():
     assert L.moe_combine_backward(sh(), None, bad, bad, BF, bad, BF, bad, bad, None) == _lib.MOE_ERR_INVALID_ARG
     # expert FFN backward
     args = [bad] * 10
-    assert L.moe_expert_ffn_backward(0, bad, 8, 256, 256, BF, *args, None) == _lib.MOE_ERR_INVALID_ARG
-    assert L.moe_expert_ffn_backward(2, None, 8, 256, 256, BF, *args, None) == _lib.MOE_ERR_INVALID_ARG
-    assert L.moe_expert_ffn_backward(1, None, 8, 256, 256, F, *args, None) == _lib.MOE_ERR_UNSUPPORTED
-    assert L.moe_expert_ffn_backward(1, None, 8, 256, 128, BF, *args, None) == _lib.MOE_ERR_UNSUPPORTED
-    assert L.moe_expert_ffn_backward(1, None, 8, 200, 256, BF, *args, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_ffn_backward(0, bad, 8, 256, 256, BF, *args, 0, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn_backward(2, None, 8, 256, 256, BF, *args, 0, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn_backward(1, None, 8, 256, 256, BF, *args, 2, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn_backward(1, None, 8, 256, 256, F, *args, 0, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_ffn_backward(1, None, 8, 256, 128, BF, *args, 0, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_ffn_backward(1, None, 8, 200, 256, BF, *args, 0, None) == _lib.MOE_ERR_UNSUPPORTED
     for i in range(10):
         a = list(args)
         a[i] = None
-        assert L.moe_expert_ffn_backward(1, None, 8, 256, 256, BF, *a, None) == _lib.MOE_ERR_INVALID_ARG
+        assert L.moe_expert_ffn_backward(1, None, 8, 256, 256, BF, *a, 0, None) == _lib.MOE_ERR_INVALID_ARG
+    # training forward
+    targs = [bad] * 6
+    assert L.moe_expert_ffn_train(1, None, 0, 256, 256, BF, *targs, None) == _lib.MOE_OK
+    assert L.moe_expert_ffn_train(2, None, 8, 256, 256, BF, *targs, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn_train(1, None, 8, 256, 128, BF, *targs, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_ffn_train(1, None, 8, 256, 256, F, *targs, None) == _lib.MOE_ERR_UNSUPPORTED
+    for i in range(6):
+        a = list(targs)
+        a[i] = None
+        assert L.moe_expert_ffn_train(1, None, 8, 256, 256, BF, *a, None) == _lib.MOE_ERR_INVALID_ARG
     # dispatch backward
     assert L.moe_dispatch_backward(sh(0), None, None, BF, None, None, 0, None) == _lib.MOE_OK
     assert L.moe_dispatch_backward(sh(), bad, bad, BF, None, bad, 2, None) == _lib.MOE_ERR_INVALID_ARG

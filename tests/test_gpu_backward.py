@@ -234,3 +234,64 @@ def test_layer_backward_v3_sampled_expert():
     assert max(errs) <= 2e-2
     del ex, r, b
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("counts", [[0, 1, 300, 257, 129], None])
+def test_train_forward_keeps_preactivations(counts):
+    """expert_ffn_train: h and yp bit-identical to expert_ffn; its [a | u] equals
+    the backward's recomputation bit for bit (same K order), so the backward
+    with the saved values equals the one that recomputes; [a | u] against the
+    oracle's fp64 products within one bf16 rounding."""
+    dev = need_gpu()
+    rng = np.random.default_rng(21)
+    d, d_ff = 512, 256
+    rows = 700 if counts is None else int(sum(counts))
+    n = 1 if counts is None else len(counts)
+    off = None if counts is None else dev_i32(_offsets(counts), dev)
+    xp = _bf16(rng.normal(size=(rows, d)), dev)
+    w13 = _bf16(rng.normal(size=(n, 2 * d_ff, d)) * 0.05, dev)
+    w2 = _bf16(rng.normal(size=(n, d, d_ff)) * 0.05, dev)
+    dy = _bf16(rng.normal(size=(rows, d)), dev)
+    offs = off if off is not None else dev_i32(np.array([0, rows]), dev)
+    yp_ref, h_ref, _ = M.expert_ffn(offs, rows, xp, w13, w2)
+    ws = {}
+    h = torch.empty_like(h_ref)
+    yp = torch.empty_like(yp_ref)
+    M.expert_ffn_train(off, rows, xp, w13, w2, h, yp, ws)
+    au_saved = ws["au"].clone()
+    b1 = M.expert_ffn_backward(off, rows, xp, w13, w2, dy, ws, au_saved=True)
+    out1 = {k_: b1[k_].clone() for k_ in ("d_xp", "dw13", "dw2")}
+    b2 = M.expert_ffn_backward(off, rows, xp, w13, w2, dy, {})
+    torch.cuda.synchronize()
+    assert torch.equal(h[:rows], h_ref[:rows]) and torch.equal(yp[:rows], yp_ref[:rows])
+    assert torch.equal(au_saved[:rows], b2["au"][:rows])
+    for k_ in out1:
+        assert torch.equal(out1[k_], b2[k_]), k_
+    # [a | u] against fp64 products
+    offs_h = _offsets(counts) if counts is not None else np.array([0, rows])
+    xh, w13h = host(xp), host(w13)
+    for e in range(n):
+        lo, hi = int(offs_h[e]), int(offs_h[e + 1])
+        if hi == lo:
+            continue
+        ref = xh[lo:hi].astype(np.float64) @ w13h[e].astype(np.float64).T
+        got = host(au_saved[lo:hi])
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6 * np.abs(ref).max()), e
+
+
+def test_layer_save_for_backward_matches():
+    dev = need_gpu()
+    cfg = _small_cfg()
+    inp = gen.make_router(cfg, device=dev)
+    ex = gen.make_experts(cfg, device=dev)
+    layer = M.MoELayer(cfg.T, cfg.d, cfg.E, cfg.G, cfg.M, cfg.k, cfg.d_ff, cfg.dtype, inp["w_gate"], inp["bias"],
+                       ex["w13"], ex["w2"], ex["sh_w13"], ex["sh_w2"], group_topk=cfg.gk)
+    g = _bf16(np.random.default_rng(2).normal(size=(cfg.T, cfg.d)), dev)
+    out_a = layer.forward(inp["x"]).clone()
+    ga = {k_: v.clone() for k_, v in layer.backward(inp["x"], g).items()}
+    out_b = layer.forward(inp["x"], save_for_backward=True).clone()
+    gb = layer.backward(inp["x"], g)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    for k_ in ga:
+        assert torch.equal(ga[k_], gb[k_]), k_
