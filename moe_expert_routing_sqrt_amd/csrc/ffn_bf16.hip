@@ -8,9 +8,9 @@
 // layout, so K is contiguous for both operands.
 //
 // Work-group tile 256 rows x 256 weight rows x 64 (K), 512 threads = 8 wave64s
-// laid out 4 x 2, each owning 64 x 128 of 32x32 fp32 accumulators fed by
-// v_mfma_f32_32x32x16_bf16; two waves share each SIMD, so one wave's memory
-// stalls are covered by the other's MFMAs.  256 x 256 tiles halve the operand
+// laid out 4 x 2, each owning 2 x 4 blocks of 32x32 fp32 accumulators (64 rows x
+// 128 weight rows) fed by v_mfma_f32_32x32x16_bf16; two waves share each SIMD,
+// so one wave's memory stalls are covered by the other's MFMAs.  256 x 256 tiles halve the operand
 // bytes per FLOP of a 128 x 128 tile; a step moves 64 KB into LDS for 8.4 MFLOP.
 //
 // Pipeline (two LDS stages of 64 KB, 128-byte rows, XOR-swizzled chunks):
@@ -24,16 +24,20 @@
 //     the first half of step k+2's DMA; the second half goes out in the first
 //     slice of step k+1.
 //
-// Ragged groups: a tile covers up to 256 rows of one expert.  A wave whose 64
-// rows all lie past the tile's valid rows skips its MFMAs, fragment reads and
-// activation DMA (it still moves its share of the weight tile and joins every
-// barrier).  In a tile of at most 128 valid rows the working waves then sit
-// one per SIMD, so such a tile costs about half a full one and the padding
-// waste is that of 128-row tiles.
+// Ragged groups: a tile covers up to 256 rows of one expert.  Wave row wm owns
+// the 32-row blocks at rows 32*wm and 128 + 32*wm, so the two waves sharing a
+// SIMD (wm and wm + 2) hold blocks in every 64-row band of the tile.  A block
+// past the tile's valid rows is skipped (no MFMAs, no fragment reads), and a
+// wave with no valid block skips its activation DMA too (it still moves its
+// share of the weight tile and joins every barrier).  The busiest SIMD then
+// runs ceil(rows / 64) of its four blocks, so a ragged tile costs its rows
+// rounded up to 64.
 //
 // SwiGLU is fused (mastering-deepseek-v4 Exp08, "Implemented"): a tile's 256
 // weight rows are 128 gate rows (W1) and the matching 128 up rows (W3), and
 // each wave holds the gate and up accumulators of the same 64 features.
+#include <type_traits>
+
 #include "common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -51,6 +55,7 @@ constexpr int kThreads = NW * 64;
 constexpr int TM = BM / WAVES_M;  // 64
 constexpr int TN = BN / WAVES_N;  // 128
 constexpr int RM = TM / 32, RN = TN / 32;
+constexpr int HB = BM / RM;       // row distance between a wave's blocks (128)
 constexpr int ADMA = BM / (8 * NW);  // 1 KB DMA blocks of 8 rows, per wave per step
 constexpr int BDMA = BN / (8 * NW);
 constexpr int NDMA = ADMA + BDMA;
@@ -59,6 +64,7 @@ constexpr int NQ = RM * RN;       // MFMAs per slice
 constexpr int NR = RM + RN;       // fragment reads per slice
 constexpr int DHALF = NDMA / 2;   // DMA issued in the last slice of the step before
 static_assert(NR <= NQ, "one fragment read per MFMA slot");
+static_assert(RM == 2, "a wave's blocks sit in the two halves of the tile");
 static_assert(NW % 2 == 0, "a wave's DMA blocks share the swizzle parity");
 
 enum { MODE_SWIGLU = 0, MODE_STORE = 1, MODE_SWIGLU_SAVE = 2 };  // SAVE: also [a | u]
@@ -109,7 +115,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
-  const bool act = wm * TM < ti.rows;  // this wave has valid rows
+  // valid 32-row blocks of this wave: block i covers rows i*HB + 32*wm + [0, 32)
+  const int nb = __builtin_amdgcn_readfirstlane((ti.rows > 32 * wm) + (ti.rows > HB + 32 * wm));
 
   // Direct-to-LDS loads: one instruction moves 64 lanes x 16 B into 1 KB of
   // LDS at lane*16, i.e. 8 rows of 128 B.  The LDS slot of a lane is fixed, so
@@ -174,46 +181,56 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
                        __attribute__((always_inline)) {
     const int kc = 2 * s + (lane >> 5);
     if (f == 0) {
-      fa[buf][0] = as_bf16x8(sa[swz(wm * TM + (lane & 31), kc)]);
+      fa[buf][0] = as_bf16x8(sa[swz(32 * wm + (lane & 31), kc)]);
     } else if (f <= RN) {
       fb[buf][f - 1] = as_bf16x8(sb[swz(wn * TN + (f - 1) * 32 + (lane & 31), kc)]);
     } else {
-      fa[buf][f - RN] = as_bf16x8(sa[swz(wm * TM + (f - RN) * 32 + (lane & 31), kc)]);
+      fa[buf][f - RN] = as_bf16x8(sa[swz((f - RN) * HB + 32 * wm + (lane & 31), kc)]);
     }
   };
-  // MFMAs of slice s; reads of slice rs of (rsa, rsb) into the other buffer
-  // (rsa == nullptr: none); DMA parts [d0, d1) of step kd (kd < 0: none).
-  auto slice = [&](int s, const uint4* rsa, const uint4* rsb, int rs, int kd, uint4* da,
+  // MFMAs of slice s over the first NB row blocks; reads of slice rs of
+  // (rsa, rsb) into the other buffer (rsa == nullptr: none); DMA parts
+  // [d0, d1) of step kd (kd < 0: none).  With one block there are five reads
+  // for four MFMA slots: the first slot takes two.
+  auto slice = [&](auto nbc, int s, const uint4* rsa, const uint4* rsb, int rs, int kd, uint4* da,
                    uint4* db, int d0, int d1) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nbc)::value;
+    constexpr int NQB = NB * RN, NRB = NB + RN;
+    constexpr int XR = NRB > NQB ? NRB - NQB : 0;  // reads doubled up in slot 0
     const int buf = s & 1;
     const int nd = d1 - d0;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
+    for (int q = 0; q < NQB; ++q) {
       const int i = q / RN, j = q % RN;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
-      if (rsa != nullptr && q < NR) read_frag(rsa, rsb, buf ^ 1, rs, q);
+      if (rsa != nullptr) {
+#pragma unroll
+        for (int f = 0; f < NRB; ++f)
+          if ((f < XR ? 0 : f - XR) == q) read_frag(rsa, rsb, buf ^ 1, rs, f);
+      }
       if (kd >= 0) {
 #pragma unroll
         for (int t = 0; t < NDMA; ++t)
-          if (t < nd && (t * NQ) / nd == q) dma_one(kd, da, db, d0 + t);
+          if (t < nd && (t * NQB) / nd == q) dma_one(kd, da, db, d0 + t);
       }
       __builtin_amdgcn_sched_barrier(0);  // keep this interleaving
     }
   };
   // Step kt computes from stage (sa, sb); (na, nb) holds step kt+1.
-  auto step = [&](int kt, uint4* sa, uint4* sb, uint4* na, uint4* nb) __attribute__((always_inline)) {
+  auto step = [&](auto nbc, int kt, uint4* sa, uint4* sb, uint4* na, uint4* nb)
+                  __attribute__((always_inline)) {
     const bool more = kt + 1 < nsteps;
     // second half of step kt+1's DMA (the prologue issued all of step 1's)
-    slice(0, sa, sb, 1, (kt >= 1 && more) ? kt + 1 : -1, na, nb, DHALF, NDMA);
+    slice(nbc, 0, sa, sb, 1, (kt >= 1 && more) ? kt + 1 : -1, na, nb, DHALF, NDMA);
 #pragma unroll
-    for (int s = 1; s + 1 < NS; ++s) slice(s, sa, sb, s + 1, -1, nullptr, nullptr, 0, 0);
+    for (int s = 1; s + 1 < NS; ++s) slice(nbc, s, sa, sb, s + 1, -1, nullptr, nullptr, 0, 0);
     if (more) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): step kt's fragments are in registers
       wait_vmcnt<0>();                     // this wave's DMA of step kt+1 has landed
       barrier_only();                      // everyone's has; stage (sa, sb) is free
     }
     // last slice: reads of step kt+1's first slice, first half of step kt+2's DMA
-    slice(NS - 1, more ? na : nullptr, nb, 0, kt + 2 < nsteps ? kt + 2 : -1, sa, sb, 0, DHALF);
+    slice(nbc, NS - 1, more ? na : nullptr, nb, 0, kt + 2 < nsteps ? kt + 2 : -1, sa, sb, 0, DHALF);
   };
   // A wave without valid rows keeps the same DMA parts and barriers.
   auto idle_step = [&](int kt, uint4* sa, uint4* sb, uint4* na, uint4* nb) __attribute__((always_inline)) {
@@ -242,12 +259,21 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
     wait_vmcnt<0>();
   }
   barrier_only();
-  if (act) {
+  if (nb == RM) {
+    using NBC = std::integral_constant<int, RM>;
 #pragma unroll
     for (int f = 0; f < NR; ++f) read_frag(sA0, sB0, 0, 0, f);
     for (int kt = 0; kt < nsteps; kt += 2) {
-      step(kt, sA0, sB0, sA1, sB1);
-      if (kt + 1 < nsteps) step(kt + 1, sA1, sB1, sA0, sB0);
+      step(NBC{}, kt, sA0, sB0, sA1, sB1);
+      if (kt + 1 < nsteps) step(NBC{}, kt + 1, sA1, sB1, sA0, sB0);
+    }
+  } else if (nb == 1) {
+    using NBC = std::integral_constant<int, 1>;
+#pragma unroll
+    for (int f = 0; f <= RN; ++f) read_frag(sA0, sB0, 0, 0, f);
+    for (int kt = 0; kt < nsteps; kt += 2) {
+      step(NBC{}, kt, sA0, sB0, sA1, sB1);
+      if (kt + 1 < nsteps) step(NBC{}, kt + 1, sA1, sB1, sA0, sB0);
     }
   } else {
     for (int kt = 0; kt < nsteps; kt += 2) {
@@ -263,12 +289,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
   // zero outstanding); the barrier ends every wave's reads of the last stage.
   char* const stage = reinterpret_cast<char*>(smem);
   barrier_only();
-  if (act) {
+  if (nb > 0) {
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int lr = wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int lr = i * HB + 32 * wm + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         uint16_t* row = reinterpret_cast<uint16_t*>(stage + lr * PITCH);
         if constexpr (SWI) {
 #pragma unroll
@@ -297,12 +323,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
     // the pre-activations for the backward: a (gate) at columns
     // [n_tile*BN/2, +BN/2) and u (up) at d_ff + the same, bf16
     __syncthreads();  // every read of the h staging is done
-    if (act) {
+    if (nb > 0) {
 #pragma unroll
       for (int i = 0; i < RM; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int lr = wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int lr = i * HB + 32 * wm + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           uint16_t* row = reinterpret_cast<uint16_t*>(stage + lr * AU_PITCH);
 #pragma unroll
           for (int jj = 0; jj < RN / 2; ++jj) {

@@ -39,6 +39,7 @@ def _ragged_case(dtype, d, d_ff, counts, seed):
     [1],                                   # a single row
     [513, 0, 0, 255],
     [64] * 16 + [0, 1000],                 # many small experts and one hot one
+    [33, 65, 97, 161, 193, 225, 256, 31],  # a tail in every 32-row band of a tile
 ])
 def test_ragged_groups(dtype, counts):
     print(f"ffn ragged {dtype} {counts}", flush=True)
