@@ -287,25 +287,39 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
   // The tile is staged in LDS (row pitch padded by 16 bytes) and leaves as
   // 16-byte row chunks.  All DMA has landed (the last in-loop wait was for
   // zero outstanding); the barrier ends every wave's reads of the last stage.
+  // Registers v and v+1 (v even) are consecutive rows of one column: each pair
+  // is rounded by one packed conversion and leaves as two 2-byte LDS writes.
+  // silu(g) = g / (1 + e^-g) takes the hardware reciprocal (1 ulp, far below
+  // the bf16 rounding of h).
   char* const stage = reinterpret_cast<char*>(smem);
+  auto put2 = [&](int lr, int col, int pitch, uint32_t pk) __attribute__((always_inline)) {
+    uint16_t* r0 = reinterpret_cast<uint16_t*>(stage + lr * pitch);
+    uint16_t* r1 = reinterpret_cast<uint16_t*>(stage + (lr + 1) * pitch);
+    r0[col] = static_cast<uint16_t>(pk);
+    r1[col] = static_cast<uint16_t>(pk >> 16);
+  };
+  auto silu_mul = [](float g, float u) __attribute__((always_inline)) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+  };
   barrier_only();
   if (nb > 0) {
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
+      for (int v = 0; v < 16; v += 2) {
         const int lr = i * HB + 32 * wm + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        uint16_t* row = reinterpret_cast<uint16_t*>(stage + lr * PITCH);
         if constexpr (SWI) {
 #pragma unroll
           for (int jj = 0; jj < RN / 2; ++jj) {
-            const float g = acc[i][jj][v];
-            const float u = acc[i][jj + RN / 2][v];
-            row[wn * (TN / 2) + jj * 32 + (lane & 31)] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+            const f32x16& g = acc[i][jj];
+            const f32x16& u = acc[i][jj + RN / 2];
+            put2(lr, wn * (TN / 2) + jj * 32 + (lane & 31), PITCH,
+                 pack_bf16x2(silu_mul(g[v], u[v]), silu_mul(g[v + 1], u[v + 1])));
           }
         } else {
 #pragma unroll
-          for (int j = 0; j < RN; ++j) row[wn * TN + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][v]);
+          for (int j = 0; j < RN; ++j)
+            put2(lr, wn * TN + j * 32 + (lane & 31), PITCH, pack_bf16x2(acc[i][j][v], acc[i][j][v + 1]));
         }
       }
     }
@@ -327,13 +341,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
 #pragma unroll
       for (int i = 0; i < RM; ++i) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 16; v += 2) {
           const int lr = i * HB + 32 * wm + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          uint16_t* row = reinterpret_cast<uint16_t*>(stage + lr * AU_PITCH);
 #pragma unroll
           for (int jj = 0; jj < RN / 2; ++jj) {
-            row[wn * (TN / 2) + jj * 32 + (lane & 31)] = f32_to_bf16(acc[i][jj][v]);
-            row[BN / 2 + wn * (TN / 2) + jj * 32 + (lane & 31)] = f32_to_bf16(acc[i][jj + RN / 2][v]);
+            const int c = wn * (TN / 2) + jj * 32 + (lane & 31);
+            put2(lr, c, AU_PITCH, pack_bf16x2(acc[i][jj][v], acc[i][jj][v + 1]));
+            put2(lr, BN / 2 + c, AU_PITCH, pack_bf16x2(acc[i][jj + RN / 2][v], acc[i][jj + RN / 2][v + 1]));
           }
         }
       }
