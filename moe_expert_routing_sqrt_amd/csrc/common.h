@@ -116,13 +116,18 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // A grouped GEMM launch covers n_exp row groups (experts): group i owns rows
 // [offsets[i], offsets[i+1]).  Each group is cut into ceil(rows/BM) row tiles;
 // each row tile meets n_tiles column tiles.  Logical tiles are numbered group by
-// group, and inside a group column-tile-major with the row tiles innermost, so
-// consecutive tiles share a weight tile and a group's tiles run together.
+// group; inside a group the row tiles form bands of kBandRows, and inside a
+// band the numbering is column-tile-major with the band's row tiles innermost.
+// The 32 tiles an XCD runs at once then cover about 4 row tiles x 8 column
+// tiles: each activation tile is shared by ~8 running tiles and each weight
+// tile by ~4 (a routed expert of at most 4 row tiles is one band).
 // Work-group w is remapped so that each XCD (w % 8) walks one contiguous slice
 // of the logical tiles: the tiles that share weights and activations then sit in
 // one XCD's L2.  Offsets live on the device; the map is rebuilt by every
 // work-group from them (a few hundred ints), so no host sync and no planning
 // kernel are needed.
+
+constexpr int kBandRows = 4;  // row tiles per band of the tile order
 
 struct TileInfo {
   int group;    // expert within the call
@@ -184,8 +189,11 @@ __device__ __forceinline__ bool map_tile(const int* __restrict__ offsets, int n_
   const int mt = s_pre[g + 1] - s_pre[g];
   const int i = L - s_pre[g] * n_tiles;
   ti.group = g;
-  ti.n_tile = i / mt;
-  ti.m_tile = i % mt;
+  const int band = i / (kBandRows * n_tiles);
+  const int bm = min(kBandRows, mt - band * kBandRows);  // row tiles in this band
+  const int ib = i - band * kBandRows * n_tiles;
+  ti.n_tile = ib / bm;
+  ti.m_tile = band * kBandRows + ib % bm;
   const int base = offsets == nullptr ? 0 : offsets[g];
   const int end = offsets == nullptr ? static_cast<int>(rows_total) : offsets[g + 1];
   ti.row0 = base + ti.m_tile * BM;
