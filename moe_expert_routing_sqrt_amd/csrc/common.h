@@ -137,55 +137,67 @@ struct TileInfo {
   int rows;     // valid rows in the tile (1..BM)
 };
 
-// s_pre: LDS scratch of n_exp + 1 ints.  Returns false for a work-group with no
-// tile (uniform across the work-group).  Must be called by all threads.
-__device__ __forceinline__ bool map_tile(const int* __restrict__ offsets, int n_exp,
-                                         int64_t rows_total, int BM, int n_tiles, int* s_pre,
-                                         TileInfo& ti) {
+// s_pre: LDS scratch of kMapInts ints: the groups' row-tile prefix (n + 1
+// ints), then a copy of the offsets at s_pre + kMaxExperts + 1.
+constexpr int kMapInts = 2 * (kMaxExperts + 1);
+
+// Builds the map in s_pre (ends with a work-group barrier); returns the number
+// of groups (1 when offsets is nullptr: one group of rows_total rows).  Must be
+// called by all threads.
+__device__ __forceinline__ int tile_map_build(const int* __restrict__ offsets, int n_exp,
+                                              int64_t rows_total, int BM, int* s_pre) {
   const int tid = threadIdx.x;
-  if (offsets == nullptr) {  // one group of rows_total rows
+  int* const s_off = s_pre + kMaxExperts + 1;
+  if (offsets == nullptr) {
     n_exp = 1;
     if (tid == 0) {
       s_pre[0] = 0;
       s_pre[1] = static_cast<int>((rows_total + BM - 1) / BM);
+      s_off[0] = 0;
+      s_off[1] = static_cast<int>(rows_total);
     }
-  } else if (tid < kWave) {
-    // wave 0: per-lane chunk of consecutive groups, then a wave prefix scan
-    const int per = (n_exp + kWave - 1) / kWave;
-    const int g0 = tid * per;
-    int sum = 0;
-    for (int g = g0; g < g0 + per && g < n_exp; ++g) {
-      int n = offsets[g + 1] - offsets[g];
-      sum += (n + BM - 1) / BM;
-    }
-    int incl = sum;
+  } else {
+    // one global round trip: every thread copies offsets into LDS, then wave 0
+    // scans per-lane chunks of consecutive groups
+    for (int g = tid; g <= n_exp; g += blockDim.x) s_off[g] = offsets[g];
+    __syncthreads();
+    if (tid < kWave) {
+      const int per = (n_exp + kWave - 1) / kWave;
+      const int g0 = tid * per;
+      int sum = 0;
+      for (int g = g0; g < g0 + per && g < n_exp; ++g) sum += (s_off[g + 1] - s_off[g] + BM - 1) / BM;
+      int incl = sum;
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      int v = __shfl_up(incl, o, kWave);
-      if (tid >= o) incl += v;
-    }
-    int run = incl - sum;
-    if (tid == 0) s_pre[0] = 0;
-    for (int g = g0; g < g0 + per && g < n_exp; ++g) {
-      int n = offsets[g + 1] - offsets[g];
-      run += (n + BM - 1) / BM;
-      s_pre[g + 1] = run;
+      for (int o = 1; o < kWave; o <<= 1) {
+        int v = __shfl_up(incl, o, kWave);
+        if (tid >= o) incl += v;
+      }
+      int run = incl - sum;
+      if (tid == 0) s_pre[0] = 0;
+      for (int g = g0; g < g0 + per && g < n_exp; ++g) {
+        run += (s_off[g + 1] - s_off[g] + BM - 1) / BM;
+        s_pre[g + 1] = run;
+      }
     }
   }
   __syncthreads();
-  const int total = s_pre[n_exp] * n_tiles;
-  const int rr = (total + kXcds - 1) / kXcds * kXcds;
-  const int w = blockIdx.x;
-  if (w >= rr) return false;
-  const int L = (w % kXcds) * (rr / kXcds) + w / kXcds;
-  if (L >= total) return false;
-  // group g with s_pre[g]*n_tiles <= L < s_pre[g+1]*n_tiles
-  int lo = 0, hi = n_exp;  // invariant: s_pre[lo]*nt <= L < s_pre[hi]*nt
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (s_pre[mid] * n_tiles <= L) lo = mid; else hi = mid;
+  return n_exp;
+}
+
+// Logical tile L (< s_pre[n_grp] * n_tiles) of a built map.  g_lo is a group
+// with s_pre[g_lo] * n_tiles <= L (0 when nothing better is known).
+__device__ __forceinline__ void tile_map_decode(int L, int n_grp, int BM, int n_tiles,
+                                                const int* s_pre, int g_lo, TileInfo& ti) {
+  const int* const s_off = s_pre + kMaxExperts + 1;
+  int g = g_lo;
+  if (s_pre[g + 1] * n_tiles <= L) {
+    int lo = g + 1, hi = n_grp;  // invariant: s_pre[lo]*nt <= L < s_pre[hi]*nt
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pre[mid] * n_tiles <= L) lo = mid; else hi = mid;
+    }
+    g = lo;
   }
-  const int g = lo;
   const int mt = s_pre[g + 1] - s_pre[g];
   const int i = L - s_pre[g] * n_tiles;
   ti.group = g;
@@ -194,10 +206,24 @@ __device__ __forceinline__ bool map_tile(const int* __restrict__ offsets, int n_
   const int ib = i - band * kBandRows * n_tiles;
   ti.n_tile = ib / bm;
   ti.m_tile = band * kBandRows + ib % bm;
-  const int base = offsets == nullptr ? 0 : offsets[g];
-  const int end = offsets == nullptr ? static_cast<int>(rows_total) : offsets[g + 1];
-  ti.row0 = base + ti.m_tile * BM;
-  ti.rows = min(BM, end - ti.row0);
+  ti.row0 = s_off[g] + ti.m_tile * BM;
+  ti.rows = min(BM, s_off[g + 1] - ti.row0);
+}
+
+// The tile of work-group blockIdx.x, for one-tile-per-work-group launches.
+// Returns false for a work-group with no tile (uniform across the work-group).
+// Must be called by all threads.
+__device__ __forceinline__ bool map_tile(const int* __restrict__ offsets, int n_exp,
+                                         int64_t rows_total, int BM, int n_tiles, int* s_pre,
+                                         TileInfo& ti) {
+  const int n_grp = tile_map_build(offsets, n_exp, rows_total, BM, s_pre);
+  const int total = s_pre[n_grp] * n_tiles;
+  const int rr = (total + kXcds - 1) / kXcds * kXcds;
+  const int w = blockIdx.x;
+  if (w >= rr) return false;
+  const int L = (w % kXcds) * (rr / kXcds) + w / kXcds;
+  if (L >= total) return false;
+  tile_map_decode(L, n_grp, BM, n_tiles, s_pre, 0, ti);
   return true;
 }
 

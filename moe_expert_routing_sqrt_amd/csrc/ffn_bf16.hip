@@ -10,8 +10,9 @@
 // Work-group tile 256 rows x 256 weight rows x 64 (K), 512 threads = 8 wave64s
 // laid out 4 x 2, each owning 2 x 4 blocks of 32x32 fp32 accumulators (64 rows x
 // 128 weight rows) fed by v_mfma_f32_32x32x16_bf16; two waves share each SIMD,
-// so one wave's memory stalls are covered by the other's MFMAs.  256 x 256 tiles halve the operand
-// bytes per FLOP of a 128 x 128 tile; a step moves 64 KB into LDS for 8.4 MFLOP.
+// so one wave's memory stalls are covered by the other's MFMAs.  256 x 256
+// tiles halve the operand bytes per FLOP of a 128 x 128 tile; a step moves
+// 64 KB into LDS for 8.4 MFLOP.
 //
 // Pipeline (two LDS stages of 64 KB, 128-byte rows, XOR-swizzled chunks):
 //   * a K step is four slices of 16; in the shadow of each MFMA a wave issues
@@ -23,6 +24,21 @@
 //     last slice's MFMAs cover both the reads of step k+1's first slice and
 //     the first half of step k+2's DMA; the second half goes out in the first
 //     slice of step k+1.
+//
+// Persistent work-groups: one per CU.  Logical tiles (the grouped tile map of
+// common.h) are split into one contiguous range per XCD, and the work-groups
+// of XCD x take tiles of range x in order from an atomic ticket counter, so
+// the tiles running together on an XCD are neighbours that share weights and
+// activations in its L2, and a CU that finishes a cheap ragged tile early
+// simply takes the next one.  A work-group holds its next ticket one tile
+// ahead; the DMA stream runs on across tiles (the last two K steps of a tile
+// fetch the first two of the next), so a new tile starts without a prologue,
+// and the tile map is built once per work-group.  The epilogue stages each
+// wave's output through a private 2 KB LDS slot, 8 rows at a time, so it never
+// touches the stages that already hold the next tile.  The ticket counters
+// live in a small device array; the last work-group to retire clears them,
+// and each launch takes the next of 16 counter sets, so launches on different
+// streams do not share one (up to 16 concurrently running launches).
 //
 // Ragged groups: a tile covers up to 256 rows of one expert.  Wave row wm owns
 // the 32-row blocks at rows 32*wm and 128 + 32*wm, so the two waves sharing a
@@ -36,6 +52,8 @@
 // SwiGLU is fused (mastering-deepseek-v4 Exp08, "Implemented"): a tile's 256
 // weight rows are 128 gate rows (W1) and the matching 128 up rows (W3), and
 // each wave holds the gate and up accumulators of the same 64 features.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -67,6 +85,17 @@ static_assert(NR <= NQ, "one fragment read per MFMA slot");
 static_assert(RM == 2, "a wave's blocks sit in the two halves of the tile");
 static_assert(NW % 2 == 0, "a wave's DMA blocks share the swizzle parity");
 
+// epilogue staging, per wave: 8 rows of up to TN bf16 columns
+constexpr int ST_PITCH = TN * 2 + 16;   // bytes; 17 chunks of 16, so rows start on different banks
+constexpr int ST_BYTES = 8 * ST_PITCH;
+
+// ticket counters: kSlots sets of kXcds counters plus a retire counter, each
+// on its own 64-byte line
+constexpr int kSlots = 16;
+constexpr int kCtrStride = 16;
+constexpr int kSlotInts = (kXcds + 1) * kCtrStride;
+__device__ int g_tickets[kSlots * kSlotInts];
+
 enum { MODE_SWIGLU = 0, MODE_STORE = 1, MODE_SWIGLU_SAVE = 2 };  // SAVE: also [a | u]
 
 struct FfnArgs {
@@ -79,298 +108,467 @@ struct FfnArgs {
   const int* offsets;      // [n_exp + 1] on the device, or nullptr (one group)
   int n_exp;
   int64_t rows_total;
-  int K;
+  int K;                   // multiple of 2*BK, at least 4*BK
   int n_tiles;             // column tiles per group
   int d_ff;                // SWIGLU: first up-projection row of w13
   uint16_t* C2;            // SWIGLU_SAVE: [a | u] output [rows, 2*d_ff]
+  int slot;                // ticket counter set of this launch
 };
+
+__device__ __forceinline__ void uniform_tile(TileInfo& t) {
+  t.group = __builtin_amdgcn_readfirstlane(t.group);
+  t.m_tile = __builtin_amdgcn_readfirstlane(t.m_tile);
+  t.n_tile = __builtin_amdgcn_readfirstlane(t.n_tile);
+  t.row0 = __builtin_amdgcn_readfirstlane(t.row0);
+  t.rows = __builtin_amdgcn_readfirstlane(t.rows);
+}
+
+// LDS writes of this wave are visible to its own later LDS reads
+__device__ __forceinline__ void wave_lds_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+}
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr bool SWI = MODE != MODE_STORE;
-  constexpr int OUT_COLS = SWI ? BN / 2 : BN;
-  constexpr int ROW_BYTES = OUT_COLS * 2;
-  constexpr int PITCH = ROW_BYTES + 16;  // output staging row pitch
-  constexpr int AU_PITCH = BN * 2 + 16;  // SWIGLU_SAVE: staging of [a | u]
   constexpr int STAGE = (BM + BN) * 8;   // uint4 per stage
-  constexpr int RING = 2 * STAGE;
-  constexpr int OUT_U4 = BM * (MODE == MODE_SWIGLU_SAVE ? AU_PITCH : PITCH) / 16;
-  __shared__ uint4 smem[RING > OUT_U4 ? RING : OUT_U4];
-  __shared__ int s_pre[kMaxExperts + 1];
+  __shared__ uint4 smem[2 * STAGE];
+  __shared__ uint4 s_stage[NW * ST_BYTES / 16];
+  __shared__ int s_map[kMapInts];
+  __shared__ int s_tick;
+  // [A stage 0 | A stage 1 | B stage 0 | B stage 1]: a fragment read is a
+  // per-lane base plus an immediate offset below 64 KB
   uint4* const sA0 = smem;
-  uint4* const sB0 = smem + BM * 8;
-  uint4* const sA1 = smem + STAGE;
-  uint4* const sB1 = smem + STAGE + BM * 8;
-
-  TileInfo ti;
-  if (!map_tile(p.offsets, p.n_exp, p.rows_total, BM, p.n_tiles, s_pre, ti)) return;
-  ti.group = __builtin_amdgcn_readfirstlane(ti.group);
-  ti.n_tile = __builtin_amdgcn_readfirstlane(ti.n_tile);
-  ti.row0 = __builtin_amdgcn_readfirstlane(ti.row0);
-  ti.rows = __builtin_amdgcn_readfirstlane(ti.rows);
+  uint4* const sA1 = smem + BM * 8;
+  uint4* const sB0 = smem + 2 * BM * 8;
+  uint4* const sB1 = smem + 2 * BM * 8 + BN * 8;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
-  // valid 32-row blocks of this wave: block i covers rows i*HB + 32*wm + [0, 32)
-  const int nb = __builtin_amdgcn_readfirstlane((ti.rows > 32 * wm) + (ti.rows > HB + 32 * wm));
+  const int xcd = blockIdx.x % kXcds;
+  int* const tickets = g_tickets + p.slot * kSlotInts;
 
-  // Direct-to-LDS loads: one instruction moves 64 lanes x 16 B into 1 KB of
-  // LDS at lane*16, i.e. 8 rows of 128 B.  The LDS slot of a lane is fixed, so
-  // the swizzle is applied to the global address: the lane filling physical
-  // chunk pc of row r fetches logical chunk pc ^ ((r >> 1) & 7).  This wave
-  // fills blocks j = wave + 8i (rows 8j..8j+7), for which (r >> 1) & 7 =
-  // 4*(wave & 1) + (lane >> 4).
-  const int lrow = lane >> 3;
-  const int lch = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
-  const uint16_t* a_src[ADMA];
-  const uint16_t* b_src[BDMA];
+  const int n_grp = tile_map_build(p.offsets, p.n_exp, p.rows_total, BM, s_map);
+  const int total = s_map[n_grp] * p.n_tiles;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int l_begin = xcd * per;
+  const int l_end = min(total, l_begin + per);
+  int tick_reg = 0;  // thread 0: the counter value fetched for the next tile
+  if (tid == 0) s_tick = l_begin + atomicAdd(&tickets[xcd * kCtrStride], 1);
+  __syncthreads();
+  const int l_first = __builtin_amdgcn_readfirstlane(s_tick);
+
+  if (l_first < l_end) {
+    const int nsteps = p.K / BK;
+    TileInfo ti, tn;
+    tile_map_decode(l_first, n_grp, BM, p.n_tiles, s_map, 0, ti);
+    uniform_tile(ti);
+    bool nx = false;  // a next tile exists (known from step nsteps-2 on)
+
+    // Direct-to-LDS loads: one instruction moves 64 lanes x 16 B into 1 KB of
+    // LDS at lane*16, i.e. 8 rows of 128 B.  The LDS slot of a lane is fixed, so
+    // the swizzle is applied to the global address: the lane filling physical
+    // chunk pc of row r fetches logical chunk pc ^ ((r >> 1) & 7).  This wave
+    // fills blocks j = wave + 8i (rows 8j..8j+7), for which (r >> 1) & 7 =
+    // 4*(wave & 1) + (lane >> 4).
+    const int lrow = lane >> 3;
+    const int lch = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+    // DMA sources: per-lane byte offsets that are the same for every tile,
+    // added to wave-uniform bases (the tile's first row; its group's weight
+    // tile).  Lanes whose row lies past the tile's valid rows are masked off,
+    // so no load leaves the tile's rows (their LDS rows keep stale values
+    // that only reach padding outputs).
+    uint32_t a_off[ADMA], b_off[BDMA];
+    int a_row[ADMA];  // tile row this lane loads for part i
 #pragma unroll
-  for (int i = 0; i < ADMA; ++i) {
-    const int r = (wave + NW * i) * 8 + lrow;
-    const int rc = r < ti.rows ? r : ti.rows - 1;  // padding rows read a valid row
-    a_src[i] = p.A + (int64_t)(ti.row0 + rc) * p.lda + lch * 8;
-  }
-  const uint16_t* bg = p.B + (int64_t)ti.group * p.b_group_stride + lch * 8;
-#pragma unroll
-  for (int i = 0; i < BDMA; ++i) {
-    const int r = (wave + NW * i) * 8 + lrow;
-    int grow;
-    if constexpr (SWI) {
-      // tile rows [part*TN, part*TN + TN/2) are gate rows, the next TN/2 the
-      // matching up rows, for features n_tile*BN/2 + part*TN/2 + [0, TN/2)
-      const int part = r / TN, within = r % TN;
-      const int h0 = ti.n_tile * (BN / 2) + part * (TN / 2);
-      grow = within < TN / 2 ? h0 + within : p.d_ff + h0 + (within - TN / 2);
-    } else {
-      grow = ti.n_tile * BN + r;
+    for (int i = 0; i < ADMA; ++i) {
+      a_row[i] = (wave + NW * i) * 8 + lrow;
+      a_off[i] = static_cast<uint32_t>((a_row[i] * p.lda + lch * 8) * 2);
     }
-    b_src[i] = bg + (int64_t)grow * p.K;
-  }
-  const int nsteps = p.K / BK;
-
-  // DMA part q of step kt into stage (sa, sb).  Activation blocks wholly past
-  // the valid rows are skipped after the first two steps (the in-loop waits are
-  // for zero outstanding loads, so per-wave counts may differ; the prologue
-  // wait counts every part).
-  auto dma_one = [&](int kt, uint4* sa, uint4* sb, int q) __attribute__((always_inline)) {
-    const int k0 = kt * BK;
-    if (q < ADMA) {
-      if (kt < 2 || (wave + NW * q) * 8 < ti.rows)
-        dma16(a_src[q] + k0, lds_addr(sa) + (wave + NW * q) * 1024);
-    } else {
-      dma16(b_src[q - ADMA] + k0, lds_addr(sb) + (wave + NW * (q - ADMA)) * 1024);
-    }
-  };
-
-  f32x16 acc[RM][RN];
 #pragma unroll
-  for (int i = 0; i < RM; ++i)
-#pragma unroll
-    for (int j = 0; j < RN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  // Fragments live in two register buffers, selected by slice parity.
-  // Fragment f of a slice, in order of first use: a0, b0..b(RN-1), a1..a(RM-1).
-  bf16x8 fa[2][RM], fb[2][RN];
-  auto read_frag = [&](const uint4* sa, const uint4* sb, int buf, int s, int f)
-                       __attribute__((always_inline)) {
-    const int kc = 2 * s + (lane >> 5);
-    if (f == 0) {
-      fa[buf][0] = as_bf16x8(sa[swz(32 * wm + (lane & 31), kc)]);
-    } else if (f <= RN) {
-      fb[buf][f - 1] = as_bf16x8(sb[swz(wn * TN + (f - 1) * 32 + (lane & 31), kc)]);
-    } else {
-      fa[buf][f - RN] = as_bf16x8(sa[swz((f - RN) * HB + 32 * wm + (lane & 31), kc)]);
-    }
-  };
-  // MFMAs of slice s over the first NB row blocks; reads of slice rs of
-  // (rsa, rsb) into the other buffer (rsa == nullptr: none); DMA parts
-  // [d0, d1) of step kd (kd < 0: none).  With one block there are five reads
-  // for four MFMA slots: the first slot takes two.
-  auto slice = [&](auto nbc, int s, const uint4* rsa, const uint4* rsb, int rs, int kd, uint4* da,
-                   uint4* db, int d0, int d1) __attribute__((always_inline)) {
-    constexpr int NB = decltype(nbc)::value;
-    constexpr int NQB = NB * RN, NRB = NB + RN;
-    constexpr int XR = NRB > NQB ? NRB - NQB : 0;  // reads doubled up in slot 0
-    const int buf = s & 1;
-    const int nd = d1 - d0;
-#pragma unroll
-    for (int q = 0; q < NQB; ++q) {
-      const int i = q / RN, j = q % RN;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
-      if (rsa != nullptr) {
-#pragma unroll
-        for (int f = 0; f < NRB; ++f)
-          if ((f < XR ? 0 : f - XR) == q) read_frag(rsa, rsb, buf ^ 1, rs, f);
+    for (int i = 0; i < BDMA; ++i) {
+      const int r = (wave + NW * i) * 8 + lrow;
+      int wrow;  // weight row relative to the tile's base
+      if constexpr (SWI) {
+        // tile rows [part*TN, part*TN + TN/2) are gate rows, the next TN/2 the
+        // matching up rows, for features n_tile*BN/2 + part*TN/2 + [0, TN/2)
+        const int part = r / TN, within = r % TN;
+        wrow = within < TN / 2 ? part * (TN / 2) + within : p.d_ff + part * (TN / 2) + (within - TN / 2);
+      } else {
+        wrow = r;
       }
-      if (kd >= 0) {
-#pragma unroll
-        for (int t = 0; t < NDMA; ++t)
-          if (t < nd && (t * NQB) / nd == q) dma_one(kd, da, db, d0 + t);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep this interleaving
+      b_off[i] = static_cast<uint32_t>(((int64_t)wrow * p.K + lch * 8) * 2);
     }
-  };
-  // Step kt computes from stage (sa, sb); (na, nb) holds step kt+1.
-  auto step = [&](auto nbc, int kt, uint4* sa, uint4* sb, uint4* na, uint4* nb)
-                  __attribute__((always_inline)) {
-    const bool more = kt + 1 < nsteps;
-    // second half of step kt+1's DMA (the prologue issued all of step 1's)
-    slice(nbc, 0, sa, sb, 1, (kt >= 1 && more) ? kt + 1 : -1, na, nb, DHALF, NDMA);
+    struct Src {
+      const char* a;  // activation row of the tile's first row
+      const char* b;  // the tile's first weight row
+      int rows;
+    };
+    auto src_of = [&](const TileInfo& t) __attribute__((always_inline)) {
+      Src x;
+      x.a = reinterpret_cast<const char*>(p.A + (int64_t)t.row0 * p.lda);
+      const int64_t w0 = (int64_t)t.n_tile * (SWI ? BN / 2 : BN);
+      x.b = reinterpret_cast<const char*>(p.B + (int64_t)t.group * p.b_group_stride + w0 * p.K);
+      x.rows = t.rows;
+      return x;
+    };
+    Src cur = src_of(ti), nxt = cur;
+
+    // DMA part q of K step kk of the current tile (or of the next one) into
+    // stage (sa, sb).
+    auto dma_one = [&](int kk, bool next, uint4* sa, uint4* sb, int q) __attribute__((always_inline)) {
+      const Src& x = next ? nxt : cur;
+      const int kb = kk * BK * 2;  // byte offset of the step along K
+      if (q < ADMA) {
+        if (a_row[q] < x.rows) dma16_s(x.a + kb, a_off[q], lds_addr(sa) + (wave + NW * q) * 1024);
+      } else {
+        dma16_s(x.b + kb, b_off[q - ADMA], lds_addr(sb) + (wave + NW * (q - ADMA)) * 1024);
+      }
+    };
+    // Step nsteps-2, after its barrier: take the next ticket and address
+    // that tile.
+    auto retarget = [&]() __attribute__((always_inline)) {
+      const int l_next = __builtin_amdgcn_readfirstlane(s_tick);
+      nx = l_next < l_end;
+      if (nx) {
+        tile_map_decode(l_next, n_grp, BM, p.n_tiles, s_map, ti.group, tn);
+        uniform_tile(tn);
+        nxt = src_of(tn);
+      }
+    };
+    // Step 0, after its barrier: thread 0 asks for the following ticket (its
+    // reply is waited for with the DMA at step 1's barrier, then published).
+    // (the counter's index carries an opaque zero, so the compiler keeps a
+    // plain one-lane atomic instead of a wave-combined one that reads its
+    // result back at once)
+    int zero = lane >> 6;
+    asm volatile("" : "+v"(zero));
+    auto ask_ticket = [&]() __attribute__((always_inline)) {
+      if (tid == 0) tick_reg = atomicAdd(&tickets[xcd * kCtrStride + zero], 1);
+    };
+    auto publish_ticket = [&]() __attribute__((always_inline)) {
+      if (tid == 0) s_tick = l_begin + tick_reg;
+    };
+
+    f32x16 acc[RM][RN];
+    bf16x8 fa[2][RM], fb[2][RN];
+    // Fragment rows start on multiples of 32, so the swizzle term (r >> 1) & 7
+    // of row r = base + (lane & 31) depends on the lane only: a read is a
+    // per-lane offset (one per slice) plus a constant row base.
+    // The wave's row base is folded into the per-lane offsets (one per slice
+    // and operand), so the fragments of a slice differ by constants only.
+    int a_lane[NS], b_lane[NS];
 #pragma unroll
-    for (int s = 1; s + 1 < NS; ++s) slice(nbc, s, sa, sb, s + 1, -1, nullptr, nullptr, 0, 0);
-    if (more) {
+    for (int s = 0; s < NS; ++s) {
+      const int off = (lane & 31) * 8 + ((2 * s + (lane >> 5)) ^ (((lane & 31) >> 1) & 7));
+      a_lane[s] = 32 * wm * 8 + off;
+      b_lane[s] = wn * TN * 8 + off;
+    }
+    auto read_frag = [&](const uint4* sa, const uint4* sb, int buf, int s, int f)
+                         __attribute__((always_inline)) {
+      if (f == 0) {
+        fa[buf][0] = as_bf16x8(sa[a_lane[s]]);
+      } else if (f <= RN) {
+        fb[buf][f - 1] = as_bf16x8(sb[b_lane[s] + (f - 1) * 32 * 8]);
+      } else {
+        fa[buf][f - RN] = as_bf16x8(sa[a_lane[s] + (f - RN) * HB * 8]);
+      }
+    };
+    // MFMAs of slice s over the first NB row blocks; reads of slice rs of
+    // (rsa, rsb) into the other buffer (rs < 0: none); DMA parts
+    // [d0, d1) of step kd (kd < 0: none).  With one block there are five reads
+    // for four MFMA slots: the first slot takes two.
+    auto slice = [&](auto nbc, int s, const uint4* rsa, const uint4* rsb, int rs, int kd, bool next,
+                     uint4* da, uint4* db, int d0, int d1) __attribute__((always_inline)) {
+      constexpr int NB = decltype(nbc)::value;
+      constexpr int NQB = NB * RN, NRB = NB + RN;
+      constexpr int XR = NRB > NQB ? NRB - NQB : 0;  // reads doubled up in slot 0
+      const int buf = s & 1;
+      const int nd = d1 - d0;
+#pragma unroll
+      for (int q = 0; q < NQB; ++q) {
+        const int i = q / RN, j = q % RN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+        if (rs >= 0) {
+#pragma unroll
+          for (int f = 0; f < NRB; ++f)
+            if ((f < XR ? 0 : f - XR) == q) read_frag(rsa, rsb, buf ^ 1, rs, f);
+        }
+        if (kd >= 0) {
+#pragma unroll
+          for (int t = 0; t < NDMA; ++t)
+            if (t < nd && (t * NQB) / nd == q) dma_one(kd, next, da, db, d0 + t);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep this interleaving
+      }
+    };
+    // K steps.  Step kt's second DMA half is that of step kt+1, its first
+    // half that of step kt+2; in the last two steps of a tile these are the
+    // first two steps of the next tile (stage parity carries over because
+    // nsteps is even).  Step kt computes from stage (sa, sb); (na, nb_) holds
+    // step kt+1.  The main loop runs steps 0 .. nsteps-3; the tail runs the
+    // last two, where the next tile is taken.
+    auto step = [&](auto nbc, int kt, uint4* sa, uint4* sb, uint4* na, uint4* nb_)
+                    __attribute__((always_inline)) {
+      slice(nbc, 0, sa, sb, 1, kt + 1, false, na, nb_, DHALF, NDMA);
+#pragma unroll
+      for (int s = 1; s + 1 < NS; ++s) slice(nbc, s, sa, sb, s + 1, -1, false, nullptr, nullptr, 0, 0);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): step kt's fragments are in registers
       wait_vmcnt<0>();                     // this wave's DMA of step kt+1 has landed
+      if (kt == 1) publish_ticket();
       barrier_only();                      // everyone's has; stage (sa, sb) is free
-    }
-    // last slice: reads of step kt+1's first slice, first half of step kt+2's DMA
-    slice(nbc, NS - 1, more ? na : nullptr, nb, 0, kt + 2 < nsteps ? kt + 2 : -1, sa, sb, 0, DHALF);
-  };
-  // A wave without valid rows keeps the same DMA parts and barriers.
-  auto idle_step = [&](int kt, uint4* sa, uint4* sb, uint4* na, uint4* nb) __attribute__((always_inline)) {
-    const bool more = kt + 1 < nsteps;
-    if (kt >= 1 && more) {
+      if (kt == 0) ask_ticket();
+      // last slice: reads of step kt+1's first slice, first DMA half of step kt+2
+      slice(nbc, NS - 1, na, nb_, 0, kt + 2, false, sa, sb, 0, DHALF);
+    };
+    // the last two steps: stages 0 and 1
+    auto tail = [&](auto nbc) __attribute__((always_inline)) {
+      // step nsteps-2: this tile's step nsteps-1, then the next tile's step 0
+      slice(nbc, 0, sA0, sB0, 1, nsteps - 1, false, sA1, sB1, DHALF, NDMA);
 #pragma unroll
-      for (int q = DHALF; q < NDMA; ++q) dma_one(kt + 1, na, nb, q);
-    }
-    if (more) {
+      for (int s = 1; s + 1 < NS; ++s) slice(nbc, s, sA0, sB0, s + 1, -1, false, nullptr, nullptr, 0, 0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
       wait_vmcnt<0>();
       barrier_only();
-    }
-    if (kt + 2 < nsteps) {
+      retarget();
+      slice(nbc, NS - 1, sA1, sB1, 0, nx ? 0 : -1, true, sA0, sB0, 0, DHALF);
+      // step nsteps-1: the next tile's step 0 (second half) and step 1 (first half)
+      slice(nbc, 0, sA1, sB1, 1, nx ? 0 : -1, true, sA0, sB0, DHALF, NDMA);
 #pragma unroll
-      for (int q = 0; q < DHALF; ++q) dma_one(kt + 2, sa, sb, q);
-    }
-  };
-
-#pragma unroll
-  for (int q = 0; q < NDMA; ++q) dma_one(0, sA0, sB0, q);
-  if (nsteps > 1) {
-#pragma unroll
-    for (int q = 0; q < NDMA; ++q) dma_one(1, sA1, sB1, q);
-    wait_vmcnt<NDMA>();  // step 0 landed; step 1 may be in flight
-  } else {
-    wait_vmcnt<0>();
-  }
-  barrier_only();
-  if (nb == RM) {
-    using NBC = std::integral_constant<int, RM>;
-#pragma unroll
-    for (int f = 0; f < NR; ++f) read_frag(sA0, sB0, 0, 0, f);
-    for (int kt = 0; kt < nsteps; kt += 2) {
-      step(NBC{}, kt, sA0, sB0, sA1, sB1);
-      if (kt + 1 < nsteps) step(NBC{}, kt + 1, sA1, sB1, sA0, sB0);
-    }
-  } else if (nb == 1) {
-    using NBC = std::integral_constant<int, 1>;
-#pragma unroll
-    for (int f = 0; f <= RN; ++f) read_frag(sA0, sB0, 0, 0, f);
-    for (int kt = 0; kt < nsteps; kt += 2) {
-      step(NBC{}, kt, sA0, sB0, sA1, sB1);
-      if (kt + 1 < nsteps) step(NBC{}, kt + 1, sA1, sB1, sA0, sB0);
-    }
-  } else {
-    for (int kt = 0; kt < nsteps; kt += 2) {
-      idle_step(kt, sA0, sB0, sA1, sB1);
-      if (kt + 1 < nsteps) idle_step(kt + 1, sA1, sB1, sA0, sB0);
-    }
-  }
-
-  // Epilogue.  Accumulator (i, j) register v holds row 8*(v/4) + 4*(lane/32) +
-  // v%4 and column lane%32 of its 32x32 block, so each lane owns one column.
-  // The tile is staged in LDS (row pitch padded by 16 bytes) and leaves as
-  // 16-byte row chunks.  All DMA has landed (the last in-loop wait was for
-  // zero outstanding); the barrier ends every wave's reads of the last stage.
-  // Registers v and v+1 (v even) are consecutive rows of one column: each pair
-  // is rounded by one packed conversion and leaves as two 2-byte LDS writes.
-  // silu(g) = g / (1 + e^-g) takes the hardware reciprocal (1 ulp, far below
-  // the bf16 rounding of h).
-  char* const stage = reinterpret_cast<char*>(smem);
-  auto put2 = [&](int lr, int col, int pitch, uint32_t pk) __attribute__((always_inline)) {
-    uint16_t* r0 = reinterpret_cast<uint16_t*>(stage + lr * pitch);
-    uint16_t* r1 = reinterpret_cast<uint16_t*>(stage + (lr + 1) * pitch);
-    r0[col] = static_cast<uint16_t>(pk);
-    r1[col] = static_cast<uint16_t>(pk >> 16);
-  };
-  auto silu_mul = [](float g, float u) __attribute__((always_inline)) {
-    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-  };
-  barrier_only();
-  if (nb > 0) {
-#pragma unroll
-    for (int i = 0; i < RM; ++i) {
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        const int lr = i * HB + 32 * wm + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if constexpr (SWI) {
-#pragma unroll
-          for (int jj = 0; jj < RN / 2; ++jj) {
-            const f32x16& g = acc[i][jj];
-            const f32x16& u = acc[i][jj + RN / 2];
-            put2(lr, wn * (TN / 2) + jj * 32 + (lane & 31), PITCH,
-                 pack_bf16x2(silu_mul(g[v], u[v]), silu_mul(g[v + 1], u[v + 1])));
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < RN; ++j)
-            put2(lr, wn * TN + j * 32 + (lane & 31), PITCH, pack_bf16x2(acc[i][j][v], acc[i][j][v + 1]));
-        }
+      for (int s = 1; s + 1 < NS; ++s) slice(nbc, s, sA1, sB1, s + 1, -1, false, nullptr, nullptr, 0, 0);
+      if (nx) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        wait_vmcnt<0>();  // the next tile's step 0 has landed
+        barrier_only();
       }
-    }
-  }
-  __syncthreads();
-  constexpr int OCH = ROW_BYTES / 16;
-  const int64_t col0 = (int64_t)ti.n_tile * OUT_COLS;
-  for (int q = tid; q < ti.rows * OCH; q += kThreads) {
-    const int r = q / OCH, c = q % OCH;
-    const uint4 v = *reinterpret_cast<const uint4*>(stage + r * PITCH + c * 16);
-    char* dst = reinterpret_cast<char*>(p.C + (ti.row0 + r) * p.ldc + col0) + c * 16;
-    *reinterpret_cast<uint4*>(dst) = v;
-  }
-  if constexpr (MODE == MODE_SWIGLU_SAVE) {
-    // the pre-activations for the backward: a (gate) at columns
-    // [n_tile*BN/2, +BN/2) and u (up) at d_ff + the same, bf16
-    __syncthreads();  // every read of the h staging is done
-    if (nb > 0) {
+      slice(nbc, NS - 1, sA0, sB0, -1, nx ? 1 : -1, true, sA1, sB1, 0, DHALF);
+    };
+    // A wave without valid rows keeps the same DMA parts and barriers.
+    auto idle_dma = [&](int kd, bool next, uint4* da, uint4* db, int d0, int d1) __attribute__((always_inline)) {
+      if (kd >= 0) {
+#pragma unroll
+        for (int q = 0; q < NDMA; ++q)
+          if (q >= d0 && q < d1) dma_one(kd, next, da, db, q);
+      }
+    };
+    auto idle_step = [&](int kt, uint4* sa, uint4* sb, uint4* na, uint4* nb_) __attribute__((always_inline)) {
+      idle_dma(kt + 1, false, na, nb_, DHALF, NDMA);
+      wait_vmcnt<0>();
+      if (kt == 1) publish_ticket();
+      barrier_only();
+      if (kt == 0) ask_ticket();
+      idle_dma(kt + 2, false, sa, sb, 0, DHALF);
+    };
+    auto idle_tail = [&]() __attribute__((always_inline)) {
+      idle_dma(nsteps - 1, false, sA1, sB1, DHALF, NDMA);
+      wait_vmcnt<0>();
+      barrier_only();
+      retarget();
+      idle_dma(nx ? 0 : -1, true, sA0, sB0, 0, DHALF);
+      idle_dma(nx ? 0 : -1, true, sA0, sB0, DHALF, NDMA);
+      if (nx) {
+        wait_vmcnt<0>();
+        barrier_only();
+      }
+      idle_dma(nx ? 1 : -1, true, sA1, sB1, 0, DHALF);
+    };
+
+    // Epilogue of tile ti, by each wave for its own rows.  Accumulator (i, j)
+    // register v holds row 8*(v/4) + 4*(lane/32) + v%4 and column lane%32 of
+    // its 32x32 block; a pass takes the 8 rows of one v/4 and leaves as
+    // 16-byte row chunks through this wave's staging slot.  Registers v and
+    // v+1 (v even) are consecutive rows of one column: each pair is rounded by
+    // one packed conversion.  silu(g) = g / (1 + e^-g) takes the hardware
+    // reciprocal (1 ulp, far below the bf16 rounding of h).
+    char* const st = reinterpret_cast<char*>(s_stage) + wave * ST_BYTES;
+    auto put2 = [&](int lr, int col, uint32_t pk) __attribute__((always_inline)) {
+      reinterpret_cast<uint16_t*>(st + lr * ST_PITCH)[col] = static_cast<uint16_t>(pk);
+      reinterpret_cast<uint16_t*>(st + (lr + 1) * ST_PITCH)[col] = static_cast<uint16_t>(pk >> 16);
+    };
+    // (the epilogue's addresses derive from an opaque copy of the lane index,
+    // so the compiler computes them per tile instead of holding them in
+    // registers through the K loop)
+    auto silu_mul = [](float g, float u) __attribute__((always_inline)) {
+      return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+    };
+    auto epilogue = [&](int nb) __attribute__((always_inline)) {
+      int lane = tid & 63;
+      asm volatile("" : "+v"(lane));
+      constexpr int OUT_COLS = SWI ? BN / 2 : BN;
+      const int64_t col0 = (int64_t)ti.n_tile * OUT_COLS;
+      const int lr0 = 4 * (lane >> 5);
 #pragma unroll
       for (int i = 0; i < RM; ++i) {
+        if (i >= nb) continue;
 #pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          const int lr = i * HB + 32 * wm + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        for (int quad = 0; quad < 4; ++quad) {
+          const int rb = i * HB + 32 * wm + 8 * quad;  // tile row of the pass's first row
+          if (rb >= ti.rows) continue;
+          const int64_t grow0 = (int64_t)ti.row0 + rb;
 #pragma unroll
-          for (int jj = 0; jj < RN / 2; ++jj) {
-            const int c = wn * (TN / 2) + jj * 32 + (lane & 31);
-            put2(lr, c, AU_PITCH, pack_bf16x2(acc[i][jj][v], acc[i][jj][v + 1]));
-            put2(lr, BN / 2 + c, AU_PITCH, pack_bf16x2(acc[i][jj + RN / 2][v], acc[i][jj + RN / 2][v + 1]));
+          for (int v = 4 * quad; v < 4 * quad + 4; v += 2) {
+            const int lr = lr0 + (v & 3);
+            if constexpr (SWI) {
+#pragma unroll
+              for (int jj = 0; jj < RN / 2; ++jj) {
+                const f32x16& g = acc[i][jj];
+                const f32x16& u = acc[i][jj + RN / 2];
+                put2(lr, jj * 32 + (lane & 31), pack_bf16x2(silu_mul(g[v], u[v]), silu_mul(g[v + 1], u[v + 1])));
+              }
+            } else {
+#pragma unroll
+              for (int j = 0; j < RN; ++j)
+                put2(lr, j * 32 + (lane & 31), pack_bf16x2(acc[i][j][v], acc[i][j][v + 1]));
+            }
           }
+          wave_lds_fence();
+          if constexpr (SWI) {
+            // 8 rows x 128 B: one chunk per lane
+            const int r = lane >> 3, c = lane & 7;
+            if (rb + r < ti.rows) {
+              const uint4 val = *reinterpret_cast<const uint4*>(st + r * ST_PITCH + c * 16);
+              *reinterpret_cast<uint4*>(p.C + (grow0 + r) * p.ldc + col0 + wn * (TN / 2) + c * 8) = val;
+            }
+          } else {
+            // 8 rows x 256 B: two chunks per lane
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int q = lane + 64 * h;
+              const int r = q >> 4, c = q & 15;
+              if (rb + r < ti.rows) {
+                const uint4 val = *reinterpret_cast<const uint4*>(st + r * ST_PITCH + c * 16);
+                *reinterpret_cast<uint4*>(p.C + (grow0 + r) * p.ldc + col0 + wn * TN + c * 8) = val;
+              }
+            }
+          }
+          if constexpr (MODE == MODE_SWIGLU_SAVE) {
+            // the pre-activations for the backward: a (gate) at column
+            // col0 + f and u (up) at d_ff + col0 + f, bf16
+            wave_lds_fence();  // the h chunks have been read
+#pragma unroll
+            for (int v = 4 * quad; v < 4 * quad + 4; v += 2) {
+              const int lr = lr0 + (v & 3);
+#pragma unroll
+              for (int jj = 0; jj < RN / 2; ++jj) {
+                const int c = jj * 32 + (lane & 31);
+                put2(lr, c, pack_bf16x2(acc[i][jj][v], acc[i][jj][v + 1]));
+                put2(lr, TN / 2 + c, pack_bf16x2(acc[i][jj + RN / 2][v], acc[i][jj + RN / 2][v + 1]));
+              }
+            }
+            wave_lds_fence();
+            const int64_t ld2 = 2 * (int64_t)p.d_ff;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int q = lane + 64 * h;
+              const int r = q >> 4, c = q & 15;
+              const int half = c >> 3, cc = c & 7;
+              if (rb + r < ti.rows) {
+                const uint4 val = *reinterpret_cast<const uint4*>(st + r * ST_PITCH + c * 16);
+                *reinterpret_cast<uint4*>(p.C2 + (grow0 + r) * ld2 + half * p.d_ff + col0 +
+                                          wn * (TN / 2) + cc * 8) = val;
+              }
+            }
+          }
+          wave_lds_fence();  // the chunks have been read before the next pass overwrites the slot
         }
       }
+    };
+
+    // prologue of the first tile: what a tile's predecessor sends in its last
+    // two steps (all of step 0, the first half of step 1)
+#pragma unroll
+    for (int q = 0; q < NDMA; ++q) dma_one(0, false, sA0, sB0, q);
+#pragma unroll
+    for (int q = 0; q < DHALF; ++q) dma_one(1, false, sA1, sB1, q);
+    wait_vmcnt<0>();
+    barrier_only();
+
+    for (;;) {
+      // valid 32-row blocks of this wave: block i covers rows i*HB + 32*wm + [0, 32)
+      const int nb = __builtin_amdgcn_readfirstlane((ti.rows > 32 * wm) + (ti.rows > HB + 32 * wm));
+#pragma unroll
+      for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int j = 0; j < RN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+      if (nb == RM) {
+        using NBC = std::integral_constant<int, RM>;
+#pragma unroll
+        for (int f = 0; f < NR; ++f) read_frag(sA0, sB0, 0, 0, f);
+        for (int kt = 0; kt < nsteps - 2; kt += 2) {
+          step(NBC{}, kt, sA0, sB0, sA1, sB1);
+          step(NBC{}, kt + 1, sA1, sB1, sA0, sB0);
+        }
+        tail(NBC{});
+      } else if (nb == 1) {
+        using NBC = std::integral_constant<int, 1>;
+#pragma unroll
+        for (int f = 0; f <= RN; ++f) read_frag(sA0, sB0, 0, 0, f);
+        for (int kt = 0; kt < nsteps - 2; kt += 2) {
+          step(NBC{}, kt, sA0, sB0, sA1, sB1);
+          step(NBC{}, kt + 1, sA1, sB1, sA0, sB0);
+        }
+        tail(NBC{});
+      } else {
+        for (int kt = 0; kt < nsteps - 2; kt += 2) {
+          idle_step(kt, sA0, sB0, sA1, sB1);
+          idle_step(kt + 1, sA1, sB1, sA0, sB0);
+        }
+        idle_tail();
+      }
+      epilogue(nb);
+      if (!nx) break;
+      ti = tn;
+      cur = nxt;
+      nx = false;
     }
-    __syncthreads();
-    constexpr int HCH = BN / 2 * 2 / 16;  // 16-byte chunks per half row
-    const int64_t ld2 = 2 * (int64_t)p.d_ff;
-    for (int q = tid; q < ti.rows * 2 * HCH; q += kThreads) {
-      const int r = q / (2 * HCH), c = q % (2 * HCH);
-      const int half = c / HCH, cc = c % HCH;
-      const uint4 v = *reinterpret_cast<const uint4*>(stage + r * AU_PITCH + c * 16);
-      uint16_t* dst = p.C2 + (ti.row0 + r) * ld2 + half * p.d_ff + col0 + cc * 8;
-      *reinterpret_cast<uint4*>(dst) = v;
+  }
+  // retire: the last work-group out clears this launch's counters
+  if (tid == 0) {
+    if (atomicAdd(&tickets[kXcds * kCtrStride], 1) == (int)gridDim.x - 1) {
+#pragma unroll
+      for (int x = 0; x <= kXcds; ++x) atomicExch(&tickets[x * kCtrStride], 0);
     }
   }
 #endif
 }
 
+std::atomic<unsigned> g_launches{0};
+
+// compute units of the current device (cached per device)
+int cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int MODE>
-hipError_t launch(const FfnArgs& a, int64_t max_rows, hipStream_t s) {
+hipError_t launch(FfnArgs& a, int64_t max_rows, hipStream_t s) {
+  if (a.K % (2 * BK) != 0 || a.K < 4 * BK) return hipErrorInvalidValue;
+  // 32-bit per-lane DMA offsets: a tile's rows and a group's weights
+  const int64_t b_rows = MODE == MODE_STORE ? (int64_t)a.n_tiles * BN : 2 * (int64_t)a.d_ff;
+  if ((int64_t)BM * a.lda * 2 >= (1LL << 31) || b_rows * a.K * 2 >= (1LL << 31)) return hipErrorInvalidValue;
   const int64_t mt = max_row_tiles(max_rows, a.offsets == nullptr ? 1 : a.n_exp, BM);
-  const int64_t grid = (mt * a.n_tiles + kXcds - 1) / kXcds * kXcds;
-  if (grid <= 0) return hipSuccess;
+  const int64_t tiles = mt * a.n_tiles;
+  if (tiles <= 0) return hipSuccess;
+  // one work-group per CU (the LDS holds one), a multiple of the XCD count
+  const int64_t grid = (std::min<int64_t>(tiles, cu_count()) + kXcds - 1) / kXcds * kXcds;
+  a.slot = static_cast<int>(g_launches.fetch_add(1, std::memory_order_relaxed) % kSlots);
   hipLaunchKernelGGL((ffn_gemm_kernel<MODE>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_bwd_kernel(const BwdArgs p) {
   constexpr int OUT_U4 = MODE == MODE_DGRAD ? BM * OUT_PITCH / 16 : 0;
   constexpr int RING = 2 * STAGE;
   __shared__ uint4 smem[RING > OUT_U4 ? RING : OUT_U4];
-  __shared__ int s_pre[kMaxExperts + 1];
+  __shared__ int s_pre[kMapInts];
   char* const base = reinterpret_cast<char*>(smem);
   char* const sA0 = base;
   char* const sB0 = base + 32 * 1024;

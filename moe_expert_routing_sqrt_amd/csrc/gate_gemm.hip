@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kThreads, 1) void gate_gemm_kernel(const GateArgs p
   // stages the output tile so it leaves in 16-byte row chunks
   constexpr int STAGE = (BM + BN) * 8;  // uint4 per stage
   __shared__ uint4 smem[3 * STAGE];
-  __shared__ int s_pre[kMaxExperts + 1];
+  __shared__ int s_pre[kMapInts];
   uint4* const sA0 = smem;
   uint4* const sB0 = smem + BM * 8;
   uint4* const sA1 = smem + STAGE;

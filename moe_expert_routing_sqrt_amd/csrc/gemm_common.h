@@ -48,6 +48,20 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(gaddr) : "memory", "m0");
 }
 
+// The same load with a wave-uniform 64-bit base in scalar registers and a
+// 32-bit per-lane byte offset (the saddr form): one address VGPR per load,
+// and stepping through K is scalar arithmetic on the base.
+__device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_t lds) {
+  // (readfirstlane yields an int: both halves go through uint32_t before
+  // widening, so the low half is not sign-extended into the high one)
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b >> 32)));
+  const uint64_t sb = (static_cast<uint64_t>(hi) << 32) | lo;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sb) : "memory", "m0");
+}
+
 // 64 lanes x 4 bytes from global memory into 256 contiguous LDS bytes at
 // lds + lane*4 (global_load_lds_dword), for per-row scale columns.
 __device__ __forceinline__ void dma4(const void* gaddr, uint32_t lds) {

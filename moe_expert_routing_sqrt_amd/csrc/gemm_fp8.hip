@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const Fp8Args p) 
   __shared__ uint4 sB0[BN * 8], sB1[BN * 8], sB2[BN * 8];
   __shared__ float sS0[BM], sS1[BM], sS2[BM];
   __shared__ float s_amax[WAVES_N][BM];
-  __shared__ int s_pre[kMaxExperts + 1];
+  __shared__ int s_pre[kMapInts];
 
   TileInfo ti;
   if (!map_tile(p.offsets, p.n_exp, p.rows_total, BM, p.n_tiles, s_pre, ti)) return;

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void gemm_simt_kernel(const SimtArgs p) {
   __shared__ float sA[BKs][BM + 1];
   __shared__ float sB[BKs][BN + 1];
   __shared__ float sB2[BKs][BN + 1];
-  __shared__ int s_pre[kMaxExperts + 1];
+  __shared__ int s_pre[kMapInts];
 
   TileInfo ti;
   if (!map_tile(p.offsets, p.n_exp, p.rows_total, BM, p.n_tiles, s_pre, ti)) return;
