@@ -181,9 +181,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
     const int lch = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
     // DMA sources: per-lane byte offsets that are the same for every tile,
     // added to wave-uniform bases (the tile's first row; its group's weight
-    // tile).  Lanes whose row lies past the tile's valid rows are masked off,
-    // so no load leaves the tile's rows (their LDS rows keep stale values
-    // that only reach padding outputs).
+    // tile).  Rows past the tile's valid rows: an 8-row block wholly past them
+    // is not loaded (a wave-uniform branch, no instruction issued); in the
+    // block that straddles the end, the lanes of invalid rows read the tile's
+    // first row instead.  Every address stays inside the tile's rows (LDS-DMA
+    // lanes switched off by EXEC were measured to still fetch), and the
+    // padding rows' LDS values only reach padding outputs.
     uint32_t a_off[ADMA], b_off[BDMA];
     int a_row[ADMA];  // tile row this lane loads for part i
 #pragma unroll
@@ -226,7 +229,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
       const Src& x = next ? nxt : cur;
       const int kb = kk * BK * 2;  // byte offset of the step along K
       if (q < ADMA) {
-        if (a_row[q] < x.rows) dma16_s(x.a + kb, a_off[q], lds_addr(sa) + (wave + NW * q) * 1024);
+        if ((wave + NW * q) * 8 < x.rows)
+          dma16_s(x.a + kb, a_row[q] < x.rows ? a_off[q] : static_cast<uint32_t>(lch * 16),
+                  lds_addr(sa) + (wave + NW * q) * 1024);
       } else {
         dma16_s(x.b + kb, b_off[q - ADMA], lds_addr(sb) + (wave + NW * (q - ADMA)) * 1024);
       }
