@@ -40,9 +40,9 @@ TRAFFIC_SOURCES = ("moe_expert_routing_sqrt_amd/csrc/ffn_bf16.hip",
                    "moe_expert_routing_sqrt_amd/csrc/common.h",
                    "moe_expert_routing_sqrt_amd/build.py")
 TRAFFIC = {
-    "v3": {"sources_sha256": "ba7a4f7cbfe7db1a83ea1e48c0ec4667e8ab3bf452e6be37ff238f17f94355fc",
-           "fetch_kib": 16543786.5, "fetch_scale": 1.99997,
-           "write_kib": 524288.0, "write_scale": 1.0},
+    "v3": {"sources_sha256": "b94bb83c4c5673da3526d482113d7a0c3caff54901c1a45ae3295581fb9aaf26",
+           "fetch_kib": 18773260.9, "fetch_scale": 1.99997,
+           "write_kib": 524627.8, "write_scale": 1.0},
 }
 
 
