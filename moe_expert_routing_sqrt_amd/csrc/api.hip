@@ -144,7 +144,7 @@ int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int3
   }
   if (max_rows == 0) return MOE_OK;
   hipStream_t s = as_stream(stream);
-  const bool mfma = dtype == MOE_BF16 && d % 256 == 0 && d_ff % 128 == 0;
+  const bool mfma = dtype == MOE_BF16 && d % 256 == 0 && d_ff % 128 == 0 && d_ff >= 256;
   if (up) {
     hipError_t e;
     if (dtype == MOE_E4M3)

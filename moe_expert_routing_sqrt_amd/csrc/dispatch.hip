@@ -40,8 +40,11 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
   const bool active = part < parts && tid < parts * n;
   const int b0 = part * bpp, b1 = min(nblk, b0 + bpp);
 
+  // (the block loops are unrolled so that a thread's loads are in flight
+  // together rather than one round trip per block)
   int sum = 0;
   if (active) {
+#pragma unroll 8
     for (int b = b0; b < b1; ++b) sum += block_counts[(int64_t)b * E + e_begin + e];
     s_part[part * n + e] = sum;
   }
@@ -82,6 +85,7 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
   __syncthreads();
   if (active) {
     int run = s_tot[e] + s_part[part * n + e];
+#pragma unroll 8
     for (int b = b0; b < b1; ++b) {
       base[(int64_t)b * n + e] = run;
       run += block_counts[(int64_t)b * E + e_begin + e];

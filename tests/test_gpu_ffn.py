@@ -55,6 +55,15 @@ def test_ffn_odd_width_uses_vector_path():
     assert rel_max_err(got, ref) <= 2e-2
 
 
+def test_ffn_narrow_hidden_width():
+    # d_ff = 128: the down-projection's K is too short for the matrix-core
+    # pipeline (it needs K >= 256); d_ff = 384: the smallest K of an odd
+    # number of 128-column blocks that still takes it
+    for d_ff, counts in ((128, [5, 300, 0, 17]), (384, [260, 1, 0, 511])):
+        got, ref = _ragged_case("bf16", 256, d_ff, counts, seed=d_ff)
+        assert rel_max_err(got, ref) <= 2e-2, d_ff
+
+
 @pytest.mark.parametrize("name", ["tiny", "flash"])
 def test_ffn_workload_full(name):
     """Every routed expert of the workload, from the oracle's packed rows."""
