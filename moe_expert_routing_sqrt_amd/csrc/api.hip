@@ -147,7 +147,11 @@ int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int3
   const bool mfma = dtype == MOE_BF16 && d % 256 == 0 && d_ff % 128 == 0 && d_ff >= 256;
   if (up) {
     hipError_t e;
-    if (dtype == MOE_E4M3)
+    if (dtype == MOE_E4M3 && ffn_fp8p_supported_k(d))
+      e = launch_ffn_up_fp8p(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint8_t*>(xp),
+                             xp_scale, static_cast<const uint8_t*>(w13), w13_scale,
+                             static_cast<uint8_t*>(h), h_scale, s);
+    else if (dtype == MOE_E4M3)
       e = launch_ffn_up_fp8(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint8_t*>(xp),
                             xp_scale, static_cast<const uint8_t*>(w13), w13_scale,
                             static_cast<uint8_t*>(h), h_scale, s);
@@ -160,7 +164,11 @@ int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int3
   }
   if (down) {
     hipError_t e;
-    if (dtype == MOE_E4M3)
+    if (dtype == MOE_E4M3 && ffn_fp8p_supported_k(d_ff))
+      e = launch_ffn_down_fp8p(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint8_t*>(h),
+                               h_scale, static_cast<const uint8_t*>(w2), w2_scale,
+                               static_cast<uint16_t*>(yp), s);
+    else if (dtype == MOE_E4M3)
       e = launch_ffn_down_fp8(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint8_t*>(h),
                               h_scale, static_cast<const uint8_t*>(w2), w2_scale,
                               static_cast<uint16_t*>(yp), s);

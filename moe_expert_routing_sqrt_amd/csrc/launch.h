@@ -53,6 +53,14 @@ hipError_t launch_ffn_down_fp8(int n_exp, const int32_t* offsets, int64_t max_ro
                                int d_ff, const uint8_t* h, const float* h_scale,
                                const uint8_t* w2, const float* w2_scale, uint16_t* yp,
                                hipStream_t s);
+// persistent form (gemm_fp8p.hip) for K % 256 == 0 and K >= 512
+bool ffn_fp8p_supported_k(int K);
+hipError_t launch_ffn_up_fp8p(int n_exp, const int32_t* offsets, int64_t max_rows, int d, int d_ff,
+                              const uint8_t* xp, const float* xp_scale, const uint8_t* w13,
+                              const float* w13_scale, uint8_t* h, float* h_scale, hipStream_t s);
+hipError_t launch_ffn_down_fp8p(int n_exp, const int32_t* offsets, int64_t max_rows, int d, int d_ff,
+                                const uint8_t* h, const float* h_scale, const uint8_t* w2,
+                                const float* w2_scale, uint16_t* yp, hipStream_t s);
 
 // combine
 hipError_t launch_combine(int64_t T, int k, int d, const int32_t* dest, const float* w,

@@ -118,6 +118,21 @@ def _fp8_ffn_case(counts, d, d_ff, seed):
     return host(yp)[: int(offsets[-1])], ref, emu, raw
 
 
+@pytest.mark.parametrize("d,d_ff", [(512, 512), (1024, 768), (768, 256), (256, 512)])
+def test_fp8_ffn_widths(d, d_ff):
+    """Reduction widths (d for the up-projection, d_ff for the down) at and
+    past the persistent kernel's minimum of 512 (4, 6 and 8 scale blocks)
+    and below it (256, taken by the other kernel), with ragged groups."""
+    counts = [0, 1, 127, 128, 129, 300, 0, 5]
+    print(f"fp8 ffn d={d} d_ff={d_ff} {counts}", flush=True)
+    got, ref, emu, raw = _fp8_ffn_case(counts, d, d_ff, seed=d + d_ff)
+    e_ref, e_emu, e_raw = rel_max_err(got, ref), rel_max_err(got, emu), rel_max_err(got, raw)
+    print(f"  vs e4m3 weights {e_ref:.3e}  vs emulation {e_emu:.3e}  vs unquantised {e_raw:.3e}")
+    assert e_emu <= 2e-2
+    assert e_ref <= 6e-2
+    assert e_raw <= 1e-1
+
+
 @pytest.mark.parametrize("counts", [[0, 1, 127, 128, 129, 300, 0, 5], [513, 0, 0, 255], [1]])
 def test_fp8_ffn_ragged(counts):
     print(f"fp8 ffn {counts}", flush=True)
