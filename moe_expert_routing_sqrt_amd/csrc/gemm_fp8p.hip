@@ -19,24 +19,27 @@
 // (the same count as an explicit FMA promotion of a partial sum) and no
 // partial-sum registers.
 //
-// Tile 128 rows x 256 weight rows: the 1 x 128 quantisation tile of h (128
-// features = 256 gate/up weight rows) must lie in one work-group.  8 waves as
-// 2 x 4, each 64 x 64 (2 x 2 blocks of 32x32; an fp8 fragment is 8 VGPRs, so
-// larger wave tiles do not fit two waves per SIMD).  A K step is 128 bytes per
-// row (one scale block; two v_mfma_scale_f32_32x32x64_f8f6f4 slices with unit
-// matrix-core scales).  The rest follows the bf16 kernel (ffn_bf16.hip): two
-// 48 KB stages of swizzled 128-byte rows filled by direct-to-LDS DMA,
-// fragment reads of the next slice one per MFMA slot, persistent work-groups
-// taking ticketed tiles with the DMA stream running on across tiles, a
-// wave's row blocks in both halves of the tile.  The activation row scales
-// travel by 4-byte DMA into a ring of four slots; the weight block scales
-// are scalar loads.
+// Tile 256 rows x 256 weight rows (the 1 x 128 quantisation tile of h, 128
+// features = 256 gate/up weight rows, lies in one work-group).  8 waves as
+// 4 x 2, each 64 x 128 (2 x 4 blocks of 32x32).  A K step is 128 bytes per row
+// (one scale block; two v_mfma_scale_f32_32x32x64_f8f6f4 slices with unit
+// matrix-core scales) and moves 64 KB for 16.8 MFLOP: a 128-row tile would
+// need half again as many bytes per FLOP, more than the per-CU load path
+// delivers at the fp8 rate.  An fp8 fragment is 8 VGPRs, so the 64 x 128 wave
+// tile fits two waves per SIMD only with one set of fragments: each read of
+// the next slice goes out in the MFMA slot right after the last use of the
+// fragment it replaces.  The rest follows the bf16 kernel (ffn_bf16.hip): two
+// 64 KB stages of swizzled 128-byte rows filled by direct-to-LDS DMA,
+// persistent work-groups taking ticketed tiles with the DMA stream running on
+// across tiles, a wave's row blocks in both halves of the tile.  The
+// activation row scales travel by 4-byte DMA into a ring of four slots; the
+// weight block scales are scalar loads.
 //
 // Epilogues
 //   SWIGLU  g, u = the accumulators times their scales, h = silu(g) * u; the
-//           1 x 128 quantisation tile of h spans the four feature waves of a
-//           row, so each wave reduces its quarter of the row amax and the
-//           quarters meet in LDS; codes = e4m3(h / scale), scale = amax / 448.
+//           1 x 128 quantisation tile of h spans the two feature waves of a
+//           row, so each wave reduces its half of the row amax and the
+//           halves meet in LDS; codes = e4m3(h / scale), scale = amax / 448.
 //   STORE   bf16 output through each wave's staging slot.
 #include <algorithm>
 #include <atomic>
@@ -49,28 +52,28 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 128;          // activation rows per tile
+constexpr int BM = 256;          // activation rows per tile
 constexpr int BN = 256;          // weight rows per tile
 constexpr int BKB = 128;         // K per step: 128 e4m3 bytes = one scale block
 constexpr int NW = 8;
-constexpr int WAVES_M = 2;
+constexpr int WAVES_M = 4;
 constexpr int WAVES_N = NW / WAVES_M;
 constexpr int kThreads = NW * 64;
 constexpr int TM = BM / WAVES_M;  // 64
-constexpr int TN = BN / WAVES_N;  // 64
+constexpr int TN = BN / WAVES_N;  // 128
 constexpr int RM = TM / 32, RN = TN / 32;
-constexpr int HB = BM / RM;       // 64: row distance between a wave's blocks
+constexpr int HB = BM / RM;       // 128: row distance between a wave's blocks
 constexpr int ADMA = BM / (8 * NW);
 constexpr int BDMA = BN / (8 * NW);
 constexpr int NDMA = ADMA + BDMA;
 constexpr int DHALF = NDMA / 2;
 constexpr int NS = 2;             // K = 64 slices per step
 constexpr int SC_SLOTS = 4;       // activation-scale ring
-static_assert(RM == 2 && RN == 2, "tile layout");
+static_assert(RM == 2 && RN == 4, "tile layout");
 
-constexpr int ST_PITCH = TN * 2 + 16;  // STORE staging: 8 rows of 64 bf16
+constexpr int ST_PITCH = TN * 2 + 16;  // STORE staging: 8 rows of 128 bf16
 constexpr int ST_BYTES = 8 * ST_PITCH;
-constexpr int H_PITCH = 32 + 16;       // SWIGLU staging: 8 rows of 32 codes
+constexpr int H_PITCH = TN / 2 + 16;   // SWIGLU staging: 8 rows of 64 codes
 constexpr int H_BYTES = 8 * H_PITCH;
 
 constexpr int kSlots = 16;
@@ -127,11 +130,25 @@ __device__ __forceinline__ float uniform_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 
+// MFMA slot of a slice (row block outer, weight block inner) after which
+// fragment f of the next slice is read (f = 0: a0, 1..RN: b, RN + 1: a1),
+// with nb row blocks in use: the slot of the last use of the fragment it
+// replaces, so one set of fragment registers is live at a time.  With one
+// block, a0 goes a slot early, as b(RN-1) takes the last one.
+__host__ __device__ constexpr int read_slot(int nb, int f) {
+  return nb == RM ? (f == 0 ? RN - 1 : f <= RN ? RN + f - 1 : 2 * RN - 1)
+                  : (f == 0 ? RN - 2 : f - 1);
+}
+static_assert(read_slot(RM, 0) == 3 && read_slot(RM, 1) == 4 && read_slot(RM, RN) == 7 &&
+              read_slot(RM, RN + 1) == 7 && read_slot(1, 0) == 2 && read_slot(1, RN) == 3,
+              "read schedule");
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr bool SWI = MODE == MODE_SWIGLU;
   constexpr int NJB = SWI ? 2 : 1;  // weight scale blocks of a wave's columns (SWIGLU: gate, up)
+  constexpr int NJW = RN / NJB;     // accumulator columns per weight scale block
   constexpr int STAGE = (BM + BN) * 8;
   constexpr int STG_U4 = NW * (SWI ? H_BYTES : ST_BYTES) / 16;
   __shared__ uint4 smem[2 * STAGE];
@@ -221,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
     // of the tile's features; STORE the 128-row block of its 128 columns
     auto sb_blk = [&](const Src& x, int jb) __attribute__((always_inline)) {
       if constexpr (SWI) return jb == 0 ? x.n_tile : p.d_ff / BKB + x.n_tile;
-      return 2 * x.n_tile + wn / 2;
+      return (x.n_tile * BN + wn * TN) / 128;
     };
     auto sb_load = [&](const Src& x, int jb, int kk) __attribute__((always_inline)) {
       return x.bs[(int64_t)sb_blk(x, jb) * nkb + kk];
@@ -322,21 +339,19 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
     // MFMAs of slice h over the first NB row blocks (buffer h); rescale:
     // multiply each block by its row factors (from s_fac) just before its
     // first MFMA.  Reads of slice rs of (ra, rb) into the other buffer
-    // (rs < 0: none), DMA parts [d0, d1) of step kd (kd < 0: none).  With one
-    // block there are three reads for two MFMA slots: the first slot takes
-    // two.
+    // (rs < 0: none) at the slots read_slot gives, DMA parts [d0, d1) of
+    // step kd (kd < 0: none) spread over the slots.
     auto slice = [&](auto nbc, int h, bool rescale, const uint4* ra, const uint4* rb, int rs, int kd,
                      bool next, uint4* da, uint4* db, int d0, int d1, int dslot) __attribute__((always_inline)) {
       constexpr int NB = decltype(nbc)::value;
       constexpr int NQB = NB * RN, NRB = NB + RN;
-      constexpr int XR = NRB > NQB ? NRB - NQB : 0;
       const int nd = d1 - d0;
       float f[16];
 #pragma unroll
       for (int q = 0; q < NQB; ++q) {
         const int i = q / RN, j = q % RN;
         if (rescale) {
-          if (SWI || j == 0) get_factors(i, SWI ? j : 0, f);
+          if (j % NJW == 0) get_factors(i, j / NJW, f);
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[i][j][v] *= f[v];
         }
@@ -348,7 +363,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
         if (rs >= 0) {
 #pragma unroll
           for (int fr = 0; fr < NRB; ++fr)
-            if ((fr < XR ? 0 : fr - XR) == q) read_frag(ra, rb, h ^ 1, rs, fr);
+            if (read_slot(NB, fr) == q) read_frag(ra, rb, h ^ 1, rs, fr);
         }
         if (kd >= 0) {
 #pragma unroll
@@ -466,7 +481,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
           if (i >= nb) continue;
 #pragma unroll
           for (int j = 0; j < RN; ++j) {
-            if (SWI || j == 0) get_factors(i, SWI ? j : 0, f);
+            if (j % NJW == 0) get_factors(i, j / NJW, f);
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] *= f[v];
           }
@@ -517,12 +532,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
                 p.C_scale[((int64_t)ti.row0 + lr) * ntile_h + ti.n_tile] = sc;
             }
             wave_lds_fence();
-            // 8 rows x 32 codes: 4 bytes per lane
+            // 8 rows x 64 codes: 8 bytes per lane
             const int r = ln >> 3, c = ln & 7;
             if (rb + r < ti.rows) {
-              const uint32_t val = *reinterpret_cast<const uint32_t*>(st + r * H_PITCH + c * 4);
-              *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(p.C) + ((int64_t)ti.row0 + rb + r) * p.ldc +
-                                           col0 + c * 4) = val;
+              const uint2 val = *reinterpret_cast<const uint2*>(st + r * H_PITCH + c * 8);
+              *reinterpret_cast<uint2*>(static_cast<uint8_t*>(p.C) + ((int64_t)ti.row0 + rb + r) * p.ldc +
+                                        col0 + c * 8) = val;
             }
             wave_lds_fence();
           }
@@ -548,9 +563,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
                 put2(lr, j * 32 + (ln & 31), pack_bf16x2(acc[i][j][v], acc[i][j][v + 1]));
             }
             wave_lds_fence();
-            {
-              // 8 rows x 64 bf16: one 16-byte chunk per lane
-              const int r = ln >> 3, c = ln & 7;
+            // 8 rows x 128 bf16: two 16-byte chunks per lane
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int q = ln + 64 * hh;
+              const int r = q >> 4, c = q & 15;
               if (rb + r < ti.rows) {
                 const uint4 val = *reinterpret_cast<const uint4*>(st + r * ST_PITCH + c * 16);
                 *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.C) + ((int64_t)ti.row0 + rb + r) * p.ldc +
