@@ -29,20 +29,24 @@ HASH_SEED = 7
 
 # HBM traffic of the routed up-projection launch, per launch, from two
 # rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over
-#   python3 bench.py --steps 2 --warmup 1 --cpu-sample 0 --copy-probe
+#   python3 bench.py [--workload W] --steps 2 --warmup 1 --cpu-sample 0 --copy-probe
 # Each counter is scaled by what it reads for the copy probe (a plain 2 GiB
 # elementwise copy run in the same process): on gfx950 FETCH_SIZE reports half
-# of the bytes a full-line read moves, WRITE_SIZE reports them exactly.  The
+# of the bytes a full-line read moves, WRITE_SIZE reports them exactly.  A
 # record holds only for the kernel sources it was taken from: any change to them
 # turns the reported traffic into null until the passes are taken again.
-TRAFFIC_SOURCES = ("moe_expert_routing_sqrt_amd/csrc/ffn_bf16.hip",
-                   "moe_expert_routing_sqrt_amd/csrc/gemm_common.h",
+_SHARED_SOURCES = ("moe_expert_routing_sqrt_amd/csrc/gemm_common.h",
                    "moe_expert_routing_sqrt_amd/csrc/common.h",
                    "moe_expert_routing_sqrt_amd/build.py")
 TRAFFIC = {
-    "v3": {"sources_sha256": "b94bb83c4c5673da3526d482113d7a0c3caff54901c1a45ae3295581fb9aaf26",
+    "v3": {"sources": ("moe_expert_routing_sqrt_amd/csrc/ffn_bf16.hip",) + _SHARED_SOURCES,
+           "sources_sha256": "b94bb83c4c5673da3526d482113d7a0c3caff54901c1a45ae3295581fb9aaf26",
            "fetch_kib": 18773260.9, "fetch_scale": 1.99997,
            "write_kib": 524627.8, "write_scale": 1.0},
+    "v3_fp8": {"sources": ("moe_expert_routing_sqrt_amd/csrc/gemm_fp8p.hip",) + _SHARED_SOURCES,
+               "sources_sha256": "32ef9d352e661fd75e30b997fd2d3a2b8f1cc12c108409e414a079b20eeb8a16",
+               "fetch_kib": 10548098.2, "fetch_scale": 1.99997,
+               "write_kib": 298310.0, "write_scale": 1.0},
 }
 
 
@@ -101,9 +105,9 @@ def algorithmic(cfg):
     }
 
 
-def sources_digest() -> str:
+def sources_digest(sources) -> str:
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
+    for rel in sources:
         path = os.path.join(ROOT, rel)
         if not os.path.exists(path):
             return ""
@@ -115,7 +119,7 @@ def sources_digest() -> str:
 def traffic(cfg, up_bytes):
     """Counter-measured HBM bytes per routed up-projection launch, or None."""
     rec = TRAFFIC.get(cfg.name)
-    if rec is None or rec["sources_sha256"] != sources_digest():
+    if rec is None or rec["sources_sha256"] != sources_digest(rec["sources"]):
         return None
     fetch = rec["fetch_kib"] * 1024 * rec["fetch_scale"]
     write = rec["write_kib"] * 1024 * rec["write_scale"]
