@@ -3,6 +3,7 @@
 // allocates, frees or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 
 #include "common.h"
@@ -32,6 +33,21 @@ int check_shape(const moe_shape* s) {
 bool is_dtype(int t) { return t == MOE_F32 || t == MOE_BF16 || t == MOE_E4M3; }
 
 }  // namespace
+
+namespace moe {
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+}  // namespace moe
 
 extern "C" {
 

@@ -24,6 +24,8 @@
 //
 // WGRAD's K is the group's row count: the last step is partial, and rows past
 // the group (or past the buffer) are fetched from a zero row.
+#include <algorithm>
+
 #include "common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -44,8 +46,6 @@ constexpr int KROW_BYTES = 512;          // K-major LDS row: 256 bf16
 constexpr int DPW = 4;                   // DMA instructions per operand per wave per step
 constexpr int NDMA = 2 * DPW;
 constexpr int DHALF = NDMA / 2;
-
-enum { MODE_DGRAD = 0, MODE_WGRAD = 1 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
@@ -69,12 +69,11 @@ struct BwdArgs {
   int m_tiles, n_tiles;    // WGRAD: tiles per group (DGRAD: n_tiles only)
 };
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void ffn_bwd_kernel(const BwdArgs p) {
+__global__ __launch_bounds__(kThreads, 1) void ffn_dgrad_kernel(const BwdArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int STAGE = 2 * 32 * 1024 / 16;  // uint4: A 32 KB + B 32 KB
-  constexpr int OUT_PITCH = BN * 2 + 16;      // DGRAD bf16 staging row
-  constexpr int OUT_U4 = MODE == MODE_DGRAD ? BM * OUT_PITCH / 16 : 0;
+  constexpr int OUT_PITCH = BN * 2 + 16;      // bf16 staging row
+  constexpr int OUT_U4 = BM * OUT_PITCH / 16;
   constexpr int RING = 2 * STAGE;
   __shared__ uint4 smem[RING > OUT_U4 ? RING : OUT_U4];
   __shared__ int s_pre[kMapInts];
@@ -91,90 +90,45 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_bwd_kernel(const BwdArgs p) {
   const int wn = wave % WAVES_N;
 
   // ---- tile of this work-group
-  int group, m_tile, n_tile, row0, rows;  // rows: DGRAD valid rows of the tile / WGRAD K
-  if constexpr (MODE == MODE_DGRAD) {
-    TileInfo ti;
-    if (!map_tile(p.offsets, p.n_exp, p.rows_total, BM, p.n_tiles, s_pre, ti)) return;
-    group = ti.group;
-    m_tile = ti.m_tile;
-    n_tile = ti.n_tile;
-    row0 = ti.row0;
-    rows = ti.rows;
-  } else {
-    const int per = p.m_tiles * p.n_tiles;
-    const int total = p.n_exp * per;
-    const int rr = (total + kXcds - 1) / kXcds * kXcds;
-    const int w = blockIdx.x;
-    if (w >= rr) return;
-    const int L = (w % kXcds) * (rr / kXcds) + w / kXcds;  // XCD-contiguous slices
-    if (L >= total) return;
-    group = L / per;
-    const int rem = L % per;
-    m_tile = rem / p.n_tiles;
-    n_tile = rem % p.n_tiles;
-    row0 = p.offsets == nullptr ? 0 : p.offsets[group];
-    rows = p.offsets == nullptr ? static_cast<int>(p.rows_total) : p.offsets[group + 1] - row0;
-  }
-  group = __builtin_amdgcn_readfirstlane(group);
-  m_tile = __builtin_amdgcn_readfirstlane(m_tile);
-  n_tile = __builtin_amdgcn_readfirstlane(n_tile);
-  row0 = __builtin_amdgcn_readfirstlane(row0);
-  rows = __builtin_amdgcn_readfirstlane(rows);
-  // DGRAD: a wave whose 64 rows lie past the valid rows skips its MFMAs
-  const bool act = MODE == MODE_WGRAD || wm * TM < rows;
-  const int nsteps = MODE == MODE_DGRAD ? p.K / BK : (rows + BK - 1) / BK;
+  TileInfo ti;
+  if (!map_tile(p.offsets, p.n_exp, p.rows_total, BM, p.n_tiles, s_pre, ti)) return;
+  const int group = __builtin_amdgcn_readfirstlane(ti.group);
+  const int n_tile = __builtin_amdgcn_readfirstlane(ti.n_tile);
+  const int row0 = __builtin_amdgcn_readfirstlane(ti.row0);
+  const int rows = __builtin_amdgcn_readfirstlane(ti.rows);  // valid rows of the tile
+  // a wave whose 64 rows lie past the valid rows skips its MFMAs
+  const bool act = wm * TM < rows;
+  const int nsteps = p.K / BK;
 
-  // ---- DMA sources.  Row-major operand (DGRAD A): blocks of 8 rows x 128 B,
-  // chunk swizzle (r >> 1) & 7 applied to the global address.  K-major
-  // operand: blocks of 2 rows x 512 B; lane l fills row 2b + l/32, physical
-  // chunk l%32, logical chunk (l%32) ^ (4*(k&3)).
+  // ---- DMA sources.  Row-major A: blocks of 8 rows x 128 B, chunk swizzle
+  // (r >> 1) & 7 applied to the global address; rows past the valid ones
+  // read the last valid row.  K-major W: blocks of 2 rows x 512 B; lane l
+  // fills row 2b + l/32, physical chunk l%32, logical chunk (l%32) ^ (4*(k&3)).
   const char* a_src[DPW];
   const char* b_src[DPW];
-  int a_row[DPW];  // K-major A: K row of the lane within the step (WGRAD)
   const int kr_lane = lane >> 5;                       // row within a K-major block
   const int kr_chunk = (lane & 31) ^ (4 * ((2 * (wave & 1) + kr_lane) & 3));
 #pragma unroll
   for (int i = 0; i < DPW; ++i) {
     const int blk = wave + NW * i;
-    if constexpr (MODE == MODE_DGRAD) {
-      const int r = blk * 8 + (lane >> 3);
-      const int rc = r < rows ? r : rows - 1;
-      const int lch = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
-      a_src[i] = reinterpret_cast<const char*>(p.A + (int64_t)(row0 + rc) * p.lda + lch * 8);
-      // W rows k = 2*blk + kr_lane of the step, columns of the n tile
-      b_src[i] = reinterpret_cast<const char*>(p.B + (int64_t)group * p.b_group_stride +
-                                               (int64_t)(2 * blk + kr_lane) * p.ldb + n_tile * BN +
-                                               kr_chunk * 8);
-      a_row[i] = 0;
-    } else {
-      a_row[i] = 2 * blk + kr_lane;
-      a_src[i] = reinterpret_cast<const char*>(p.A + (int64_t)m_tile * BM + kr_chunk * 8);
-      b_src[i] = reinterpret_cast<const char*>(p.B + (int64_t)n_tile * BN + kr_chunk * 8);
-    }
+    const int r = blk * 8 + (lane >> 3);
+    const int rc = r < rows ? r : rows - 1;
+    const int lch = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+    a_src[i] = reinterpret_cast<const char*>(p.A + (int64_t)(row0 + rc) * p.lda + lch * 8);
+    // W rows k = 2*blk + kr_lane of the step, columns of the n tile
+    b_src[i] = reinterpret_cast<const char*>(p.B + (int64_t)group * p.b_group_stride +
+                                             (int64_t)(2 * blk + kr_lane) * p.ldb + n_tile * BN + kr_chunk * 8);
   }
-  const char* zrow = reinterpret_cast<const char*>(g_zero_row) + kr_chunk * 16;
 
   // DMA part q (< DPW: A, else B) of step kt into stage (sa, sb)
   auto dma_one = [&](int kt, char* sa, char* sb, int q) __attribute__((always_inline)) {
     const int i = q < DPW ? q : q - DPW;
     const int blk = wave + NW * i;
-    if constexpr (MODE == MODE_DGRAD) {
-      if (q < DPW) {
-        if (kt < 2 || blk * 8 < rows)
-          dma16(a_src[i] + (int64_t)kt * BK * 2, lds_addr(sa) + blk * 1024);
-      } else {
-        dma16(b_src[i] + (int64_t)kt * BK * p.ldb * 2, lds_addr(sb) + blk * 1024);
-      }
+    if (q < DPW) {
+      if (kt < 2 || blk * 8 < rows)
+        dma16(a_src[i] + (int64_t)kt * BK * 2, lds_addr(sa) + blk * 1024);
     } else {
-      const int k = kt * BK + a_row[i];  // row within the group
-      const bool in = k < rows;
-      if (q < DPW) {
-        const char* g = in ? a_src[i] + (int64_t)(row0 + k) * p.lda * 2 : zrow;
-        dma16(g, lds_addr(sa) + blk * 1024);
-      } else {
-        const char* g = in ? b_src[i] + (int64_t)(row0 + k) * p.ldb * 2 : zrow;
-        dma16(g, lds_addr(sb) + blk * 1024);
-      }
+      dma16(b_src[i] + (int64_t)kt * BK * p.ldb * 2, lds_addr(sb) + blk * 1024);
     }
   };
 
@@ -208,12 +162,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_bwd_kernel(const BwdArgs p) {
     const bool is_a = f == 0 || f > RN;
     const int idx = f == 0 ? 0 : (f <= RN ? f - 1 : f - RN);
     if (is_a) {
-      if constexpr (MODE == MODE_DGRAD) {
-        const uint4* s = reinterpret_cast<const uint4*>(sa);
-        fa[buf][idx] = as_bf16x8(s[swz(wm * TM + idx * 32 + (lane & 31), 2 * s16 + (lane >> 5))]);
-      } else {
-        fa[buf][idx] = kmajor_frag(sa, wm * TM + idx * 32, s16);
-      }
+      const uint4* s = reinterpret_cast<const uint4*>(sa);
+      fa[buf][idx] = as_bf16x8(s[swz(wm * TM + idx * 32 + (lane & 31), 2 * s16 + (lane >> 5))]);
     } else {
       fb[buf][idx] = kmajor_frag(sb, wn * TN + idx * 32, s16);
     }
@@ -293,49 +243,248 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_bwd_kernel(const BwdArgs p) {
 
   // ---- epilogue.  Accumulator (i, j) register v holds row 8*(v/4) +
   // 4*(lane/32) + v%4 and column lane%32 of its 32x32 block.
-  if constexpr (MODE == MODE_DGRAD) {
-    barrier_only();
-    if (act) {
-#pragma unroll
-      for (int i = 0; i < RM; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int lr = wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          uint16_t* row = reinterpret_cast<uint16_t*>(base + lr * OUT_PITCH);
-#pragma unroll
-          for (int j = 0; j < RN; ++j) row[wn * TN + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][v]);
-        }
-    }
-    __syncthreads();
-    constexpr int OCH = BN * 2 / 16;
-    uint16_t* C = static_cast<uint16_t*>(p.C);
-    for (int q = tid; q < rows * OCH; q += kThreads) {
-      const int r = q / OCH, c = q % OCH;
-      const uint4 v = *reinterpret_cast<const uint4*>(base + r * OUT_PITCH + c * 16);
-      *reinterpret_cast<uint4*>(C + (int64_t)(row0 + r) * p.ldc + (int64_t)n_tile * BN + c * 8) = v;
-    }
-  } else {
-    // fp32 weight gradient: for a fixed register, the 32 lanes of a half-wave
-    // write 128 contiguous bytes of one row, so direct stores stay coalesced
-    float* C = static_cast<float*>(p.C) + (int64_t)group * p.c_group_stride;
+  barrier_only();
+  if (act) {
 #pragma unroll
     for (int i = 0; i < RM; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = m_tile * BM + wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int lr = wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        uint16_t* row = reinterpret_cast<uint16_t*>(base + lr * OUT_PITCH);
 #pragma unroll
-        for (int j = 0; j < RN; ++j)
-          C[(int64_t)m * p.ldc + n_tile * BN + wn * TN + j * 32 + (lane & 31)] = acc[i][j][v];
+        for (int j = 0; j < RN; ++j) row[wn * TN + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][v]);
       }
+  }
+  __syncthreads();
+  constexpr int OCH = BN * 2 / 16;
+  uint16_t* C = static_cast<uint16_t*>(p.C);
+  for (int q = tid; q < rows * OCH; q += kThreads) {
+    const int r = q / OCH, c = q % OCH;
+    const uint4 v = *reinterpret_cast<const uint4*>(base + r * OUT_PITCH + c * 16);
+    *reinterpret_cast<uint4*>(C + (int64_t)(row0 + r) * p.ldc + (int64_t)n_tile * BN + c * 8) = v;
   }
 #endif
 }
 
-template <int MODE>
-hipError_t launch(const BwdArgs& a, int64_t tiles, hipStream_t s) {
+// WGRAD, persistent: one work-group per CU walks a static list of tiles
+// (those of its XCD's contiguous range, every (grid / 8)-th), and its K steps
+// form one stream across tiles: the DMA two steps ahead and the fragment reads
+// one slice ahead run on into the next tile, so a tile (an expert's ~8 steps
+// on V3) starts without a pipeline fill.  Between tiles the accumulators are
+// stored straight from registers and cleared.  A tile of an expert with no
+// rows runs one step over the zero row and stores zeros.  Past the end of
+// the stream the DMA and fragment reads keep going, on the zero row and on
+// stale LDS, so no MFMA slot holds a branch.
+struct WgradCursor {
+  const char* a;  // A bytes of the step's first K row, the tile's columns
+  const char* b;  // the same for B
+  int valid, group, m_tile, n_tile, rows, ns, s, lim;  // lim: valid K rows from the step's first
+};
+
+__global__ __launch_bounds__(kThreads, 1) void ffn_wgrad_kernel(const BwdArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // stages as [A0 | A1 | B0 | B1] (32 KB each): every fragment read is a
+  // per-lane base plus an immediate offset below 64 KB
+  __shared__ uint4 smem[4 * 32 * 1024 / 16];
+  char* const base = reinterpret_cast<char*>(smem);
+  char* const sA0 = base;
+  char* const sA1 = base + 32 * 1024;
+  char* const sB0 = base + 64 * 1024;
+  char* const sB1 = base + 96 * 1024;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+
+  // this work-group's tiles: L = begin + j + i * gpx within [begin, end)
+  const int per = p.m_tiles * p.n_tiles;
+  const int total = p.n_exp * per;
+  const int gpx = static_cast<int>(gridDim.x) / kXcds;
+  const int xcd = blockIdx.x % kXcds, j0 = blockIdx.x / kXcds;
+  const int per_x = (total + kXcds - 1) / kXcds;
+  const int l_end = min(total, (xcd + 1) * per_x);
+  int l_next = xcd * per_x + j0;  // next tile of the list to open
+  const int64_t a_step = (int64_t)BK * p.lda * 2, b_step = (int64_t)BK * p.ldb * 2;
+  auto open_tile = [&](WgradCursor& c) __attribute__((always_inline)) {
+    const int L = l_next;
+    l_next += gpx;
+    c.valid = L < l_end;
+    if (!c.valid) {
+      c.lim = 0;
+      return;
+    }
+    c.group = L / per;
+    const int rem = L % per;
+    c.m_tile = rem / p.n_tiles;
+    c.n_tile = rem % p.n_tiles;
+    const int row0 = p.offsets == nullptr ? 0 : __builtin_amdgcn_readfirstlane(p.offsets[c.group]);
+    c.rows = p.offsets == nullptr ? static_cast<int>(p.rows_total)
+                                  : __builtin_amdgcn_readfirstlane(p.offsets[c.group + 1]) - row0;
+    c.ns = max(1, (c.rows + BK - 1) / BK);
+    c.s = 0;
+    c.lim = c.rows;
+    c.a = reinterpret_cast<const char*>(p.A + (int64_t)row0 * p.lda + (int64_t)c.m_tile * BM);
+    c.b = reinterpret_cast<const char*>(p.B + (int64_t)row0 * p.ldb + (int64_t)c.n_tile * BN);
+  };
+  auto advance = [&](WgradCursor& c) __attribute__((always_inline)) {
+    if (!c.valid) return;
+    if (++c.s == c.ns) {
+      open_tile(c);
+    } else {
+      c.lim -= BK;
+      c.a += a_step;
+      c.b += b_step;
+    }
+  };
+
+  // DMA: K-major operand blocks of 2 rows x 512 B; lane l fills K row
+  // 2 * blk + l / 32 of the step, physical chunk l % 32, logical chunk
+  // (l % 32) ^ (4 * (k & 3)).  Rows past the group read the zero row.
+  int k_row[DPW];
+  uint32_t a_off[DPW], b_off[DPW];
+  const int kr_lane = lane >> 5;
+  const int kr_chunk = (lane & 31) ^ (4 * ((2 * (wave & 1) + kr_lane) & 3));
+#pragma unroll
+  for (int i = 0; i < DPW; ++i) {
+    k_row[i] = 2 * (wave + NW * i) + kr_lane;
+    a_off[i] = static_cast<uint32_t>(k_row[i] * p.lda * 2 + kr_chunk * 16);
+    b_off[i] = static_cast<uint32_t>(k_row[i] * p.ldb * 2 + kr_chunk * 16);
+  }
+  const char* zrow = reinterpret_cast<const char*>(g_zero_row) + kr_chunk * 16;
+  auto dma_one = [&](const WgradCursor& c, char* sa, char* sb, int q) __attribute__((always_inline)) {
+    const int i = q < DPW ? q : q - DPW;
+    const int blk = wave + NW * i;
+    const bool in = k_row[i] < c.lim;
+    if (q < DPW) dma16(in ? c.a + a_off[i] : zrow, lds_addr(sa) + blk * 1024);
+    else dma16(in ? c.b + b_off[i] : zrow, lds_addr(sb) + blk * 1024);
+  };
+
+  f32x16 acc[RM][RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i)
+#pragma unroll
+    for (int j = 0; j < RN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // fragment of 32 columns from col0 for K16 slice s16 of a K-major stage:
+  // lane reads (transposing) 4 columns of K row k0 = 16 s16 + 8 (lane / 32)
+  // + r, r = (lane % 16) / 4, and of row k0 + 4; the chunk XOR 4 (k & 3) is
+  // 4 r for both, so a fragment is a per-lane offset plus immediates
+  const int tr_a = lane & 15;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (tr_a & 3);
+  const int tr_row = tr_a >> 2;
+  auto frag_off = [&](int col0) __attribute__((always_inline)) {
+    const int n = col0 + tr_col;
+    const int k0 = 8 * (lane >> 5) + tr_row;
+    return k0 * KROW_BYTES + (((n >> 3) ^ (4 * tr_row)) << 4) + (n & 7) * 2;
+  };
+  int fo_a[RM], fo_b[RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i) fo_a[i] = frag_off(wm * TM + i * 32);
+#pragma unroll
+  for (int j = 0; j < RN; ++j) fo_b[j] = frag_off(wn * TN + j * 32);
+  auto kmajor_frag = [&](const char* st, int off, int s16) __attribute__((always_inline)) {
+    const char* q = st + off + s16 * 16 * KROW_BYTES;
+    const v4i16 lo = lds_tr16(q);
+    const v4i16 hi = lds_tr16(q + 4 * KROW_BYTES);
+    const v4i16 v[2] = {lo, hi};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+  bf16x8 fa[2][RM], fb[2][RN];
+  auto read_frag = [&](const char* sa, const char* sb, int buf, int s16, int f) __attribute__((always_inline)) {
+    // order of first use: a0, b0 .. b(RN-1), a1 .. a(RM-1)
+    const bool is_a = f == 0 || f > RN;
+    const int idx = f == 0 ? 0 : (f <= RN ? f - 1 : f - RN);
+    if (is_a) fa[buf][idx] = kmajor_frag(sa, fo_a[idx], s16);
+    else fb[buf][idx] = kmajor_frag(sb, fo_b[idx], s16);
+  };
+  constexpr int NR = RM + RN;
+  // MFMAs of slice s (buffer s & 1); reads of slice rs of (rsa, rsb) into the
+  // other buffer; DMA parts [d0, d1) of cursor dc (dc == nullptr: none)
+  auto slice = [&](int s, const char* rsa, const char* rsb, int rs, const WgradCursor* dc, char* da, char* db,
+                   int d0, int d1) __attribute__((always_inline)) {
+    const int buf = s & 1;
+    const int nd = d1 - d0;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int i = q / RN, j = q % RN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+      asm volatile("" : "+v"(acc[i][j]));  // keeps the MFMA in its slot
+      if (q < NR) read_frag(rsa, rsb, buf ^ 1, rs, q);
+      if (dc != nullptr) {
+#pragma unroll
+        for (int t = 0; t < NDMA; ++t)
+          if (t < nd && (t * NQ) / nd == q) dma_one(*dc, da, db, d0 + t);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // fp32 tile store (nontemporal: nothing here reads it again), then clear
+  auto epilogue = [&](const WgradCursor& c) __attribute__((always_inline)) {
+    float* C = static_cast<float*>(p.C) + (int64_t)c.group * p.c_group_stride;
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = c.m_tile * BM + wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+#pragma unroll
+        for (int j = 0; j < RN; ++j) {
+          __builtin_nontemporal_store(acc[i][j][v],
+                                      &C[(int64_t)m * p.ldc + c.n_tile * BN + wn * TN + j * 32 + (lane & 31)]);
+          acc[i][j][v] = 0.0f;
+        }
+      }
+  };
+
+  // cur: the step being multiplied; c1, c2: the next two steps of the stream
+  WgradCursor cur, c1, c2;
+  open_tile(cur);
+  if (cur.valid) {
+    c1 = cur;
+    advance(c1);
+    c2 = c1;
+    advance(c2);
+#pragma unroll
+    for (int q = 0; q < NDMA; ++q) dma_one(cur, sA0, sB0, q);
+#pragma unroll
+    for (int q = 0; q < NDMA; ++q) dma_one(c1, sA1, sB1, q);
+    wait_vmcnt<NDMA>();
+    barrier_only();
+#pragma unroll
+    for (int f = 0; f < NR; ++f) read_frag(sA0, sB0, 0, 0, f);
+    // one step of the stream from stage (sa, sb), next stage (na, nb); first:
+    // the stream's first step (its successor's DMA went out whole)
+    auto step = [&](bool first, char* sa, char* sb, char* na, char* nb) __attribute__((always_inline)) {
+      slice(0, sa, sb, 1, first ? nullptr : &c1, na, nb, DHALF, NDMA);
+#pragma unroll
+      for (int s = 1; s + 1 < NS; ++s) slice(s, sa, sb, s + 1, nullptr, nullptr, nullptr, 0, 0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      wait_vmcnt<0>();
+      barrier_only();
+      slice(NS - 1, na, nb, 0, &c2, sa, sb, 0, DHALF);
+      if (cur.s == cur.ns - 1) epilogue(cur);
+      cur = c1;
+      c1 = c2;
+      advance(c2);
+    };
+    step(true, sA0, sB0, sA1, sB1);
+    while (cur.valid) {
+      step(false, sA1, sB1, sA0, sB0);
+      if (!cur.valid) break;
+      step(false, sA0, sB0, sA1, sB1);
+    }
+    wait_vmcnt<0>();  // the zero-row DMA issued past the stream's end
+  }
+#endif
+}
+
+hipError_t launch_dgrad(const BwdArgs& a, int64_t tiles, hipStream_t s) {
   const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((ffn_bwd_kernel<MODE>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(ffn_dgrad_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -360,7 +509,7 @@ hipError_t launch_ffn_dgrad_bf16(int n_exp, const int32_t* offsets, int64_t max_
   a.K = K;
   a.n_tiles = N / BN;
   const int64_t mt = max_row_tiles(max_rows, offsets == nullptr ? 1 : n_exp, BM);
-  return launch<MODE_DGRAD>(a, mt * a.n_tiles, s);
+  return launch_dgrad(a, mt * a.n_tiles, s);
 }
 
 // C_g [M, N] fp32 = sum over the group's rows r of A[r][m] * B[r][n]
@@ -379,7 +528,13 @@ hipError_t launch_ffn_wgrad_bf16(int n_exp, const int32_t* offsets, int64_t rows
   a.rows_total = rows_total;
   a.m_tiles = M / BM;
   a.n_tiles = N / BN;
-  return launch<MODE_WGRAD>(a, (int64_t)a.n_exp * a.m_tiles * a.n_tiles, s);
+  const int64_t tiles = (int64_t)a.n_exp * a.m_tiles * a.n_tiles;
+  if (tiles <= 0) return hipSuccess;
+  // tile numbers and the 32-bit per-lane DMA offsets (64 K rows of A and B)
+  if (tiles >= (1LL << 31) || (int64_t)BK * std::max(M, N) * 2 >= (1LL << 31)) return hipErrorInvalidValue;
+  const int64_t grid = (std::min<int64_t>(tiles, device_cu_count()) + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL(ffn_wgrad_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -7,6 +7,9 @@
 
 namespace moe {
 
+// compute units of the current device (cached per device; 256 if the query fails)
+int device_cu_count();
+
 // gate logits
 hipError_t launch_gate_gemm_bf16(const uint16_t* x, const uint16_t* w_prep, float* logits,
                                  int64_t T, int d, int E, hipStream_t s);
