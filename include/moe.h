@@ -314,7 +314,12 @@ int moe_dispatch_backward(const moe_shape* shape, const int32_t* dest, const voi
  * x [T, d] in x_dtype; w_gate [d, E] fp32; logits [T, E] as moe_route wrote
  * them (without the offset); logit_offset [E] or NULL.  dw_gate sums over the
  * T tokens in up to 16 K-parts held in ws (moe_route_backward_workspace_size
- * bytes; MOE_ERR_WORKSPACE if smaller), added in part order (deterministic).
+ * bytes, enough for either path below; MOE_ERR_WORKSPACE if smaller), added
+ * in part order (deterministic).  With bf16 x, d % 256 == 0 and E % 64 == 0
+ * both products run on the matrix cores: each fp32 operand is split into
+ * three bf16 planes (hi + mid + lo, 24 significant bits) and the plane
+ * products above 2^-24 of a product are summed in fp32 (six for dx, three
+ * for dw_gate, x being exact in bf16); otherwise fp32 vector products.
  */
 size_t moe_route_backward_workspace_size(const moe_shape* shape);
 int moe_route_backward(const moe_shape* shape, const void* x, int x_dtype, const float* w_gate,

@@ -263,6 +263,80 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float* parts, int 
   }
 }
 
+// ---------------------------------------------------------------- matrix-core gate products
+// fp32 operands as three bf16 planes, a = hi + mid + lo, each plane the bf16
+// rounding of what the planes before it leave (24 significant bits in all).
+__device__ __forceinline__ void planes3(float v, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  hi = f32_to_bf16(v);
+  const float r1 = v - bf16_to_f32(hi);
+  mid = f32_to_bf16(r1);
+  lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+}
+
+// dL [T, E] -> a6 [T, 6E] = [hi | hi | mid | hi | lo | mid] and p3 [T, ld3] =
+// [hi | mid | lo | zero padding]; one thread per (row, column < E + ld3 - 3E)
+__global__ __launch_bounds__(256) void dl_planes_kernel(const float* __restrict__ dl, int64_t T, int E, int ld3,
+                                                        uint16_t* __restrict__ a6, uint16_t* __restrict__ p3) {
+  const int cols = E + (ld3 - 3 * E);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * cols) return;
+  const int64_t t = i / cols;
+  const int c = static_cast<int>(i % cols);
+  if (c >= E) {
+    p3[t * ld3 + 3 * E + (c - E)] = 0;
+    return;
+  }
+  uint16_t hi, mid, lo;
+  planes3(dl[t * E + c], hi, mid, lo);
+  uint16_t* a = a6 + t * 6 * E + c;
+  a[0] = hi;
+  a[E] = hi;
+  a[2 * E] = mid;
+  a[3 * E] = hi;
+  a[4 * E] = lo;
+  a[5 * E] = mid;
+  uint16_t* q = p3 + t * ld3 + c;
+  q[0] = hi;
+  q[E] = mid;
+  q[2 * E] = lo;
+}
+
+// W_g [d, E] -> w6 [d, 6E] = [hi | mid | hi | lo | hi | mid], matching a6
+// block by block: hi.hi, hi.mid, mid.hi, hi.lo, lo.hi, mid.mid (the plane
+// products above 2^-24 of the product)
+__global__ __launch_bounds__(256) void w_planes_kernel(const float* __restrict__ w, int d, int E,
+                                                       uint16_t* __restrict__ w6) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)d * E) return;
+  const int64_t c = i / E;
+  const int e = static_cast<int>(i % E);
+  uint16_t hi, mid, lo;
+  planes3(w[i], hi, mid, lo);
+  uint16_t* o = w6 + c * 6 * E + e;
+  o[0] = hi;
+  o[E] = mid;
+  o[2 * E] = hi;
+  o[3 * E] = lo;
+  o[4 * E] = hi;
+  o[5 * E] = mid;
+}
+
+// dW_g[c][e] = sum over row splits z (in order) of ((hi + mid) + lo) partials
+__global__ __launch_bounds__(256) void plane_sum_kernel(const float* __restrict__ part, int splits, int d, int E,
+                                                        int ld3, float* __restrict__ dw) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)d * E) return;
+  const int64_t c = i / E;
+  const int e = static_cast<int>(i % E);
+  const int64_t zs = (int64_t)d * ld3;
+  float v = 0.0f;
+  for (int z = 0; z < splits; ++z) {
+    const float* q = part + z * zs + c * ld3 + e;
+    v += (q[0] + q[E]) + q[2 * E];
+  }
+  dw[i] = v;
+}
+
 hipError_t launch_f32(const F32Args& a, int a_dtype, hipStream_t s, int splits = 1) {
   const dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, splits);
   if (a_dtype == MOE_BF16) hipLaunchKernelGGL(gemm_f32_kernel<uint16_t>, grid, dim3(256), 0, s, a);
@@ -302,9 +376,39 @@ int gate_bwd_splits(int64_t T) {
   return s < 1 ? 1 : (s > 16 ? 16 : s);
 }
 
+namespace {
+
+// matrix-core path: bf16 x, d a multiple of 256, E a multiple of 64
+bool gate_bwd_mfma(int d, int E, int x_dtype) { return x_dtype == MOE_BF16 && d % 256 == 0 && E % 64 == 0; }
+
+struct GateMfmaWs {
+  int ld3, splits, split_rows;
+  size_t a6, w6, p3, part, total;  // byte offsets into the workspace
+};
+
+GateMfmaWs gate_mfma_ws(int64_t T, int d, int E) {
+  GateMfmaWs w{};
+  w.ld3 = (3 * E + 255) / 256 * 256;
+  int64_t sp = T / 2048;
+  w.splits = static_cast<int>(sp < 1 ? 1 : (sp > 16 ? 16 : sp));
+  w.split_rows = static_cast<int>(((T + w.splits - 1) / w.splits + 63) / 64 * 64);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  w.a6 = 0;
+  w.w6 = up(w.a6 + (size_t)T * 6 * E * 2);
+  w.p3 = up(w.w6 + (size_t)d * 6 * E * 2);
+  w.part = up(w.p3 + (size_t)T * w.ld3 * 2);
+  w.total = w.part + (size_t)w.splits * d * w.ld3 * 4;
+  return w;
+}
+
+}  // namespace
+
 size_t gate_bwd_workspace_bytes(int64_t T, int d, int E) {
   const int s = gate_bwd_splits(T);
-  return s > 1 ? (size_t)s * d * E * sizeof(float) : 0;
+  const size_t simt = s > 1 ? (size_t)s * d * E * sizeof(float) : 0;
+  // the larger of the two paths' needs: the path depends on x's dtype
+  const size_t mfma = d % 256 == 0 && E % 64 == 0 ? gate_mfma_ws(T, d, E).total : 0;
+  return simt > mfma ? simt : mfma;
 }
 
 hipError_t launch_gate_bwd(int64_t T, int d, int E, int k, const void* x, int x_dtype, const float* w_gate,
@@ -314,6 +418,30 @@ hipError_t launch_gate_bwd(int64_t T, int d, int E, int k, const void* x, int x_
                      logits, offset, idx, d_w, dL);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (gate_bwd_mfma(d, E, x_dtype)) {
+    const GateMfmaWs w = gate_mfma_ws(T, d, E);
+    char* base = reinterpret_cast<char*>(ws);
+    uint16_t* a6 = reinterpret_cast<uint16_t*>(base + w.a6);
+    uint16_t* w6 = reinterpret_cast<uint16_t*>(base + w.w6);
+    uint16_t* p3 = reinterpret_cast<uint16_t*>(base + w.p3);
+    float* part = reinterpret_cast<float*>(base + w.part);
+    const int64_t n1 = T * (E + (w.ld3 - 3 * E));
+    hipLaunchKernelGGL(dl_planes_kernel, dim3(static_cast<unsigned>((n1 + 255) / 256)), dim3(256), 0, s, dL, T, E,
+                       w.ld3, a6, p3);
+    const int64_t n2 = (int64_t)d * E;
+    hipLaunchKernelGGL(w_planes_kernel, dim3(static_cast<unsigned>((n2 + 255) / 256)), dim3(256), 0, s, w_gate, d,
+                       E, w6);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // dx[t][c] += sum over K' = 6E of a6[t][k'] w6[c][k']
+    if ((e = launch_gemm_acc_f32(T, 6 * E, d, a6, w6, dx, s)) != hipSuccess) return e;
+    // partials[z][c][k] = sum over split z's rows t of x[t][c] p3[t][k]
+    if ((e = launch_ffn_wgrad_bf16(0, nullptr, T, d, w.ld3, static_cast<const uint16_t*>(x), p3, part, s,
+                                   w.split_rows)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(plane_sum_kernel, dim3(static_cast<unsigned>((n2 + 255) / 256)), dim3(256), 0, s, part,
+                       static_cast<int>((T + w.split_rows - 1) / w.split_rows), d, E, w.ld3, dw_gate);
+    return hipGetLastError();
+  }
   // dx[t][c] += sum_e dL[t][e] W_g[c][e]
   F32Args a{dL, E, 1, w_gate, E, 1, dx, d, static_cast<int>(T), d, E, 1, 0, E};
   if ((e = launch_f32(a, MOE_F32, s)) != hipSuccess) return e;

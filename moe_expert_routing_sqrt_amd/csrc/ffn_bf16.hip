@@ -96,7 +96,8 @@ constexpr int kCtrStride = 16;
 constexpr int kSlotInts = (kXcds + 1) * kCtrStride;
 __device__ int g_tickets[kSlots * kSlotInts];
 
-enum { MODE_SWIGLU = 0, MODE_STORE = 1, MODE_SWIGLU_SAVE = 2 };  // SAVE: also [a | u]
+// SAVE: also [a | u]; ACC_F32: C (fp32) += A B^T, one group
+enum { MODE_SWIGLU = 0, MODE_STORE = 1, MODE_SWIGLU_SAVE = 2, MODE_ACC_F32 = 3 };
 
 struct FfnArgs {
   const uint16_t* A;       // packed rows [rows, K]
@@ -112,6 +113,7 @@ struct FfnArgs {
   int n_tiles;             // column tiles per group
   int d_ff;                // SWIGLU: first up-projection row of w13
   uint16_t* C2;            // SWIGLU_SAVE: [a | u] output [rows, 2*d_ff]
+  float* Cf;               // ACC_F32: fp32 output [rows, ldc], accumulated into
   int slot;                // ticket counter set of this launch
 };
 
@@ -133,7 +135,7 @@ __device__ __forceinline__ void wave_lds_fence() {
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-  constexpr bool SWI = MODE != MODE_STORE;
+  constexpr bool SWI = MODE == MODE_SWIGLU || MODE == MODE_SWIGLU_SAVE;
   constexpr int STAGE = (BM + BN) * 8;   // uint4 per stage
   __shared__ uint4 smem[2 * STAGE];
   __shared__ uint4 s_stage[NW * ST_BYTES / 16];
@@ -408,6 +410,23 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
       constexpr int OUT_COLS = SWI ? BN / 2 : BN;
       const int64_t col0 = (int64_t)ti.n_tile * OUT_COLS;
       const int lr0 = 4 * (lane >> 5);
+      if constexpr (MODE == MODE_ACC_F32) {
+        // fp32 read-modify-write straight from the registers: for a fixed
+        // register the 32 lanes of a half-wave cover 128 contiguous bytes
+#pragma unroll
+        for (int i = 0; i < RM; ++i) {
+          if (i >= nb) continue;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = i * HB + 32 * wm + 8 * (v >> 2) + lr0 + (v & 3);
+            if (r >= ti.rows) continue;
+            float* row = p.Cf + ((int64_t)ti.row0 + r) * p.ldc + col0 + wn * TN + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < RN; ++j) row[j * 32] += acc[i][j][v];
+          }
+        }
+        return;
+      }
 #pragma unroll
       for (int i = 0; i < RM; ++i) {
         if (i >= nb) continue;
@@ -566,7 +585,8 @@ template <int MODE>
 hipError_t launch(FfnArgs& a, int64_t max_rows, hipStream_t s) {
   if (a.K % (2 * BK) != 0 || a.K < 4 * BK) return hipErrorInvalidValue;
   // 32-bit per-lane DMA offsets: a tile's rows and a group's weights
-  const int64_t b_rows = MODE == MODE_STORE ? (int64_t)a.n_tiles * BN : 2 * (int64_t)a.d_ff;
+  constexpr bool swi = MODE == MODE_SWIGLU || MODE == MODE_SWIGLU_SAVE;
+  const int64_t b_rows = swi ? 2 * (int64_t)a.d_ff : (int64_t)a.n_tiles * BN;
   if ((int64_t)BM * a.lda * 2 >= (1LL << 31) || b_rows * a.K * 2 >= (1LL << 31)) return hipErrorInvalidValue;
   const int64_t mt = max_row_tiles(max_rows, a.offsets == nullptr ? 1 : a.n_exp, BM);
   const int64_t tiles = mt * a.n_tiles;
@@ -616,6 +636,22 @@ hipError_t launch_ffn_store_bf16(int n_exp, const int32_t* offsets, int64_t max_
   a.K = K;
   a.n_tiles = N / BN;
   return launch<MODE_STORE>(a, max_rows, s);
+}
+
+hipError_t launch_gemm_acc_f32(int64_t rows, int K, int N, const uint16_t* A, const uint16_t* B, float* C,
+                               hipStream_t s) {
+  FfnArgs a{};
+  a.A = A;
+  a.lda = K;
+  a.B = B;
+  a.Cf = C;
+  a.ldc = N;
+  a.offsets = nullptr;
+  a.n_exp = 1;
+  a.rows_total = rows;
+  a.K = K;
+  a.n_tiles = N / BN;
+  return launch<MODE_ACC_F32>(a, rows, s);
 }
 
 hipError_t launch_ffn_down_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,

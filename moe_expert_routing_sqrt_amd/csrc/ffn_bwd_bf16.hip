@@ -62,9 +62,10 @@ struct BwdArgs {
   void* C;
   int64_t ldc;
   int64_t c_group_stride;  // WGRAD: elements between groups' outputs
-  const int* offsets;
-  int n_exp;
+  const int* offsets;      // [n_exp + 1] on the device, or nullptr: WGRAD groups of
+  int n_exp;               // split_rows consecutive rows (the last one shorter)
   int64_t rows_total;
+  int split_rows;
   int K;                   // DGRAD: reduction length
   int m_tiles, n_tiles;    // WGRAD: tiles per group (DGRAD: n_tiles only)
 };
@@ -319,9 +320,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_wgrad_kernel(const BwdArgs p)
     const int rem = L % per;
     c.m_tile = rem / p.n_tiles;
     c.n_tile = rem % p.n_tiles;
-    const int row0 = p.offsets == nullptr ? 0 : __builtin_amdgcn_readfirstlane(p.offsets[c.group]);
-    c.rows = p.offsets == nullptr ? static_cast<int>(p.rows_total)
-                                  : __builtin_amdgcn_readfirstlane(p.offsets[c.group + 1]) - row0;
+    int row0;
+    if (p.offsets == nullptr) {
+      row0 = c.group * p.split_rows;
+      c.rows = static_cast<int>(min((int64_t)p.split_rows, p.rows_total - row0));
+    } else {
+      row0 = __builtin_amdgcn_readfirstlane(p.offsets[c.group]);
+      c.rows = __builtin_amdgcn_readfirstlane(p.offsets[c.group + 1]) - row0;
+    }
     c.ns = max(1, (c.rows + BK - 1) / BK);
     c.s = 0;
     c.lim = c.rows;
@@ -514,7 +520,14 @@ hipError_t launch_ffn_dgrad_bf16(int n_exp, const int32_t* offsets, int64_t max_
 
 // C_g [M, N] fp32 = sum over the group's rows r of A[r][m] * B[r][n]
 hipError_t launch_ffn_wgrad_bf16(int n_exp, const int32_t* offsets, int64_t rows_total, int M, int N,
-                                 const uint16_t* A, const uint16_t* B, float* C, hipStream_t s) {
+                                 const uint16_t* A, const uint16_t* B, float* C, hipStream_t s, int split_rows) {
+  if (offsets == nullptr) {
+    // groups of split_rows consecutive rows (all rows when split_rows <= 0)
+    const int64_t sr = split_rows > 0 && split_rows < rows_total ? split_rows : std::max<int64_t>(rows_total, 1);
+    if (sr >= (1LL << 31)) return hipErrorInvalidValue;
+    split_rows = static_cast<int>(sr);
+    n_exp = static_cast<int>(std::max<int64_t>((rows_total + sr - 1) / sr, 1));
+  }
   BwdArgs a{};
   a.A = A;
   a.lda = M;
@@ -524,8 +537,9 @@ hipError_t launch_ffn_wgrad_bf16(int n_exp, const int32_t* offsets, int64_t rows
   a.ldc = N;
   a.c_group_stride = (int64_t)M * N;
   a.offsets = offsets;
-  a.n_exp = offsets == nullptr ? 1 : n_exp;
+  a.n_exp = n_exp;
   a.rows_total = rows_total;
+  a.split_rows = split_rows;
   a.m_tiles = M / BM;
   a.n_tiles = N / BN;
   const int64_t tiles = (int64_t)a.n_exp * a.m_tiles * a.n_tiles;

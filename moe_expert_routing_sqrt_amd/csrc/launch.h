@@ -44,8 +44,13 @@ hipError_t launch_ffn_store_bf16(int n_exp, const int32_t* offsets, int64_t max_
 bool ffn_bwd_bf16_supported(int d, int d_ff);
 hipError_t launch_ffn_dgrad_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int K, int N,
                                  const uint16_t* A, const uint16_t* W, uint16_t* C, hipStream_t s);
+// (offsets == nullptr: groups of split_rows consecutive rows, one group when split_rows <= 0)
 hipError_t launch_ffn_wgrad_bf16(int n_exp, const int32_t* offsets, int64_t rows_total, int M, int N,
-                                 const uint16_t* A, const uint16_t* B, float* C, hipStream_t s);
+                                 const uint16_t* A, const uint16_t* B, float* C, hipStream_t s,
+                                 int split_rows = 0);
+// C [rows, N] fp32 += A [rows, K] B [N, K]^T, bf16 operands (K % 128 == 0, K >= 256, N % 256 == 0)
+hipError_t launch_gemm_acc_f32(int64_t rows, int K, int N, const uint16_t* A, const uint16_t* B, float* C,
+                               hipStream_t s);
 hipError_t launch_ffn_simt(int stage, int n_exp, const int32_t* offsets, int64_t max_rows, int d,
                            int d_ff, int dtype, const void* in, const void* w, void* out,
                            hipStream_t s);

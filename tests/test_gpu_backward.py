@@ -122,13 +122,19 @@ def test_dispatch_backward():
     assert np.abs(host(dx) - (host(base) + OB.dispatch_backward(host(dxp), dest, T))).max() <= 1e-6 * np.abs(ref).max()
 
 
-@pytest.mark.parametrize("with_offset,T", [(False, 300), (True, 300), (False, 4100)])
-def test_route_backward(with_offset, T):
-    """T = 4100 sums dW_g over four K parts of the workspace (ragged last part)."""
+@pytest.mark.parametrize("with_offset,T,x_f32", [(False, 300, False), (True, 300, False), (False, 4100, False),
+                                                 (False, 4100, True), (True, 300, True)])
+def test_route_backward(with_offset, T, x_f32):
+    """bf16 x: the matrix-core products over three bf16 planes per fp32
+    operand (T = 4100: two row splits of dW_g, the second ragged); fp32 x: the
+    vector products (T = 4100: four K parts of the workspace)."""
     dev = need_gpu()
+    print(f"route backward offset={with_offset} T={T} x_f32={x_f32}", flush=True)
     rng = np.random.default_rng(5 + with_offset + T)
     E, k, d = 64, 6, 512
     x = _bf16(rng.normal(size=(T, d)), dev)
+    if x_f32:
+        x = x.float()
     wg = (rng.normal(size=(d, E)) * 0.02).astype(np.float32)
     L = (rng.normal(size=(T, E)) * 3).astype(np.float32)
     L.reshape(-1)[:6] = [0.0, -40.0, 40.0, 1e-6, -1e-6, 88.0]
