@@ -40,13 +40,13 @@ _SHARED_SOURCES = ("moe_expert_routing_sqrt_amd/csrc/gemm_common.h",
                    "moe_expert_routing_sqrt_amd/build.py")
 TRAFFIC = {
     "v3": {"sources": ("moe_expert_routing_sqrt_amd/csrc/ffn_bf16.hip",) + _SHARED_SOURCES,
-           "sources_sha256": "b94bb83c4c5673da3526d482113d7a0c3caff54901c1a45ae3295581fb9aaf26",
-           "fetch_kib": 18773260.9, "fetch_scale": 1.99997,
+           "sources_sha256": "4f5ca019e4448e8250ebb5a31de27c215eec408a7105162f9ef9c2eafccb24ab",
+           "fetch_kib": 18116837.2, "fetch_scale": 1.99997,
            "write_kib": 524627.8, "write_scale": 1.0},
     "v3_fp8": {"sources": ("moe_expert_routing_sqrt_amd/csrc/gemm_fp8p.hip",) + _SHARED_SOURCES,
-               "sources_sha256": "32ef9d352e661fd75e30b997fd2d3a2b8f1cc12c108409e414a079b20eeb8a16",
-               "fetch_kib": 10548098.2, "fetch_scale": 1.99997,
-               "write_kib": 298310.0, "write_scale": 1.0},
+               "sources_sha256": "1dca5adcaaacf7cc28641e5ca031dfd4150da32daf59f3ec19aba076a4915d5c",
+               "fetch_kib": 10424332.3, "fetch_scale": 1.99997,
+               "write_kib": 298133.8, "write_scale": 1.0},
 }
 
 

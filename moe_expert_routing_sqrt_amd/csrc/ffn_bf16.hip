@@ -566,21 +566,6 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
 
 std::atomic<unsigned> g_launches{0};
 
-// compute units of the current device (cached per device)
-int cu_count() {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cached[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 template <int MODE>
 hipError_t launch(FfnArgs& a, int64_t max_rows, hipStream_t s) {
   if (a.K % (2 * BK) != 0 || a.K < 4 * BK) return hipErrorInvalidValue;
@@ -592,7 +577,7 @@ hipError_t launch(FfnArgs& a, int64_t max_rows, hipStream_t s) {
   const int64_t tiles = mt * a.n_tiles;
   if (tiles <= 0) return hipSuccess;
   // one work-group per CU (the LDS holds one), a multiple of the XCD count
-  const int64_t grid = (std::min<int64_t>(tiles, cu_count()) + kXcds - 1) / kXcds * kXcds;
+  const int64_t grid = (std::min<int64_t>(tiles, device_cu_count()) + kXcds - 1) / kXcds * kXcds;
   a.slot = static_cast<int>(g_launches.fetch_add(1, std::memory_order_relaxed) % kSlots);
   hipLaunchKernelGGL((ffn_gemm_kernel<MODE>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();

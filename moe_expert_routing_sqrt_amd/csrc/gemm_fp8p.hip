@@ -644,19 +644,6 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
 
 std::atomic<unsigned> g_launches_fp8{0};
 
-int cu_count_fp8() {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cached[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 template <int MODE>
 hipError_t launch(Fp8Args& a, int64_t max_rows, hipStream_t s) {
   if (!ffn_fp8p_supported_k(a.K)) return hipErrorInvalidValue;
@@ -665,7 +652,7 @@ hipError_t launch(Fp8Args& a, int64_t max_rows, hipStream_t s) {
   const int64_t mt = max_row_tiles(max_rows, a.offsets == nullptr ? 1 : a.n_exp, BM);
   const int64_t tiles = mt * a.n_tiles;
   if (tiles <= 0) return hipSuccess;
-  const int64_t grid = (std::min<int64_t>(tiles, cu_count_fp8()) + kXcds - 1) / kXcds * kXcds;
+  const int64_t grid = (std::min<int64_t>(tiles, device_cu_count()) + kXcds - 1) / kXcds * kXcds;
   a.slot = static_cast<int>(g_launches_fp8.fetch_add(1, std::memory_order_relaxed) % kSlots);
   hipLaunchKernelGGL((ffn_fp8_kernel<MODE>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
