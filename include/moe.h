@@ -188,13 +188,17 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const int32_t*
  *   stages    MOE_FFN_UP, MOE_FFN_DOWN or MOE_FFN_ALL
  * Supported: MOE_BF16 any d, d_ff: on the matrix cores when d % 256 == 0,
  * d_ff % 128 == 0 and d_ff >= 256, on the vector ALUs otherwise; MOE_E4M3
- * needs d % 256 == 0 and d_ff % 128 == 0; MOE_F32 any d, d_ff.
- * The bf16 matrix-core products schedule their tiles with device-side ticket
- * counters owned by the library (16 sets per device, one per launch in
- * rotation, cleared by each launch as it ends): up to 16 of these launches may
- * execute at the same time on one device (e.g. on different streams); more
- * concurrently executing launches are outside the contract.  The same holds
- * for moe_expert_ffn_train.
+ * needs d % 256 == 0 and d_ff % 128 == 0 (a product whose reduction width,
+ * d for the up-projection and d_ff for the down, is a multiple of 256 and
+ * at least 512 runs persistent, a narrower one one tile per work-group);
+ * MOE_F32 any d, d_ff.
+ * The bf16 matrix-core products and the persistent e4m3 products schedule
+ * their tiles with device-side ticket counters owned by the library (16 sets
+ * per device and kernel, one per launch in rotation, cleared by each launch as
+ * it ends): up to 16 of these launches of one kind may execute at the same
+ * time on one device (e.g. on different streams); more concurrently executing
+ * launches are outside the contract.  The same holds for
+ * moe_expert_ffn_train.
  */
 int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int32_t d,
                    int32_t d_ff, int dtype, const void* xp, const float* xp_scale,
