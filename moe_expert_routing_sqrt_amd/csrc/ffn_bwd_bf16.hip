@@ -25,6 +25,7 @@
 // WGRAD's K is the group's row count: the last step is partial, and rows past
 // the group (or past the buffer) are fetched from a zero row.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "gemm_common.h"
@@ -41,6 +42,7 @@ constexpr int NW = 8, WAVES_M = 4, WAVES_N = 2;
 constexpr int kThreads = NW * 64;
 constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;  // 64 x 128 per wave
 constexpr int RM = TM / 32, RN = TN / 32;
+constexpr int HB = BM / RM;  // DGRAD: row distance between a wave's two 32-row blocks
 constexpr int NS = BK / 16, NQ = RM * RN;
 constexpr int KROW_BYTES = 512;          // K-major LDS row: 256 bf16
 constexpr int DPW = 4;                   // DMA instructions per operand per wave per step
@@ -97,8 +99,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_dgrad_kernel(const BwdArgs p)
   const int n_tile = __builtin_amdgcn_readfirstlane(ti.n_tile);
   const int row0 = __builtin_amdgcn_readfirstlane(ti.row0);
   const int rows = __builtin_amdgcn_readfirstlane(ti.rows);  // valid rows of the tile
-  // a wave whose 64 rows lie past the valid rows skips its MFMAs
-  const bool act = wm * TM < rows;
+  // valid 32-row blocks of this wave: block i covers rows i*HB + 32*wm + [0, 32),
+  // so the two waves sharing a SIMD (wm and wm + 2) hold blocks in every 64-row
+  // band and a ragged tile costs its rows rounded up to 64; a block past the
+  // valid rows skips its MFMAs and fragment reads
+  const int nb = __builtin_amdgcn_readfirstlane((rows > 32 * wm) + (rows > HB + 32 * wm));
   const int nsteps = p.K / BK;
 
   // ---- DMA sources.  Row-major A: blocks of 8 rows x 128 B, chunk swizzle
@@ -164,47 +169,55 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_dgrad_kernel(const BwdArgs p)
     const int idx = f == 0 ? 0 : (f <= RN ? f - 1 : f - RN);
     if (is_a) {
       const uint4* s = reinterpret_cast<const uint4*>(sa);
-      fa[buf][idx] = as_bf16x8(s[swz(wm * TM + idx * 32 + (lane & 31), 2 * s16 + (lane >> 5))]);
+      fa[buf][idx] = as_bf16x8(s[swz(idx * HB + 32 * wm + (lane & 31), 2 * s16 + (lane >> 5))]);
     } else {
       fb[buf][idx] = kmajor_frag(sb, wn * TN + idx * 32, s16);
     }
   };
-  constexpr int NR = RM + RN;
-  static_assert(NR <= NQ, "one read per MFMA slot");
-  auto slice = [&](int s, const char* rsa, const char* rsb, int rs, int kd, char* da, char* db, int d0,
+  static_assert(RM + RN <= NQ, "one read per MFMA slot");
+  // MFMAs of slice s over the first NB row blocks; with one block there are
+  // five reads for four MFMA slots: the first slot takes two
+  auto slice = [&](auto nbc, int s, const char* rsa, const char* rsb, int rs, int kd, char* da, char* db, int d0,
                    int d1) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nbc)::value;
+    constexpr int NQB = NB * RN, NRB = NB + RN;
+    constexpr int XR = NRB > NQB ? NRB - NQB : 0;
     const int buf = s & 1;
     const int nd = d1 - d0;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
+    for (int q = 0; q < NQB; ++q) {
       const int i = q / RN, j = q % RN;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
-      if (rsa != nullptr && q < NR) read_frag(rsa, rsb, buf ^ 1, rs, q);
+      if (rsa != nullptr) {
+#pragma unroll
+        for (int f = 0; f < NRB; ++f)
+          if ((f < XR ? 0 : f - XR) == q) read_frag(rsa, rsb, buf ^ 1, rs, f);
+      }
       if (kd >= 0) {
 #pragma unroll
         for (int t = 0; t < NDMA; ++t)
-          if (t < nd && (t * NQ) / nd == q) dma_one(kd, da, db, d0 + t);
+          if (t < nd && (t * NQB) / nd == q) dma_one(kd, da, db, d0 + t);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto step = [&](int kt, char* sa, char* sb, char* na, char* nb) __attribute__((always_inline)) {
+  auto step = [&](auto nbc, int kt, char* sa, char* sb, char* na, char* nb_) __attribute__((always_inline)) {
     const bool more = kt + 1 < nsteps;
-    slice(0, sa, sb, 1, (kt >= 1 && more) ? kt + 1 : -1, na, nb, DHALF, NDMA);
+    slice(nbc, 0, sa, sb, 1, (kt >= 1 && more) ? kt + 1 : -1, na, nb_, DHALF, NDMA);
 #pragma unroll
-    for (int s = 1; s + 1 < NS; ++s) slice(s, sa, sb, s + 1, -1, nullptr, nullptr, 0, 0);
+    for (int s = 1; s + 1 < NS; ++s) slice(nbc, s, sa, sb, s + 1, -1, nullptr, nullptr, 0, 0);
     if (more) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       wait_vmcnt<0>();
       barrier_only();
     }
-    slice(NS - 1, more ? na : nullptr, nb, 0, kt + 2 < nsteps ? kt + 2 : -1, sa, sb, 0, DHALF);
+    slice(nbc, NS - 1, more ? na : nullptr, nb_, 0, kt + 2 < nsteps ? kt + 2 : -1, sa, sb, 0, DHALF);
   };
-  auto idle_step = [&](int kt, char* sa, char* sb, char* na, char* nb) __attribute__((always_inline)) {
+  auto idle_step = [&](int kt, char* sa, char* sb, char* na, char* nb_) __attribute__((always_inline)) {
     const bool more = kt + 1 < nsteps;
     if (kt >= 1 && more) {
 #pragma unroll
-      for (int q = DHALF; q < NDMA; ++q) dma_one(kt + 1, na, nb, q);
+      for (int q = DHALF; q < NDMA; ++q) dma_one(kt + 1, na, nb_, q);
     }
     if (more) {
       wait_vmcnt<0>();
@@ -227,12 +240,21 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_dgrad_kernel(const BwdArgs p)
       wait_vmcnt<0>();
     }
     barrier_only();
-    if (act) {
+    if (nb == RM) {
+      using NBC = std::integral_constant<int, RM>;
 #pragma unroll
-      for (int f = 0; f < NR; ++f) read_frag(sA0, sB0, 0, 0, f);
+      for (int f = 0; f < RM + RN; ++f) read_frag(sA0, sB0, 0, 0, f);
       for (int kt = 0; kt < nsteps; kt += 2) {
-        step(kt, sA0, sB0, sA1, sB1);
-        if (kt + 1 < nsteps) step(kt + 1, sA1, sB1, sA0, sB0);
+        step(NBC{}, kt, sA0, sB0, sA1, sB1);
+        if (kt + 1 < nsteps) step(NBC{}, kt + 1, sA1, sB1, sA0, sB0);
+      }
+    } else if (nb == 1) {
+      using NBC = std::integral_constant<int, 1>;
+#pragma unroll
+      for (int f = 0; f <= RN; ++f) read_frag(sA0, sB0, 0, 0, f);
+      for (int kt = 0; kt < nsteps; kt += 2) {
+        step(NBC{}, kt, sA0, sB0, sA1, sB1);
+        if (kt + 1 < nsteps) step(NBC{}, kt + 1, sA1, sB1, sA0, sB0);
       }
     } else {
       for (int kt = 0; kt < nsteps; kt += 2) {
@@ -245,16 +267,16 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_dgrad_kernel(const BwdArgs p)
   // ---- epilogue.  Accumulator (i, j) register v holds row 8*(v/4) +
   // 4*(lane/32) + v%4 and column lane%32 of its 32x32 block.
   barrier_only();
-  if (act) {
 #pragma unroll
-    for (int i = 0; i < RM; ++i)
+  for (int i = 0; i < RM; ++i) {
+    if (i >= nb) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int lr = wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        uint16_t* row = reinterpret_cast<uint16_t*>(base + lr * OUT_PITCH);
+    for (int v = 0; v < 16; ++v) {
+      const int lr = i * HB + 32 * wm + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      uint16_t* row = reinterpret_cast<uint16_t*>(base + lr * OUT_PITCH);
 #pragma unroll
-        for (int j = 0; j < RN; ++j) row[wn * TN + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][v]);
-      }
+      for (int j = 0; j < RN; ++j) row[wn * TN + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][v]);
+    }
   }
   __syncthreads();
   constexpr int OCH = BN * 2 / 16;
