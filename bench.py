@@ -63,6 +63,9 @@ def parse():
                     help="also time forward+backward steps (bf16 top-k workload) and report the backward")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 2 GiB copy (counter calibration for --pmc passes)")
+    ap.add_argument("--up-variants", action="store_true",
+                    help="instead of the bench: time the routed up-projection against the same rows in "
+                         "equal shares per expert and against one expert's weights (one JSON line)")
     return ap.parse_args()
 
 
@@ -217,6 +220,46 @@ def cpu_baseline(cfg, inp, ex, S, ids=None):
             "seconds": t}
 
 
+def up_variants(torch, M, cfg, layer, x, ids):
+    """The routed up-projection of one forward, then the same packed rows split
+    equally over the experts (every tile full, every expert's own weights) and
+    given to one expert (one weight set), in that order: the mean of five
+    back-to-back launches each, printed as one JSON line.  Three forwards
+    first bring the clocks up."""
+    for _ in range(3):
+        layer.forward(x, token_ids=ids)
+    torch.cuda.synchronize()
+    b = layer.dbufs
+    rows = int(b["offsets"][-1].item())
+    n = layer.w13.shape[0]
+    dev = x.device
+    first = lambda t: None if t is None else t[:1]
+    variants = [("routed", b["offsets"], layer.w13, layer.w13_s)]
+    if rows % n == 0:
+        variants.append(("uniform", torch.arange(0, rows + 1, rows // n, dtype=torch.int32, device=dev),
+                         layer.w13, layer.w13_s))
+    variants.append(("dense", torch.tensor([0, rows], dtype=torch.int32, device=dev), layer.w13[:1],
+                     first(layer.w13_s)))
+    flops = 4 * cfg.d * cfg.d_ff * rows
+    res = {}
+    for name, off, w13, w13_s in variants:
+        # five back-to-back launches between two events on the launch stream
+        # (no host gap between them); the first (untimed) brings the clocks up
+        run = lambda: M.expert_ffn(off, layer.max_rows, b["xp"], w13, layer.w2, layer.dtype,
+                                   xp_scale=b["xp_scale"], w13_scale=w13_s, w2_scale=layer.w2_s, h=layer.h,
+                                   h_scale=layer.h_s, yp=layer.yp, stages=M.MOE_FFN_UP)
+        run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        res[name] = {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
+    print(json.dumps({"up_variants": res, "workload": workload_name(cfg), "rows": rows}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -243,6 +286,9 @@ def main():
     ids = gen.token_ids(cfg, device=dev) if a.router == "hash" else None
     torch.cuda.synchronize()
     print(f"setup {time.perf_counter() - t_setup:.1f}s: {workload_name(cfg, a.router)}", file=sys.stderr, flush=True)
+    if a.up_variants:
+        up_variants(torch, M, cfg, layer, x, ids)
+        return
 
     for _ in range(a.warmup):
         layer.forward(x, token_ids=ids)
