@@ -201,7 +201,11 @@ def test_backward_checks():
                                 None, 0, None) == _lib.MOE_ERR_INVALID_ARG
     big = ctypes.byref(_lib.MoeShape(16384, 7168, 256, 8, 4, 8, 2, 2048))
     need = L.moe_route_backward_workspace_size(big)
-    assert need == 16 * 7168 * 256 * 4
+    # the larger of the two paths: 16 fp32 K-parts of dW_g, or the bf16-plane
+    # path (dlogits as 6 and 3 planes, W_g as 6 planes, 8 row splits of fp32
+    # [d, 3E] partials)
+    T, d, E = 16384, 7168, 256
+    assert need == max(16 * d * E * 4, T * 6 * E * 2 + d * 6 * E * 2 + T * 3 * E * 2 + 8 * d * 3 * E * 4)
     assert L.moe_route_backward(big, bad, BF, bad, None, bad, bad, bad, bad, bad, bad, bad, need - 1,
                                 None) == _lib.MOE_ERR_WORKSPACE
     assert L.moe_route_backward_workspace_size(sh(T=1000)) == 0
