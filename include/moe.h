@@ -153,7 +153,10 @@ int moe_route(const moe_shape* shape, const void* x, int x_dtype, const void* w_
  *            with one fp32 scale per 1 x 128 tile: scale = amax/448, or 1
  *            for an all-zero tile; code = e4m3(x / scale) rounded to
  *            nearest-even, saturating)
- *   xp_scale [T*k, d/128] fp32 out for MOE_E4M3, else ignored (may be NULL)
+ *   xp_scale [d/128, T*k] fp32 out for MOE_E4M3, else ignored (may be NULL):
+ *            block-major, the scale of row r's 128-column block b at
+ *            xp_scale[b * T*k + r], so one block's scales are contiguous
+ *            over rows (the layout moe_expert_ffn reads)
  *   ws       workspace of at least moe_dispatch_workspace_size() bytes
  * Row numbering is stable: within an expert, rows follow token order.
  */
@@ -177,13 +180,14 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const int32_t*
  *   max_rows  host upper bound on offsets[n_exp]: sizes the launch
  *   dtype     MOE_F32, MOE_BF16 or MOE_E4M3 (the storage type of xp, the
  *             weights and h); accumulation is fp32 throughout
- *   xp        [max_rows, d];  xp_scale [max_rows, d/128] fp32 for e4m3
+ *   xp        [max_rows, d];  xp_scale [d/128, max_rows] fp32 for e4m3
+ *             (block-major, as moe_dispatch writes it with max_rows = T*k)
  *   w13       [n_exp, 2*d_ff, d]: rows 0..d_ff-1 = W1 (gate), d_ff.. = W3 (up)
  *   w2        [n_exp, d, d_ff]
  *   w13_scale [n_exp, 2*d_ff/128, d/128], w2_scale [n_exp, d/128, d_ff/128]
  *             fp32 block scales for e4m3, else ignored
  *   h         [max_rows, d_ff] intermediate in dtype (bf16 for MOE_BF16);
- *             h_scale [max_rows, d_ff/128] for e4m3
+ *             h_scale [d_ff/128, max_rows] for e4m3 (block-major)
  *   yp        [max_rows, d] out: fp32 for MOE_F32, bf16 otherwise
  *   stages    MOE_FFN_UP, MOE_FFN_DOWN or MOE_FFN_ALL
  * Supported: MOE_BF16 any d, d_ff: on the matrix cores when d % 256 == 0,
@@ -223,8 +227,8 @@ int moe_combine(const moe_shape* shape, const int32_t* dest, const float* topk_w
 
 /*
  * moe_quantize_rows_e4m3 - bf16 [rows, cols] -> e4m3 codes [rows, cols] with
- * one fp32 scale per 1 x 128 tile of a row [rows, cols/128] (the same rule as
- * moe_dispatch's MOE_E4M3 output).  For the shared expert of the fp8 workload,
+ * one fp32 scale per 1 x 128 tile of a row, block-major [cols/128, rows] (the
+ * same rule and layout as moe_dispatch's MOE_E4M3 output).  For the shared expert of the fp8 workload,
  * whose input is the unpermuted token rows.  cols must be a multiple of 128.
  */
 int moe_quantize_rows_e4m3(int64_t rows, int32_t cols, const void* x, uint8_t* q, float* scale,

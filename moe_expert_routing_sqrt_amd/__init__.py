@@ -166,7 +166,7 @@ def dispatch(sh: MoeShape, idx: torch.Tensor, block_counts: torch.Tensor, x: tor
         b["dest"] = torch.empty((T, k), dtype=torch.int32, device=dev)
         b["src"] = torch.empty(rows, dtype=torch.int32, device=dev)
         b["xp"] = torch.empty((rows, d), dtype=_TORCH[out_dtype], device=dev)
-        b["xp_scale"] = (torch.empty((rows, d // MOE_FP8_TILE), dtype=torch.float32, device=dev)
+        b["xp_scale"] = (torch.empty((d // MOE_FP8_TILE, rows), dtype=torch.float32, device=dev)
                          if out_dtype == MOE_E4M3 else None)
         wsb = dispatch_workspace_bytes(sh, e_begin, e_end)
         b["ws"] = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
@@ -205,7 +205,7 @@ def expert_ffn(offsets: torch.Tensor, max_rows: int, xp: Optional[torch.Tensor],
     if h is None:
         h = torch.empty((max_rows, d_ff), dtype=_TORCH[dtype], device=dev)
     if dtype == MOE_E4M3 and h_scale is None:
-        h_scale = torch.empty((max_rows, d_ff // MOE_FP8_TILE), dtype=torch.float32, device=dev)
+        h_scale = torch.empty((d_ff // MOE_FP8_TILE, max_rows), dtype=torch.float32, device=dev)
     if yp is None and stages & MOE_FFN_DOWN:
         yp = torch.empty((max_rows, d), dtype=torch.float32 if dtype == MOE_F32 else torch.bfloat16,
                          device=dev)
@@ -243,14 +243,15 @@ def combine(sh: MoeShape, dest: torch.Tensor, topk_w: torch.Tensor, yp: torch.Te
 
 
 def quantize_rows_e4m3(x: torch.Tensor, q=None, scale=None):
-    """bf16 [rows, cols] -> e4m3 codes (uint8) + fp32 scales per 1x128 row tile."""
+    """bf16 [rows, cols] -> e4m3 codes (uint8) + fp32 scales per 1x128 row tile,
+    stored block-major: scale [cols/128, rows]."""
     rows, cols = x.shape
     if x.dtype != torch.bfloat16:
         raise TypeError("x must be bf16")
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if scale is None:
-        scale = torch.empty((rows, cols // MOE_FP8_TILE), dtype=torch.float32, device=x.device)
+        scale = torch.empty((cols // MOE_FP8_TILE, rows), dtype=torch.float32, device=x.device)
     _need(q, rows * cols, "q")
     _need(scale, rows * (cols // MOE_FP8_TILE), "scale")
     st = lib().moe_quantize_rows_e4m3(rows, cols, _ptr(x), _ptr(q), _ptr(scale), _stream())

@@ -107,7 +107,7 @@ struct PermArgs {
   int32_t* dest;
   int32_t* src;
   void* xp;
-  float* xp_scale;
+  float* xp_scale;  // [d/128][T*k]: the scales of one 128-column block contiguous over rows
 };
 
 // ROW_BYTES_ELEM: bytes per input element (2 bf16, 4 f32); FP8: quantise bf16 -> e4m3
@@ -184,12 +184,11 @@ __global__ __launch_bounds__(kPermThreads) void dispatch_permute_kernel(const Pe
 #pragma unroll
       for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(f[4 + i] / scale) << (8 * i);
       const uint2 out = make_uint2(lo, hi);
-      const int ntile = p.d / MOE_FP8_TILE;
       for (int j = 0; j < k; ++j) {
         const int r = s_dest[tt * kMaxK + j];
         if (r >= 0) {
           reinterpret_cast<uint2*>(static_cast<uint8_t*>(p.xp) + (int64_t)r * p.d)[c] = out;
-          if ((c & 15) == 0) p.xp_scale[(int64_t)r * ntile + (c >> 4)] = scale;
+          if ((c & 15) == 0) p.xp_scale[(int64_t)(c >> 4) * (p.T * p.k) + r] = scale;
         }
       }
     }

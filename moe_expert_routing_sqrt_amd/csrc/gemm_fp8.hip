@@ -44,14 +44,14 @@ enum { MODE_SWIGLU = 0, MODE_STORE = 1 };
 
 struct Fp8Args {
   const uint8_t* A;       // [rows, K] codes
-  const float* A_scale;   // [rows, K/128]
+  const float* A_scale;   // [K/128][rows_total]: a 128-wide block's scales contiguous over rows
   int64_t lda;            // bytes per row (= K)
   const uint8_t* B;       // [groups][N_rows][K] codes
   const float* B_scale;   // [groups][N_rows/128][K/128]
   int64_t b_group_stride; // bytes
   int64_t bs_group_stride;// floats
   void* C;
-  float* C_scale;         // SWIGLU: [rows, d_ff/128]
+  float* C_scale;         // SWIGLU: [d_ff/128][rows_total]
   int64_t ldc;
   const int* offsets;
   int n_exp;
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const Fp8Args p) 
   // row scales: lanes 0..15 of wave w fetch rows 16w..16w+15
   const int nkb = p.K / BKB;
   const int srow = 16 * wave + (lane & 15);
-  const float* s_src = p.A_scale + (int64_t)(ti.row0 + (srow < ti.rows ? srow : ti.rows - 1)) * nkb;
+  const float* s_src = p.A_scale + (ti.row0 + (srow < ti.rows ? srow : ti.rows - 1));
   // block scales of B for this wave's two 32-column blocks
   const float* bs = p.B_scale + (int64_t)ti.group * p.bs_group_stride;
   int sb_row[RN];
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const Fp8Args p) 
       } else if (q < ADMA + BDMA) {
         dma16(b_src[q - ADMA] + k0, lb + (wave + NW * (q - ADMA)) * 1024);
       } else {
-        if (lane < 16) dma4(s_src + kt, lds_addr(ss) + 64 * wave);
+        if (lane < 16) dma4(s_src + (int64_t)kt * p.rows_total, lds_addr(ss) + 64 * wave);
       }
     }
   };
@@ -254,7 +254,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const Fp8Args p) 
       }
     }
     __syncthreads();
-    const int ntile_h = p.d_ff / BKB;
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
 #pragma unroll
@@ -268,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const Fp8Args p) 
         const int64_t grow = ti.row0 + lr;
         const int col = ti.n_tile * (BN / 2) + wn * (TN / 2) + (lane & 31);
         static_cast<uint8_t*>(p.C)[grow * p.ldc + col] = static_cast<uint8_t>(f32_to_e4m3(hv[i][v] / sc));
-        if (wn == 0 && (lane & 31) == 0) p.C_scale[grow * ntile_h + ti.n_tile] = sc;
+        if (wn == 0 && (lane & 31) == 0) p.C_scale[(int64_t)ti.n_tile * p.rows_total + grow] = sc;
       }
     }
   } else {

@@ -85,14 +85,15 @@ enum { MODE_SWIGLU = 0, MODE_STORE = 1 };
 
 struct Fp8Args {
   const uint8_t* A;         // [rows, K] codes
-  const float* A_scale;     // [rows, K/128]
+  const float* A_scale;     // [K/128][scale_ld]: one 128-wide block's scales contiguous over rows
   int64_t lda;              // bytes per row (= K)
   const uint8_t* B;         // [groups][N_rows][K] codes
   const float* B_scale;     // [groups][N_rows/128][K/128]
   int64_t b_group_stride;   // bytes
   int64_t bs_group_stride;  // floats
   void* C;
-  float* C_scale;           // SWIGLU: [rows, d_ff/128]
+  float* C_scale;           // SWIGLU: [d_ff/128][scale_ld]
+  int64_t scale_ld;         // rows of the scale matrices (the buffers' row capacity)
   int64_t ldc;              // elements
   const int* offsets;
   int n_exp;
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
       x.a = reinterpret_cast<const char*>(p.A + (int64_t)t.row0 * p.lda);
       const int64_t w0 = (int64_t)t.n_tile * (SWI ? BN / 2 : BN);
       x.b = reinterpret_cast<const char*>(p.B + (int64_t)t.group * p.b_group_stride + w0 * p.K);
-      x.as = p.A_scale + (int64_t)t.row0 * nkb;
+      x.as = p.A_scale + t.row0;
       x.bs = p.B_scale + (int64_t)t.group * p.bs_group_stride;
       x.rows = t.rows;
       x.n_tile = t.n_tile;
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
           const int r = 64 * (wave % (BM / 64)) + lane;
           const int rr = r < x.rows ? r : 0;
           const uint32_t dst = wave < BM / 64 ? lds_addr(&s_sc[slot][0]) + 64 * 4 * wave : lds_addr(&s_sc_junk[0]);
-          dma4(x.as + (int64_t)rr * nkb + kk, dst);
+          dma4(x.as + (int64_t)kk * p.scale_ld + rr, dst);
         }
       } else {
         dma16_s(x.b + kb, b_off[q - ADMA], lds_addr(sb) + (wave + NW * (q - ADMA)) * 1024);
@@ -507,7 +508,6 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
           }
         }
         barrier_only();
-        const int ntile_h = p.d_ff / BKB;
         const int64_t col0 = (int64_t)ti.n_tile * (BN / 2) + wn * (TN / 2);
 #pragma unroll
         for (int i = 0; i < RM; ++i) {
@@ -529,7 +529,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
                 reinterpret_cast<uint8_t*>(st + (lr0 + vv) * H_PITCH)[jj * 32 + (ln & 31)] =
                     static_cast<uint8_t>(f32_to_e4m3(acc[i][jj][v] / sc));
               if (wn == 0 && (ln & 31) == 0 && lr < ti.rows)
-                p.C_scale[((int64_t)ti.row0 + lr) * ntile_h + ti.n_tile] = sc;
+                p.C_scale[(int64_t)ti.n_tile * p.scale_ld + ti.row0 + lr] = sc;
             }
             wave_lds_fence();
             // 8 rows x 64 codes: 8 bytes per lane
@@ -675,6 +675,7 @@ hipError_t launch_ffn_up_fp8p(int n_exp, const int32_t* offsets, int64_t max_row
   a.bs_group_stride = (int64_t)(2 * d_ff / BKB) * (d / BKB);
   a.C = h;
   a.C_scale = h_scale;
+  a.scale_ld = max_rows;
   a.ldc = d_ff;
   a.offsets = offsets;
   a.n_exp = n_exp;
@@ -697,6 +698,7 @@ hipError_t launch_ffn_down_fp8p(int n_exp, const int32_t* offsets, int64_t max_r
   a.b_group_stride = (int64_t)d * d_ff;
   a.bs_group_stride = (int64_t)(d / BKB) * (d_ff / BKB);
   a.C = yp;
+  a.scale_ld = max_rows;
   a.ldc = d;
   a.offsets = offsets;
   a.n_exp = n_exp;

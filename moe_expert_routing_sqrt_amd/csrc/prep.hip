@@ -104,7 +104,8 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(int64_t ntiles, int 
 #pragma unroll
   for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(f[4 + i] / sc) << (8 * i);
   *reinterpret_cast<uint2*>(q + row * cols + col) = make_uint2(lo, hi);
-  if (sub == 0) scale[t] = sc;
+  // scales block-major: [cols/128][rows]
+  if (sub == 0) scale[(t % tiles_per_row) * (ntiles / tiles_per_row) + row] = sc;
 }
 
 }  // namespace

@@ -63,18 +63,18 @@ class MoELayer:
         self.block_counts = torch.empty((n_blocks(T), E), dtype=torch.int32, device=dev)
         self.dbufs = None
         self.h = torch.empty((rows, d_ff), dtype=store, device=dev)
-        self.h_s = (torch.empty((rows, d_ff // MOE_FP8_TILE), dtype=torch.float32, device=dev)
+        self.h_s = (torch.empty((d_ff // MOE_FP8_TILE, rows), dtype=torch.float32, device=dev)
                     if self.dtype == MOE_E4M3 else None)
         self.yp = torch.empty((rows, d), dtype=act, device=dev)
         if self.has_shared:
             self.sh_offsets = torch.tensor([0, T], dtype=torch.int32, device=dev)
             self.sh_h = torch.empty((T, d_ff), dtype=store, device=dev)
-            self.sh_h_s = (torch.empty((T, d_ff // MOE_FP8_TILE), dtype=torch.float32, device=dev)
+            self.sh_h_s = (torch.empty((d_ff // MOE_FP8_TILE, T), dtype=torch.float32, device=dev)
                            if self.dtype == MOE_E4M3 else None)
             self.ysh = torch.empty((T, d), dtype=act, device=dev)
             if self.dtype == MOE_E4M3:
                 self.sh_xq = torch.empty((T, d), dtype=torch.uint8, device=dev)
-                self.sh_xs = torch.empty((T, d // MOE_FP8_TILE), dtype=torch.float32, device=dev)
+                self.sh_xs = torch.empty((d // MOE_FP8_TILE, T), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, d), dtype=torch.float32 if self.local else act, device=dev)
 
     def update_bias(self, gamma: float) -> torch.Tensor:

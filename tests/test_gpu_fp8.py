@@ -57,7 +57,8 @@ def test_quantize_rows_bitexact():
     torch.cuda.synchronize()
     qo, so = Q.quantize_rows(host(x))
     assert np.array_equal(_codes(q), qo)
-    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert s.shape == (1024 // 128, 777)                  # block-major: [cols/128, rows]
+    assert np.array_equal(np.ascontiguousarray(host(s).T).view(np.uint32), so.view(np.uint32))
 
 
 @pytest.mark.parametrize("name,T", [("v3_fp8", 1000), ("v3_fp8", None)])
@@ -78,8 +79,8 @@ def test_fp8_dispatch_bitexact(name, T):
     sel = np.arange(rows) if rows <= 3000 else np.random.default_rng(0).choice(rows, 3000, replace=False)
     qx, sx = Q.quantize_rows(o["x"][src[sel]])
     assert np.array_equal(_codes(b["xp"][torch.from_numpy(sel).to(dev)]), qx)
-    assert np.array_equal(host(b["xp_scale"][torch.from_numpy(sel).to(dev)]).view(np.uint32),
-                          sx.view(np.uint32))
+    xs_sel = host(b["xp_scale"][:, torch.from_numpy(sel).to(dev)])   # block-major [d/128, rows]
+    assert np.array_equal(np.ascontiguousarray(xs_sel.T).view(np.uint32), sx.view(np.uint32))
 
 
 def _deq_blocks(w):
