@@ -44,9 +44,9 @@ TRAFFIC = {
            "fetch_kib": 18116837.2, "fetch_scale": 1.99997,
            "write_kib": 524627.8, "write_scale": 1.0},
     "v3_fp8": {"sources": ("moe_expert_routing_sqrt_amd/csrc/gemm_fp8p.hip",) + _SHARED_SOURCES,
-               "sources_sha256": "1dca5adcaaacf7cc28641e5ca031dfd4150da32daf59f3ec19aba076a4915d5c",
-               "fetch_kib": 10424332.3, "fetch_scale": 1.99997,
-               "write_kib": 298133.8, "write_scale": 1.0},
+               "sources_sha256": "51b5af86b0a8f7ef87c5b93dc490239cf0567b046070dca8abcc248e7874feea",
+               "fetch_kib": 10515005.3, "fetch_scale": 1.99997,
+               "write_kib": 274459.8, "write_scale": 1.0},
 }
 
 
