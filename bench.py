@@ -182,7 +182,7 @@ def backward_bench(a, cfg, layer, x, ev, torch, alg, rows):
 def cpu_baseline(cfg, inp, ex, S, ids=None):
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import combine as OC, dispatch as OD, ffn as OF, hash_route as OH, route as OR
 
@@ -198,26 +198,50 @@ def cpu_baseline(cfg, inp, ex, S, ids=None):
     sh13 = ex["sh_w13"][0].cpu()
     sh2 = ex["sh_w2"][0].cpu()
     f = lambda t: t.float().numpy()
+    st = {}
+
+    def route_dispatch():
+        if ids is None:
+            _, idx_, w_ = OR.route(x, wg, bias, cfg.G, cfg.M, cfg.k, cfg.gk, off)
+        else:
+            idx_, w_ = OH.hash_route(ids[:S], cfg.E, cfg.k, HASH_SEED)
+        ta = time.perf_counter()
+        disp = OD.dispatch(idx_, cfg.E, cfg.e_begin, cfg.e_end)
+        return idx_, w_, disp, ta
+
     t0 = time.perf_counter()
-    if ids is None:
-        L, idx, w = OR.route(x, wg, bias, cfg.G, cfg.M, cfg.k, cfg.gk, off)
-    else:
-        idx, w = OH.hash_route(ids[:S], cfg.E, cfg.k, HASH_SEED)
-    counts, offsets, dest, src = OD.dispatch(idx, cfg.E, cfg.e_begin, cfg.e_end)
-    yp, _ = OF.grouped_ffn(OD.pack(x, src), offsets, None, None,
-                           weight_fn=lambda i: (f(w13_h[i]), f(w2_h[i])))
+    idx, w, (counts, offsets, dest, src), t1 = route_dispatch()
+    xp = OD.pack(x, src)
+    t2 = time.perf_counter()
+    yp, _ = OF.grouped_ffn(xp, offsets, None, None, weight_fn=lambda i: (f(w13_h[i]), f(w2_h[i])))
+    t3 = time.perf_counter()
+    ysh = None
+    if not cfg.local:
+        ysh, _ = OF.expert_forward(x, f(sh13), f(sh2))
+    t4 = time.perf_counter()
     if cfg.local:
         out = OC.combine(yp, dest, w, out_init=np.zeros((S, cfg.d)))
     else:
-        ysh, _ = OF.expert_forward(x, f(sh13), f(sh2))
         out = OC.combine(yp, dest, w, ysh=ysh)
-    t = time.perf_counter() - t0
+    t5 = time.perf_counter()
+    t = t5 - t0
+    for name, a, b in (("route", t0, t1), ("dispatch", t1, t2), ("routed_experts", t2, t3),
+                       ("shared_expert", t3, t4), ("combine", t4, t5)):
+        st[name] = {"seconds": b - a, "tokens_per_s": S / max(b - a, 1e-9)}
+    # route and dispatch again on one core
+    with threadpool_limits(1):
+        u0 = time.perf_counter()
+        _, _, (_, _, _, src1), u1 = route_dispatch()
+        OD.pack(x, src1)
+        u2 = time.perf_counter()
+    st["route_one_core"] = {"seconds": u1 - u0, "tokens_per_s": S / max(u1 - u0, 1e-9)}
+    st["dispatch_one_core"] = {"seconds": u2 - u1, "tokens_per_s": S / max(u2 - u1, 1e-9)}
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": S / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {S} of the {cfg.T} tokens, whole layer (route, dispatch, all routed "
                       f"experts they reach, shared expert, combine) in fp64 numpy; {t:.1f} s; "
                       f"host affinity {len(os.sched_getaffinity(0))} cpus",
-            "seconds": t}
+            "seconds": t, "stages": st}
 
 
 def up_variants(torch, M, cfg, layer, x, ids):
