@@ -84,7 +84,8 @@ def workload_name(cfg, router="topk") -> str:
 
 
 def algorithmic(cfg):
-    """Per-launch algorithmic work of each stage."""
+    """Per-launch algorithmic work of each stage: the bytes the method must move
+    or the FLOPs it must compute, padding and re-reads excluded."""
     T, d, E, k, d_ff = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
     P = T * k if not cfg.local else None
     act = 4 if cfg.dtype == "f32" else 2
@@ -287,7 +288,7 @@ def up_variants(torch, M, cfg, layer, x, ids):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this library runs on one GPU only; --gpus must be 1",
                           "n_gpus": a.gpus}))
         sys.exit(2)
     import torch

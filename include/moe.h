@@ -48,7 +48,7 @@ extern "C" {
 /* status codes */
 #define MOE_OK 0
 #define MOE_ERR_INVALID_ARG (-1)  /* null pointer, inconsistent shape, bad range */
-#define MOE_ERR_UNSUPPORTED (-2)  /* valid, but not a shape/dtype this build runs */
+#define MOE_ERR_UNSUPPORTED (-2)  /* valid, but not a shape/dtype this library runs */
 #define MOE_ERR_WORKSPACE (-3)    /* workspace smaller than *_workspace_size() */
 #define MOE_ERR_HIP (-4)          /* a kernel launch failed */
 

@@ -7,7 +7,7 @@ backward carries its own communication and splits into the gradient for the
 input and the gradient for the weights); zenaique "Why all to all dominates"
 (the backward mirrors dispatch and combine with two more all-to-alls).
 
-The pages give no formulas.  Reading (listed in the design doc): the backward is the
+The pages give no formulas.  Reading: the backward is the
 exact derivative of the forward the other modules define, with the expert
 selection held fixed (it is piecewise constant in the logits) and no gradient
 for the routing bias (it only steers selection and is moved by the balancing

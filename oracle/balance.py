@@ -8,7 +8,7 @@ Source
     auxiliary loss; Measured: the bias keeps the load from collapsing onto the
     expert that dominates at the start.
 
-Reading where the page is silent (listed in the design doc): after a batch, each
+Reading where the page is silent: after a batch, each
 expert's bias moves one fixed step gamma towards balance,
 
     bias_e <- bias_e + gamma * sign(mean_load - load_e),

@@ -6,7 +6,7 @@ tile of a row; expert weights are e4m3 with one fp32 scale per 128x128 block.
 price"; the 1.5 average bytes per element of mastering-deepseek-v4
 "Measured" is fp8 dispatch + bf16 combine.)
 
-Readings (listed in the design doc): e4m3 is the OCP E4M3FN format (bias 7, no
+Readings: e4m3 is the OCP E4M3FN format (bias 7, no
 infinities, max finite 448); conversion rounds to nearest, ties to the even
 code, and saturates at +-448; a tile's scale is fp32(amax / 448), or 1 when the
 tile is all zeros; the element code is e4m3(fp32(x / scale)); the sign bit

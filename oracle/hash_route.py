@@ -7,7 +7,7 @@ Source
     besides the affinity-based top-k router, a hash router emulates the early
     layers -- the expert set depends on the token, not on the gate.
 
-Readings where the page is silent (listed in the design doc):
+Readings where the page is silent:
   * the hash is a published counter-based generator, Philox4x64-10 (Salmon,
     Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11),
     keyed by (seed, 0) with counter (token id as uint32, block, 0, 0); each block

@@ -9,7 +9,7 @@ Sources
   * deepnotes "DeepSeek-V3 671B: the real parallelism mesh", The real cluster:
     4 consecutive experts per GPU, so a node holds a contiguous expert range.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * group g holds experts [g*E/G, (g+1)*E/G)  (consecutive placement);
   * a group's score is the sum of its gk = ceil(k/M) largest biased
     affinities, added in descending order in fp32;
