@@ -93,24 +93,6 @@ __device__ __forceinline__ void st_stream(void* p, uint4 v) {
   __builtin_nontemporal_store(w, static_cast<u32x4*>(p));
 }
 
-// ---------------------------------------------------------------- wave reductions
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
-  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
-  lo = __shfl_xor(lo, mask, kWave);
-  hi = __shfl_xor(hi, mask, kWave);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    uint64_t o = shfl_xor_u64(v, m);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
 // ---------------------------------------------------------------- grouped tile map
 //
 // A grouped GEMM launch covers n_exp row groups (experts): group i owns rows

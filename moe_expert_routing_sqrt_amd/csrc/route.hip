@@ -46,8 +46,57 @@ __device__ __forceinline__ int key_index(uint64_t key) {
   return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
 }
 
+// ---------------------------------------------------------------- lane exchanges
+// A max over aligned groups of 2^s lanes is built stage by stage: once every
+// lane of each 2^(s-1)-lane group holds its group's max, any exchange that
+// pairs each such group with its partner group finishes the next stage.
+// Inside a 16-lane row the exchanges are DPP moves (quad permutes, then the
+// 8- and 16-lane mirrors); across rows they are gfx950's row swaps (16 and
+// 32 lanes).  Every lane of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(v), CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(v >> 32), CTRL, 0xF, 0xF, false);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// max of v and the value of the lane 16 (ROW32: 32) lanes away
+template <bool ROW32>
+__device__ __forceinline__ uint64_t row_swap_max_u64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  uint32_t l0, l1, h0, h1;
+  if constexpr (ROW32) {
+    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    l0 = l[0]; l1 = l[1]; h0 = h[0]; h1 = h[1];
+  } else {
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    l0 = l[0]; l1 = l[1]; h0 = h[0]; h1 = h[1];
+  }
+  // one of the two halves is the lane's own value, the other its partner's
+  return umax64((static_cast<uint64_t>(h0) << 32) | l0, (static_cast<uint64_t>(h1) << 32) | l1);
+}
+
+// max over aligned groups of `width` lanes (a power of two, 1..64), in every lane
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v, int width) {
+  if (width >= 2) v = umax64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
+  if (width >= 4) v = umax64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
+  if (width >= 8) v = umax64(v, dpp_u64<0x141>(v));  // row_half_mirror
+  if (width >= 16) v = umax64(v, dpp_u64<0x140>(v)); // row_mirror
+  if (width >= 32) v = row_swap_max_u64<false>(v);
+  if (width >= 64) v = row_swap_max_u64<true>(v);
+  return v;
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane_uniform) {
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), __builtin_amdgcn_readfirstlane(lane_uniform)));
+}
+
 constexpr int kTokPerBlock = MOE_ROUTE_BLOCK;
-constexpr int kWavesPerWg = 8;
+constexpr int kWavesPerWg = 16;
 
 struct RouteArgs {
   const float* logits;
@@ -106,10 +155,7 @@ __global__ __launch_bounds__(kWavesPerWg * kWave) void route_select_kernel(const
         uint64_t kk = (lane_ok && !used[i]) ? make_key(b[i], e0 + i) : 0;
         key = kk > key ? kk : key;
       }
-      for (int m = 1; m < lpg; m <<= 1) {
-        uint64_t o = shfl_xor_u64(key, m);
-        key = o > key ? o : key;
-      }
+      key = group_max_u64(key, lpg);
       const float v = key_value(key);
       gscore = r == 0 ? v : gscore + v;
       const int win = key_index(key);
@@ -121,7 +167,7 @@ __global__ __launch_bounds__(kWavesPerWg * kWave) void route_select_kernel(const
     uint64_t gkey = lane_ok ? make_key(gscore, my_group) : 0;
     bool gsel = false;
     for (int r = 0; r < p.M; ++r) {
-      const uint64_t m = wave_max_u64(gkey);
+      const uint64_t m = group_max_u64(gkey, kWave);
       if (lane_ok && gkey == m) {
         gsel = true;
         gkey = 0;
@@ -145,10 +191,10 @@ __global__ __launch_bounds__(kWavesPerWg * kWave) void route_select_kernel(const
           best_s = s[i];
         }
       }
-      const uint64_t m = wave_max_u64(key);
+      const uint64_t m = group_max_u64(key, kWave);
       const int win = key_index(m);
       const int owner = win / EPL;
-      const float s_win = __shfl(best_s, owner, kWave);
+      const float s_win = lane_value(best_s, owner);
       if (lane == owner) {
 #pragma unroll
         for (int i = 0; i < EPL; ++i) taken[i] = taken[i] || (e0 + i == win);
