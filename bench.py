@@ -40,13 +40,13 @@ _SHARED_SOURCES = ("moe_expert_routing_sqrt_amd/csrc/gemm_common.h",
                    "moe_expert_routing_sqrt_amd/build.py")
 TRAFFIC = {
     "v3": {"sources": ("moe_expert_routing_sqrt_amd/csrc/ffn_bf16.hip",) + _SHARED_SOURCES,
-           "sources_sha256": "4f5ca019e4448e8250ebb5a31de27c215eec408a7105162f9ef9c2eafccb24ab",
-           "fetch_kib": 18116837.2, "fetch_scale": 1.99997,
+           "sources_sha256": "23cf24a5e55cfb4ef500be7805ed0550240ecd14a608aa5a728a97b5c461a077",
+           "fetch_kib": 18642588.6, "fetch_scale": 1.99997,
            "write_kib": 524627.8, "write_scale": 1.0},
     "v3_fp8": {"sources": ("moe_expert_routing_sqrt_amd/csrc/gemm_fp8p.hip",) + _SHARED_SOURCES,
-               "sources_sha256": "51b5af86b0a8f7ef87c5b93dc490239cf0567b046070dca8abcc248e7874feea",
-               "fetch_kib": 10515005.3, "fetch_scale": 1.99997,
-               "write_kib": 274459.8, "write_scale": 1.0},
+               "sources_sha256": "d66ee96f45d1a738a35ef06a243694d553fee477e2f3d1d052995c4258c0b504",
+               "fetch_kib": 10603950.3, "fetch_scale": 1.99997,
+               "write_kib": 274610.8, "write_scale": 1.0},
 }
 
 

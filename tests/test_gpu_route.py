@@ -38,11 +38,12 @@ def test_route_bitexact_from_oracle_logits(name, T):
     assert np.array_equal(bc, block_counts(o["idx"], cfg.E))
 
 
-@pytest.mark.parametrize("name", ["tiny", "flash", "v3"])
-def test_gate_logits_tolerance(name):
+@pytest.mark.parametrize("name,T", [("tiny", None), ("flash", None), ("v3", None), ("v3", 1000), ("flash", 77)])
+def test_gate_logits_tolerance(name, T):
+    """Full sizes, and token counts that end in a partial 128- or 64-row tile."""
     dev = need_gpu()
-    cfg, inp, o = router_inputs(name)
-    print(f"route S1 {name}", flush=True)
+    cfg, inp, o = router_inputs(name, T)
+    print(f"route S1 {name} T={cfg.T}", flush=True)
     sh = moe_shape(cfg)
     w_prep = M.gate_prepare(inp["w_gate"])
     L, idx, w, bc = M.route(sh, inp["x"], w_prep, inp["bias"], inp["logit_offset"])
@@ -92,9 +93,12 @@ def test_affinity_bitexact_all_experts_selected():
 
 
 @pytest.mark.parametrize("E,G,M,k", [(16, 4, 2, 4), (64, 8, 4, 6), (256, 8, 4, 8), (256, 8, 1, 3),
-                                     (64, 1, 1, 4), (128, 4, 3, 7), (32, 8, 8, 16)])
+                                     (64, 1, 1, 4), (128, 4, 3, 7), (32, 8, 8, 16),
+                                     (256, 64, 8, 8), (128, 32, 4, 8), (64, 2, 2, 8), (256, 2, 2, 8)])
 def test_adversarial_ties(E, G, M, k):
-    """Dyadic logits with many exact ties and negative biased scores."""
+    """Dyadic logits with many exact ties and negative biased scores.  The
+    shapes give a group every lane width the kernel reduces over: 1, 2, 4, 8,
+    16, 32 and 64 lanes (experts per group / experts per lane)."""
     dev = need_gpu()
     rng = np.random.default_rng(E + 7 * M + k)
     T = 300
