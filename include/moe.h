@@ -157,7 +157,10 @@ int moe_route(const moe_shape* shape, const void* x, int x_dtype, const void* w_
  *            block-major, the scale of row r's 128-column block b at
  *            xp_scale[b * T*k + r], so one block's scales are contiguous
  *            over rows (the layout moe_expert_ffn reads)
- *   ws       workspace of at least moe_dispatch_workspace_size() bytes
+ *   ws       workspace of at least moe_dispatch_workspace_size() bytes: the
+ *            per-(64-token block, expert) base rows and, when d % 128 == 0, a
+ *            [d/128, T] fp32 table of each token's e4m3 scales (written once
+ *            per token, then gathered into xp_scale by packed row)
  * Row numbering is stable: within an expert, rows follow token order.
  */
 size_t moe_dispatch_workspace_size(const moe_shape* shape, int32_t e_begin, int32_t e_end);

@@ -102,10 +102,22 @@ int moe_route(const moe_shape* shape, const void* x, int x_dtype, const void* w_
                                         shape->group_topk, s));
 }
 
-size_t moe_dispatch_workspace_size(const moe_shape* shape, int32_t e_begin, int32_t e_end) {
-  if (check_shape(shape) != MOE_OK || e_begin < 0 || e_end < e_begin || e_end > shape->E) return 0;
+// dispatch workspace: per-(block, expert) base rows, then (when d % 128 == 0,
+// for the e4m3 output) the token-major scale table [d/128][T] at a 256-byte
+// aligned offset
+static size_t dispatch_base_bytes(const moe_shape* shape, int32_t e_begin, int32_t e_end) {
   const int64_t nblk = (shape->T + MOE_ROUTE_BLOCK - 1) / MOE_ROUTE_BLOCK;
   return static_cast<size_t>(nblk) * static_cast<size_t>(e_end - e_begin) * sizeof(int32_t);
+}
+static size_t dispatch_scale_offset(const moe_shape* shape, int32_t e_begin, int32_t e_end) {
+  return (dispatch_base_bytes(shape, e_begin, e_end) + 255) / 256 * 256;
+}
+
+size_t moe_dispatch_workspace_size(const moe_shape* shape, int32_t e_begin, int32_t e_end) {
+  if (check_shape(shape) != MOE_OK || e_begin < 0 || e_end < e_begin || e_end > shape->E) return 0;
+  if (shape->d % MOE_FP8_TILE != 0) return dispatch_base_bytes(shape, e_begin, e_end);
+  return dispatch_scale_offset(shape, e_begin, e_end) +
+         static_cast<size_t>(shape->d / MOE_FP8_TILE) * static_cast<size_t>(shape->T) * sizeof(float);
 }
 
 int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const int32_t* block_counts,
@@ -133,9 +145,12 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const int32_t*
   if (ws == nullptr || ws_bytes < moe_dispatch_workspace_size(shape, e_begin, e_end))
     return MOE_ERR_WORKSPACE;
   if (shape->T == 0) return MOE_OK;
+  float* tok_scale = out_dtype == MOE_E4M3
+                         ? reinterpret_cast<float*>(static_cast<char*>(ws) + dispatch_scale_offset(shape, e_begin, e_end))
+                         : nullptr;
   return hip_status(launch_dispatch(topk_idx, block_counts, shape->T, shape->k, shape->E, e_begin,
                                     e_end, x, x_dtype, out_dtype, shape->d, counts, offsets, dest,
-                                    src, xp, xp_scale, static_cast<int32_t*>(ws),
+                                    src, xp, xp_scale, static_cast<int32_t*>(ws), tok_scale,
                                     as_stream(stream)));
 }
 

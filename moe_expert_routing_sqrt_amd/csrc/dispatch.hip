@@ -16,7 +16,11 @@
 // The copy reads each token row once and writes it to its k rows with 16-byte
 // vector accesses; for the fp8 workload each 1 x 128 tile is quantised on the
 // way (scale = amax/448, code = e4m3(x/scale)), once per token, and the codes
-// and scale are stored to every copy.
+// are stored to every copy.  The scales go once per token into a token-major
+// table (block-major over tokens, coalesced); a second pass gathers them into
+// the block-major packed layout, xp_scale[b][r] = table[b][src[r]], so that the
+// packed scales are written contiguously instead of as one scattered 4-byte
+// store per (copy, block).
 #pragma clang fp contract(off)
 
 #include "common.h"
@@ -107,7 +111,7 @@ struct PermArgs {
   int32_t* dest;
   int32_t* src;
   void* xp;
-  float* xp_scale;  // [d/128][T*k]: the scales of one 128-column block contiguous over rows
+  float* tok_scale;  // [d/128][T]: e4m3 scale of token t's block b at tok_scale[b * T + t]
 };
 
 // ROW_BYTES_ELEM: bytes per input element (2 bf16, 4 f32); FP8: quantise bf16 -> e4m3
@@ -154,45 +158,60 @@ __global__ __launch_bounds__(kPermThreads) void dispatch_permute_kernel(const Pe
   constexpr int kVec = 16 / ELEM;  // elements per chunk
   const int nch = p.d / kVec;
   const int k = p.k;
-  for (int q = tid; q < ntok * nch; q += kPermThreads) {
-    const int tt = q / nch, c = q % nch;
-    const int64_t t = t0 + tt;
-    const uint4 v = reinterpret_cast<const uint4*>(static_cast<const char*>(p.x) + t * (int64_t)p.d * ELEM)[c];
-    if constexpr (!FP8) {
+  if constexpr (!FP8) {
+    for (int q = tid; q < ntok * nch; q += kPermThreads) {
+      const int tt = q / nch, c = q % nch;
+      const uint4 v = reinterpret_cast<const uint4*>(static_cast<const char*>(p.x) + (t0 + tt) * (int64_t)p.d * ELEM)[c];
       for (int j = 0; j < k; ++j) {
         const int r = s_dest[tt * kMaxK + j];
         if (r >= 0) st_stream(static_cast<char*>(p.xp) + ((int64_t)r * p.d * ELEM + (int64_t)c * 16), v);
       }
-    } else {
-      // 8 bf16 per chunk; a 128-wide tile is 16 consecutive chunks = 16 lanes
-      float f[8];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    }
+  } else {
+    // e4m3: a lane takes 16 bf16 (two 16-byte chunks) and writes their 16
+    // codes as one 16-byte store; a 128-column tile is 8 consecutive lanes
+    const int npair = p.d / 16;
+    for (int q = tid; q < ntok * npair; q += kPermThreads) {
+      const int tt = q / npair, c2 = q % npair;
+      const int64_t t = t0 + tt;
+      const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + t * (int64_t)p.d);
+      const uint4 v0 = xr[2 * c2], v1 = xr[2 * c2 + 1];
+      float f[16];
+      const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 8; ++i) {
         f[2 * i] = bf16_to_f32(static_cast<uint16_t>(w[i] & 0xFFFFu));
         f[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
       }
       float amax = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
 #pragma unroll
-      for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+      for (int m = 1; m < 8; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
       const float scale = e4m3_tile_scale(amax);
-      uint32_t lo = 0, hi = 0;
+      uint32_t o[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(f[i] / scale) << (8 * i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(f[4 + i] / scale) << (8 * i);
-      const uint2 out = make_uint2(lo, hi);
+      for (int i = 0; i < 16; ++i) o[i >> 2] |= f32_to_e4m3(f[i] / scale) << (8 * (i & 3));
+      const uint4 out = make_uint4(o[0], o[1], o[2], o[3]);
+      if ((c2 & 7) == 0) p.tok_scale[(int64_t)(c2 >> 3) * p.T + t] = scale;
       for (int j = 0; j < k; ++j) {
         const int r = s_dest[tt * kMaxK + j];
-        if (r >= 0) {
-          reinterpret_cast<uint2*>(static_cast<uint8_t*>(p.xp) + (int64_t)r * p.d)[c] = out;
-          if ((c & 15) == 0) p.xp_scale[(int64_t)(c >> 4) * (p.T * p.k) + r] = scale;
-        }
+        if (r >= 0) st_stream(static_cast<uint8_t*>(p.xp) + (int64_t)r * p.d + (int64_t)c2 * 16, out);
       }
     }
   }
+}
+
+// xp_scale[b][r] = tok_scale[b][src[r]] for the packed rows r < offsets[n]
+// (block b = blockIdx.y; rows past them are left as they are)
+__global__ __launch_bounds__(256) void scale_gather_kernel(const int32_t* __restrict__ src,
+                                                           const int32_t* __restrict__ n_rows,
+                                                           const float* __restrict__ tok_scale, int64_t T,
+                                                           int64_t P, float* __restrict__ xp_scale) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= *n_rows) return;
+  const int64_t b = blockIdx.y;
+  xp_scale[b * P + r] = tok_scale[b * T + src[r]];
 }
 
 }  // namespace
@@ -201,18 +220,22 @@ hipError_t launch_dispatch(const int32_t* idx, const int32_t* block_counts, int6
                            int E, int e_begin, int e_end, const void* x, int x_dtype,
                            int out_dtype, int d, int32_t* counts, int32_t* offsets,
                            int32_t* dest, int32_t* src, void* xp, float* xp_scale, int32_t* base,
-                           hipStream_t s) {
+                           float* tok_scale, hipStream_t s) {
   const int n = e_end - e_begin;
   const int nblk = static_cast<int>((T + MOE_ROUTE_BLOCK - 1) / MOE_ROUTE_BLOCK);
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, block_counts, nblk, E,
                      e_begin, n, counts, offsets, base);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  PermArgs a{idx, base, T, k, e_begin, e_end, n, x, d, dest, src, xp, xp_scale};
+  PermArgs a{idx, base, T, k, e_begin, e_end, n, x, d, dest, src, xp, tok_scale};
   const unsigned grid = static_cast<unsigned>((T + kTokPerWg - 1) / kTokPerWg);
-  if (out_dtype == MOE_E4M3)
+  if (out_dtype == MOE_E4M3) {
     hipLaunchKernelGGL((dispatch_permute_kernel<2, true>), dim3(grid), dim3(kPermThreads), 0, s, a);
-  else if (x_dtype == MOE_BF16)
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const int64_t P = T * k;
+    const dim3 g(static_cast<unsigned>((P + 255) / 256), static_cast<unsigned>(d / MOE_FP8_TILE));
+    hipLaunchKernelGGL(scale_gather_kernel, g, dim3(256), 0, s, src, offsets + n, tok_scale, T, P, xp_scale);
+  } else if (x_dtype == MOE_BF16)
     hipLaunchKernelGGL((dispatch_permute_kernel<2, false>), dim3(grid), dim3(kPermThreads), 0, s, a);
   else
     hipLaunchKernelGGL((dispatch_permute_kernel<4, false>), dim3(grid), dim3(kPermThreads), 0, s, a);

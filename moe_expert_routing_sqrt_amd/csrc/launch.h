@@ -28,7 +28,7 @@ hipError_t launch_dispatch(const int32_t* idx, const int32_t* block_counts, int6
                            int E, int e_begin, int e_end, const void* x, int x_dtype,
                            int out_dtype, int d, int32_t* counts, int32_t* offsets,
                            int32_t* dest, int32_t* src, void* xp, float* xp_scale, int32_t* base,
-                           hipStream_t s);
+                           float* tok_scale, hipStream_t s);
 
 // grouped expert FFN
 hipError_t launch_ffn_up_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,

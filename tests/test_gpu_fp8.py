@@ -61,17 +61,20 @@ def test_quantize_rows_bitexact():
     assert np.array_equal(np.ascontiguousarray(host(s).T).view(np.uint32), so.view(np.uint32))
 
 
-@pytest.mark.parametrize("name,T", [("v3_fp8", 1000), ("v3_fp8", None)])
-def test_fp8_dispatch_bitexact(name, T):
+@pytest.mark.parametrize("name,T,e_begin,e_end", [("v3_fp8", 1000, 0, None), ("v3_fp8", None, 0, None),
+                                                  ("v3_fp8", 1000, 4, 40)])
+def test_fp8_dispatch_bitexact(name, T, e_begin, e_end):
+    """Codes and block-major scales of the packed rows; the last case packs one
+    expert-parallel share (experts 4..39), so fewer rows than T*k."""
     dev = need_gpu()
     cfg, inp, o = router_inputs(name, T)
-    print(f"fp8 dispatch {name} T={cfg.T}", flush=True)
+    print(f"fp8 dispatch {name} T={cfg.T} experts [{e_begin}, {e_end})", flush=True)
     sh = moe_shape(cfg)
     from gpu_util import block_counts
     b = M.dispatch(sh, dev_i32(o["idx"], dev), dev_i32(block_counts(o["idx"], cfg.E), dev), inp["x"],
-                   out_dtype=M.MOE_E4M3)
+                   e_begin, e_end, out_dtype=M.MOE_E4M3)
     torch.cuda.synchronize()
-    counts, offsets, dest, src = OD.dispatch(o["idx"], cfg.E)
+    counts, offsets, dest, src = OD.dispatch(o["idx"], cfg.E, e_begin, e_end)
     rows = int(offsets[-1])
     assert np.array_equal(host(b["dest"]), dest)
     assert np.array_equal(host(b["src"])[:rows], src)
