@@ -73,49 +73,50 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(int rows, int cols
   }
 }
 
-// 16 threads per 128-wide tile, 8 elements each; 16 tiles per work-group.
-__global__ __launch_bounds__(256) void quantize_rows_kernel(int64_t ntiles, int cols,
+// 8 lanes per 128-wide tile, 16 elements each (two 16-byte loads, one
+// 16-byte store of codes); a wave covers 8 rows of one tile column and a
+// work-group 32 rows, so a work-group's block-major scales are 32
+// consecutive floats.
+__global__ __launch_bounds__(256) void quantize_rows_kernel(int64_t rows, int cols,
                                                             const uint16_t* __restrict__ x,
                                                             uint8_t* __restrict__ q,
                                                             float* __restrict__ scale) {
-  const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // tile index
-  if (t >= ntiles) return;                                          // whole 16-lane groups
-  const int sub = threadIdx.x & 15;
-  const int tiles_per_row = cols / kBlk;
-  const int64_t row = t / tiles_per_row;
-  const int64_t col = (t % tiles_per_row) * kBlk + sub * 8;
-  const uint4 v = *reinterpret_cast<const uint4*>(x + row * cols + col);
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float f[8];
+  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  if (row >= rows) return;  // whole 8-lane groups
+  const int blk = blockIdx.y;
+  const int sub = threadIdx.x & 7;
+  const int64_t col = (int64_t)blk * kBlk + sub * 16;
+  const uint4* src = reinterpret_cast<const uint4*>(x + row * cols + col);
+  const uint4 v0 = src[0], v1 = src[1];
+  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  float f[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     f[2 * i] = bf16_to_f32(static_cast<uint16_t>(w[i] & 0xFFFFu));
     f[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
   }
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
 #pragma unroll
-  for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+  for (int m = 1; m < 8; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
   const float sc = e4m3_tile_scale(amax);
-  uint32_t lo = 0, hi = 0;
+  uint32_t o[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(f[i] / sc) << (8 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(f[4 + i] / sc) << (8 * i);
-  *reinterpret_cast<uint2*>(q + row * cols + col) = make_uint2(lo, hi);
+  for (int i = 0; i < 16; ++i) o[i >> 2] |= f32_to_e4m3(f[i] / sc) << (8 * (i & 3));
+  *reinterpret_cast<uint4*>(q + row * cols + col) = make_uint4(o[0], o[1], o[2], o[3]);
   // scales block-major: [cols/128][rows]
-  if (sub == 0) scale[(t % tiles_per_row) * (ntiles / tiles_per_row) + row] = sc;
+  if (sub == 0) scale[(int64_t)blk * rows + row] = sc;
 }
 
 }  // namespace
 
 hipError_t launch_quantize_rows(int64_t rows, int cols, const uint16_t* x, uint8_t* q, float* scale,
                                 hipStream_t s) {
-  const int64_t ntiles = rows * (cols / kBlk);
-  if (ntiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)((ntiles + 15) / 16)), dim3(256), 0, s, ntiles,
-                     cols, x, q, scale);
+  if (rows == 0) return hipSuccess;
+  if (cols / kBlk > 65535) return hipErrorInvalidValue;  // tile columns are the grid's y
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)((rows + 31) / 32), (unsigned)(cols / kBlk)), dim3(256),
+                     0, s, rows, cols, x, q, scale);
   return hipGetLastError();
 }
 
