@@ -13,9 +13,11 @@ with weights stored [out, in]: w13 = [W1; W3] is [2*d_ff, d] and w2 is
 storage type between the two products).
 
 Pins (tests/test_oracle_ffn.py): a hand-derived worked example
-(tests/golden/swiglu_worked.json); flop counter equal to 6*d*d_ff per row;
-the dense evaluation (every expert on every token, gated by a T x E matrix)
-equals dispatch -> ffn -> combine.
+(tests/golden/swiglu_worked.json) for expert_forward and for expert_hidden
+(h = 1.5 ln3 there; a W1/W3 swap gives 2 sigmoid(2) ln3); expert_hidden
+followed by h W2^T equals expert_forward; flop counter equal to 6*d*d_ff per
+row; the dense evaluation (every expert on every token, gated by a T x E
+matrix) equals dispatch -> ffn -> combine.
 """
 from __future__ import annotations
 

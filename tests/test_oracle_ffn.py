@@ -72,3 +72,30 @@ def test_dense_equals_sparse(name, T):
     dense = _layer_dense(*args)
     assert np.allclose(sparse, dense, rtol=1e-12, atol=1e-12 * np.abs(dense).max())
     assert flops == (T * cfg.k + T) * 6 * cfg.d * cfg.d_ff
+
+
+def test_hidden_worked_example():
+    # expert_hidden feeds the fp8 emulation: h = silu(x W1^T) * (x W3^T) = 1.5 ln3
+    # on the hand-derived example (a W1/W3 swap gives 2 sigmoid(2) ln3 instead)
+    g = json.load(open(os.path.join(GOLD, "swiglu_worked.json")))
+    ln3 = math.log(3.0)
+    w13 = np.array([[ln3 if v == "ln3" else v for v in row] for row in g["w13"]])
+    h = F.expert_hidden(np.array([g["x"]]), w13)
+    assert h.shape == (1, 1)
+    assert abs(h[0, 0] - 1.5 * ln3) <= 1e-15 * ln3
+
+
+def test_hidden_then_down_projection_is_the_expert():
+    # h W2^T of expert_hidden equals expert_forward on random rows, and a swap
+    # of the gate and up halves of w13 changes the result
+    rng = np.random.default_rng(5)
+    d, d_ff, n = 16, 12, 9
+    X = rng.standard_normal((n, d))
+    w13 = rng.standard_normal((2 * d_ff, d))
+    w2 = rng.standard_normal((d, d_ff))
+    y, _ = F.expert_forward(X, w13, w2)
+    h = F.expert_hidden(X, w13)
+    assert h.shape == (n, d_ff)
+    assert np.allclose(h @ w2.T, y, rtol=1e-13, atol=1e-13 * np.abs(y).max())
+    swapped = np.concatenate([w13[d_ff:], w13[:d_ff]])
+    assert not np.allclose(F.expert_hidden(X, swapped), h)
