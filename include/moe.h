@@ -22,8 +22,13 @@
  *     allocates, frees or synchronises, and reads no device value back to the
  *     host (data-dependent sizes such as per-expert counts stay on the device,
  *     so row buffers are sized for the worst case T*k).
+ *   - Workspaces (`ws`, `ws_bytes`): device memory of at least
+ *     moe_workspace_size(op, shape, dtype) bytes, 256-byte aligned, else
+ *     MOE_ERR_WORKSPACE.  Calls that may execute at the same time (on other
+ *     streams, or replays of captured graphs) need distinct workspaces.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
- *     stream) in call order.  Calls are reentrant given distinct buffers.
+ *     stream) in call order.  Calls are reentrant given distinct buffers and
+ *     workspaces; the library keeps no device state between calls.
  *   - Everything is row-major.  Weights are [out, in], so the reduction
  *     dimension is contiguous for both products.  bf16 is IEEE bfloat16 (bit
  *     pattern in a uint16), e4m3 is OCP E4M3FN in a uint8.
@@ -43,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* status codes */
 #define MOE_OK 0
@@ -64,6 +69,14 @@ extern "C" {
 #define MOE_FFN_UP 1              /* h = silu(x W1^T) * (x W3^T)   */
 #define MOE_FFN_DOWN 2            /* y = h W2^T                    */
 #define MOE_FFN_ALL 3
+
+/* moe_workspace_size operations */
+#define MOE_OP_ROUTE 1
+#define MOE_OP_DISPATCH 2
+#define MOE_OP_EXPERT_FFN 3           /* also moe_expert_ffn_train */
+#define MOE_OP_COMBINE 4
+#define MOE_OP_ROUTE_BACKWARD 5
+#define MOE_OP_EXPERT_FFN_BACKWARD 6
 
 /* tokens per row of the block histogram written by moe_route */
 #define MOE_ROUTE_BLOCK 64
@@ -92,17 +105,17 @@ int moe_abi_version(void);
 const char* moe_status_str(int status);
 
 /*
- * moe_gate_prepare - store the fp32 router weight for the gate product.
- *   w_gate  [d, E] fp32 (in)
- *   w_prep  [3, E, d] bf16 (out): planes hi, mid, lo with hi+mid+lo == w
- *           exactly in fp32 (each plane the round-to-nearest bf16 of what the
- *           planes before it leave).  bf16 x times a bf16 plane is exact in
- *           fp32, so the gate product runs on bf16 matrix cores and stays
- *           fp32-accurate (the router is kept out of low precision: deepnotes
- *           "The iteration loop", the FP8 recipe excludes the router gate).
- * One-time weight preparation, like loading a checkpoint; not part of a step.
+ * moe_workspace_size - bytes of device workspace a call needs (0: none).
+ *   op     MOE_OP_*
+ *   shape  the call's shape (moe_expert_ffn*: any shape; the size does not
+ *          depend on it)
+ *   dtype  MOE_OP_ROUTE: x's type; MOE_OP_DISPATCH: the output type (the
+ *          e4m3 output needs a per-token scale table); otherwise ignored
+ * MOE_OP_ROUTE covers a call with logits = NULL (the larger case);
+ * MOE_OP_DISPATCH covers any expert range.  Returns 0 for an invalid shape
+ * or op.
  */
-int moe_gate_prepare(int32_t d, int32_t E, const float* w_gate, void* w_prep, moe_stream_t stream);
+size_t moe_workspace_size(int op, const moe_shape* shape, int dtype);
 
 /*
  * moe_route - routing for T tokens (mastering-deepseek-v4 "MoE + Expert-
@@ -110,29 +123,44 @@ int moe_gate_prepare(int32_t d, int32_t E, const float* w_gate, void* w_prep, mo
  * affinities, per-expert bias for balancing; zenaique "MoE node-limited
  * routing": at most M nodes per token).
  *   x             [T, d] in x_dtype (MOE_BF16 or MOE_F32); unused with LOGITS_IN
- *   w_prep        [3, E, d] bf16 from moe_gate_prepare; unused with LOGITS_IN
+ *   w_gate        [d, E] fp32 router weight; unused with LOGITS_IN.  The
+ *                 product runs on bf16 matrix cores and stays fp32-accurate:
+ *                 w_gate is split into three bf16 planes hi + mid + lo == w
+ *                 exactly (each the nearest bf16 of what the planes before it
+ *                 leave), bf16 x times a plane is exact in fp32, and the
+ *                 plane products accumulate in fp32 (the router is kept out of
+ *                 low precision: deepnotes "The iteration loop", the FP8
+ *                 recipe excludes the router gate)
  *   bias          [E] fp32 per-expert selection bias
  *   logit_offset  [E] fp32 added to every token's logits, or NULL
- *   logits        [T, E] fp32: out = x . W_g (fp32-accurate), or in with
- *                 MOE_ROUTE_LOGITS_IN
+ *   logits        [T, E] fp32: out = x . W_g, or NULL (kept in ws, not
+ *                 returned); in with MOE_ROUTE_LOGITS_IN (then required)
  *   topk_idx      [T, k] int32 out: chosen experts, biased affinity
  *                 descending, ties to the lower expert index
  *   topk_w        [T, k] fp32 out: s_j / (s_0 + s_1 + ... ) over the chosen
  *                 experts, s = unbiased affinity, left-to-right fp32 sum
  *   block_counts  [ceil(T/MOE_ROUTE_BLOCK), E] int32 out: pairs routed to each
  *                 expert within each block of MOE_ROUTE_BLOCK tokens
- * From logits on, every value is produced by a fixed fp32 operation sequence
- * (affinity = sqrt(max(l,0) + log1p(exp(-|l|))) with Cody-Waite exp and the
- * Goldberg log1p; group score = top group_topk biased affinities summed
+ * From logits on, every value is produced by a fixed operation sequence
+ * (affinity = fp32 of sqrt(softplus(l)) evaluated in fp64 -- ln2 + l/2 + l*l/8
+ * for |l| < 2^-14, else max(l,0) + log1p(exp(-|l|)) with a Cody-Waite exp and
+ * the Goldberg log1p -- and rounded once, so it never decreases as l grows;
+ * b = affinity + bias in fp32; group score = top group_topk biased affinities summed
  * largest first; top-M groups, ties to the lower group; experts outside kept
  * groups excluded), so results are reproducible bit for bit from the logits.
  * Supported: E <= 256 with E a multiple of 64 or E <= 64; E/G a multiple of
  * ceil(E/64) forming a power-of-two number of 64-lane wave lanes;
- * group_topk <= 4; k <= 16.  MOE_BF16 x needs d % 64 == 0 and E % 64 == 0.
+ * group_topk <= 4; k <= 16.  The matrix-core gate product needs bf16 x,
+ * d % 64 == 0 and E % 64 == 0 (else fp32 vector products, same planes).
+ *   ws            moe_workspace_size(MOE_OP_ROUTE, shape, x_dtype) bytes: the
+ *                 planes [3, E, d] bf16 (rewritten by every call), then the
+ *                 logits when `logits` is NULL.  Unused with LOGITS_IN (may be
+ *                 NULL).
  */
-int moe_route(const moe_shape* shape, const void* x, int x_dtype, const void* w_prep,
+int moe_route(const moe_shape* shape, const void* x, int x_dtype, const float* w_gate,
               const float* bias, const float* logit_offset, float* logits, int32_t* topk_idx,
-              float* topk_w, int32_t* block_counts, int flags, moe_stream_t stream);
+              float* topk_w, int32_t* block_counts, int flags, void* ws, size_t ws_bytes,
+              moe_stream_t stream);
 
 /*
  * moe_dispatch - pack token rows into an expert-contiguous buffer (deepmox
@@ -157,13 +185,12 @@ int moe_route(const moe_shape* shape, const void* x, int x_dtype, const void* w_
  *            block-major, the scale of row r's 128-column block b at
  *            xp_scale[b * T*k + r], so one block's scales are contiguous
  *            over rows (the layout moe_expert_ffn reads)
- *   ws       workspace of at least moe_dispatch_workspace_size() bytes: the
- *            per-(64-token block, expert) base rows and, when d % 128 == 0, a
+ *   ws       moe_workspace_size(MOE_OP_DISPATCH, shape, out_dtype) bytes: the
+ *            per-(64-token block, expert) base rows and, for MOE_E4M3, a
  *            [d/128, T] fp32 table of each token's e4m3 scales (written once
  *            per token, then gathered into xp_scale by packed row)
  * Row numbering is stable: within an expert, rows follow token order.
  */
-size_t moe_dispatch_workspace_size(const moe_shape* shape, int32_t e_begin, int32_t e_end);
 int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const int32_t* block_counts,
                  int32_t e_begin, int32_t e_end, const void* x, int x_dtype, int out_dtype,
                  int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src, void* xp,
@@ -193,25 +220,25 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const int32_t*
  *             h_scale [d_ff/128, max_rows] for e4m3 (block-major)
  *   yp        [max_rows, d] out: fp32 for MOE_F32, bf16 otherwise
  *   stages    MOE_FFN_UP, MOE_FFN_DOWN or MOE_FFN_ALL
+ *   ws        moe_workspace_size(MOE_OP_EXPERT_FFN, ...) bytes: the ticket
+ *             counters the persistent products schedule their tiles with (one
+ *             set for the up and one for the down product).  It must be
+ *             zero-filled before its first use; every call leaves it zero
+ *             again when its kernels complete, so it can serve any number of
+ *             calls in stream order (and replays of a captured graph).  Calls
+ *             that may execute at the same time need distinct workspaces.
  * Supported: MOE_BF16 any d, d_ff: on the matrix cores when d % 256 == 0,
  * d_ff % 128 == 0 and d_ff >= 256, on the vector ALUs otherwise; MOE_E4M3
  * needs d % 256 == 0 and d_ff % 128 == 0 (a product whose reduction width,
  * d for the up-projection and d_ff for the down, is a multiple of 256 and
  * at least 512 runs persistent, a narrower one one tile per work-group);
  * MOE_F32 any d, d_ff.
- * The bf16 matrix-core products and the persistent e4m3 products schedule
- * their tiles with device-side ticket counters owned by the library (16 sets
- * per device and kernel, one per launch in rotation, cleared by each launch as
- * it ends): up to 16 of these launches of one kind may execute at the same
- * time on one device (e.g. on different streams); more concurrently executing
- * launches are outside the contract.  The same holds for
- * moe_expert_ffn_train.
  */
 int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int32_t d,
                    int32_t d_ff, int dtype, const void* xp, const float* xp_scale,
                    const void* w13, const float* w13_scale, const void* w2,
                    const float* w2_scale, void* h, float* h_scale, void* yp, int stages,
-                   moe_stream_t stream);
+                   void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
  * moe_combine - out[t] = ysh[t] + sum_j topk_w[t,j] * yp[dest[t,j]]
@@ -280,11 +307,11 @@ int moe_combine_backward(const moe_shape* shape, const int32_t* dest, const floa
  * for moe_expert_ffn_backward with MOE_BWD_AU_SAVED, which then skips
  * recomputing them.  h and yp are bit-identical to moe_expert_ffn's.
  * offsets may be NULL with n_exp = 1 (one group of max_rows rows); d and d_ff
- * multiples of 256.
+ * multiples of 256.  ws as moe_expert_ffn's (MOE_OP_EXPERT_FFN).
  */
 int moe_expert_ffn_train(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int32_t d, int32_t d_ff,
                          int dtype, const void* xp, const void* w13, const void* w2, void* h, void* au, void* yp,
-                         moe_stream_t stream);
+                         void* ws, size_t ws_bytes, moe_stream_t stream);
 
 #define MOE_BWD_AU_SAVED 1  /* moe_expert_ffn_backward: au already holds [a | u] */
 
@@ -301,12 +328,15 @@ int moe_expert_ffn_train(int32_t n_exp, const int32_t* offsets, int64_t max_rows
  * [max_rows, 2*d_ff].  offsets as moe_expert_ffn (device, [n_exp+1]); NULL with
  * n_exp = 1 means one group of max_rows rows (the shared expert on x).  Weight
  * gradients are written (not accumulated); a group with no rows gets zeros.
- * dtype must be MOE_BF16; d and d_ff multiples of 256.
+ * dtype must be MOE_BF16; d and d_ff multiples of 256.  ws:
+ * moe_workspace_size(MOE_OP_EXPERT_FFN_BACKWARD, ...) bytes of ticket counters
+ * for the recomputed up-projection, zero-filled before first use and left zero
+ * by every call (as moe_expert_ffn's).
  */
 int moe_expert_ffn_backward(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int32_t d, int32_t d_ff,
                             int dtype, const void* xp, const void* w13, const void* w2, const void* d_yp,
                             void* au, void* h, void* d_au, void* d_xp, float* dw13, float* dw2, int flags,
-                            moe_stream_t stream);
+                            void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
  * moe_dispatch_backward - dx[t] (+)= d_extra[t] + sum_j d_xp[dest[t,j]] (slots
@@ -324,15 +354,14 @@ int moe_dispatch_backward(const moe_shape* shape, const int32_t* dest, const voi
  *   dx [T, d] fp32 += dlogits W_g^T;   dw_gate [d, E] fp32 = x^T dlogits.
  * x [T, d] in x_dtype; w_gate [d, E] fp32; logits [T, E] as moe_route wrote
  * them (without the offset); logit_offset [E] or NULL.  dw_gate sums over the
- * T tokens in up to 16 K-parts held in ws (moe_route_backward_workspace_size
- * bytes, enough for either path below; MOE_ERR_WORKSPACE if smaller), added
- * in part order (deterministic).  With bf16 x, d % 256 == 0 and E % 64 == 0
+ * T tokens in up to 16 K-parts held in ws (moe_workspace_size(
+ * MOE_OP_ROUTE_BACKWARD, shape, 0) bytes, enough for either path below;
+ * MOE_ERR_WORKSPACE if smaller), added in part order (deterministic).  With bf16 x, d % 256 == 0 and E % 64 == 0
  * both products run on the matrix cores: each fp32 operand is split into
  * three bf16 planes (hi + mid + lo, 24 significant bits) and the plane
  * products above 2^-24 of a product are summed in fp32 (six for dx, three
  * for dw_gate, x being exact in bf16); otherwise fp32 vector products.
  */
-size_t moe_route_backward_workspace_size(const moe_shape* shape);
 int moe_route_backward(const moe_shape* shape, const void* x, int x_dtype, const float* w_gate,
                        const float* logit_offset, const float* logits, const int32_t* topk_idx,
                        const float* d_topk_w, float* dlogits, float* dx, float* dw_gate, void* ws,
@@ -353,7 +382,7 @@ int moe_route_backward(const moe_shape* shape, const void* x, int x_dtype, const
  *   seed       key of the hash (one per layer)
  *   logits     [T, E] fp32 device or NULL.  NULL: topk_w = 1/k.  Otherwise
  *              topk_w[t,j] = s_j / (s_0 + ... + s_{k-1}) (left to right) with
- *              s = sqrt(softplus(logit)) by the same fp32 sequence as moe_route
+ *              s = sqrt(softplus(logit)) by the same operation sequence as moe_route
  *   topk_idx   [T, k] int32, topk_w [T, k] fp32, block_counts as moe_route
  * T = 0 is a no-op returning MOE_OK.
  */

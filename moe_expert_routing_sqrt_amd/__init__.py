@@ -5,7 +5,7 @@ HIP stream into the C ABI declared in include/moe.h; every step of the layer
 runs in the library's HIP kernels.  There is no CPU or PyTorch fallback: if the
 library is missing, or a tensor is not on the GPU, calls raise.
 
-    route(shape, x, w_prep, bias)            -> logits, topk_idx, topk_w, block_counts
+    route(shape, x, w_gate, bias)            -> logits, topk_idx, topk_w, block_counts
     route_hash(shape, token_ids, seed)       -> topk_idx, topk_w, block_counts
     dispatch(shape, topk_idx, block_counts, x) -> counts, offsets, dest, src, xp, xp_scale
     expert_ffn(offsets, max_rows, xp, w13, w2) -> yp
@@ -24,10 +24,12 @@ import torch
 
 from . import _lib
 from ._lib import (MOE_BF16, MOE_BWD_AU_SAVED, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN,  # noqa: F401
-                   MOE_FFN_UP,
-                   MOE_FP8_TILE, MOE_ROUTE_BLOCK, MOE_ROUTE_LOGITS_IN, MoeError, MoeShape)
+                   MOE_FFN_UP, MOE_FP8_TILE, MOE_OP_COMBINE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN,
+                   MOE_OP_EXPERT_FFN_BACKWARD, MOE_OP_ROUTE, MOE_OP_ROUTE_BACKWARD, MOE_ROUTE_BLOCK,
+                   MOE_ROUTE_LOGITS_IN, MoeError, MoeShape)
 
-__all__ = ["shape", "gate_prepare", "route", "route_hash", "dispatch", "combine_backward", "expert_ffn_train",
+__all__ = ["shape", "workspace_bytes", "workspace", "route", "route_hash", "dispatch", "combine_backward",
+           "expert_ffn_train",
            "expert_ffn_backward", "dispatch_backward", "route_backward", "expert_ffn", "combine",
            "quantize_blocks_e4m3", "quantize_rows_e4m3", "bias_update", "MoELayer", "MoeError", "lib"]
 
@@ -76,27 +78,38 @@ def n_blocks(T: int) -> int:
     return (T + MOE_ROUTE_BLOCK - 1) // MOE_ROUTE_BLOCK
 
 
-def gate_prepare(w_gate: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """fp32 W_g [d, E] -> [3, E, d] bf16 planes summing exactly to W_g."""
-    d, E = w_gate.shape
-    if w_gate.dtype != torch.float32:
-        raise TypeError("w_gate must be fp32")
-    if out is None:
-        out = torch.empty((3, E, d), dtype=torch.bfloat16, device=w_gate.device)
-    _need(out, 3 * E * d, "w_prep")
-    _lib.check("moe_gate_prepare", lib().moe_gate_prepare(d, E, _ptr(w_gate), _ptr(out), _stream()))
-    return out
+def workspace_bytes(op: int, sh: Optional[MoeShape] = None, dtype: int = MOE_BF16) -> int:
+    """moe_workspace_size: device bytes a call of kind `op` (MOE_OP_*) needs."""
+    if sh is None:
+        sh = MoeShape(1, 1, 1, 1, 1, 1, 1, 1)
+    return int(lib().moe_workspace_size(op, ctypes.byref(sh), dtype))
 
 
-def route(sh: MoeShape, x: Optional[torch.Tensor], w_prep: Optional[torch.Tensor], bias: torch.Tensor,
+def workspace(op: int, sh: Optional[MoeShape], dtype: int, device) -> Optional[torch.Tensor]:
+    """A zero-filled workspace for `op` (the expert products' ticket counters
+    must start at zero), or None when the call needs none."""
+    n = workspace_bytes(op, sh, dtype)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def _ws_len(ws: Optional[torch.Tensor]) -> int:
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def route(sh: MoeShape, x: Optional[torch.Tensor], w_gate: Optional[torch.Tensor], bias: torch.Tensor,
           logit_offset: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
-          logits_in: bool = False, idx=None, w=None, block_counts=None):
+          logits_in: bool = False, idx=None, w=None, block_counts=None, ws: Optional[torch.Tensor] = None,
+          keep_logits: bool = True):
+    """Gate logits (fp32 W_g [d, E]), sqrt(softplus) affinities, node-limited
+    top-k and block histogram.  keep_logits=False leaves the logits in the
+    workspace (returned logits is then None)."""
     T, E, k = sh.T, sh.E, sh.k
     dev = bias.device
     if logits is None:
         if logits_in:
             raise ValueError("logits_in needs logits")
-        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        if keep_logits:
+            logits = torch.empty((T, E), dtype=torch.float32, device=dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev) if idx is None else idx
     w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
     if block_counts is None:
@@ -110,12 +123,17 @@ def route(sh: MoeShape, x: Optional[torch.Tensor], w_prep: Optional[torch.Tensor
     x_dtype = MOE_BF16
     if not logits_in:
         _need(x, T * sh.d, "x")
-        _need(w_prep, 3 * E * sh.d, "w_prep")
+        _need(w_gate, sh.d * E, "w_gate")
+        if w_gate.dtype != torch.float32:
+            raise TypeError("w_gate must be fp32")
         x_dtype = _dt(x)
+        if ws is None:
+            ws = workspace(MOE_OP_ROUTE, sh, x_dtype, dev)
     st = lib().moe_route(ctypes.byref(sh), _ptr(x) if not logits_in else 0, x_dtype,
-                         _ptr(w_prep) if not logits_in else 0, _ptr(bias), _ptr(logit_offset),
+                         _ptr(w_gate) if not logits_in else 0, _ptr(bias), _ptr(logit_offset),
                          _ptr(logits), _ptr(idx), _ptr(w), _ptr(block_counts),
-                         MOE_ROUTE_LOGITS_IN if logits_in else 0, _stream())
+                         MOE_ROUTE_LOGITS_IN if logits_in else 0, _ptr(ws) if not logits_in else 0,
+                         _ws_len(ws) if not logits_in else 0, _stream())
     _lib.check("moe_route", st)
     return logits, idx, w, block_counts
 
@@ -144,11 +162,6 @@ def route_hash(sh: MoeShape, token_ids: torch.Tensor, seed: int, logits: Optiona
     return idx, w, block_counts
 
 
-def dispatch_workspace_bytes(sh: MoeShape, e_begin=0, e_end=None) -> int:
-    e_end = sh.E if e_end is None else e_end
-    return lib().moe_dispatch_workspace_size(ctypes.byref(sh), e_begin, e_end)
-
-
 def dispatch(sh: MoeShape, idx: torch.Tensor, block_counts: torch.Tensor, x: torch.Tensor,
              e_begin: int = 0, e_end: Optional[int] = None, out_dtype: Optional[int] = None,
              bufs: Optional[dict] = None) -> dict:
@@ -168,8 +181,8 @@ def dispatch(sh: MoeShape, idx: torch.Tensor, block_counts: torch.Tensor, x: tor
         b["xp"] = torch.empty((rows, d), dtype=_TORCH[out_dtype], device=dev)
         b["xp_scale"] = (torch.empty((d // MOE_FP8_TILE, rows), dtype=torch.float32, device=dev)
                          if out_dtype == MOE_E4M3 else None)
-        wsb = dispatch_workspace_bytes(sh, e_begin, e_end)
-        b["ws"] = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
+        wsb = workspace_bytes(MOE_OP_DISPATCH, sh, out_dtype)
+        b["ws"] = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
     _need(b["counts"], n, "counts")
     _need(b["offsets"], n + 1, "offsets")
     _need(b["dest"], T * k, "dest")
@@ -191,8 +204,11 @@ def dispatch(sh: MoeShape, idx: torch.Tensor, block_counts: torch.Tensor, x: tor
 def expert_ffn(offsets: torch.Tensor, max_rows: int, xp: Optional[torch.Tensor], w13, w2,
                dtype: Optional[int] = None, xp_scale=None, w13_scale=None, w2_scale=None,
                h: Optional[torch.Tensor] = None, h_scale=None, yp: Optional[torch.Tensor] = None,
-               stages: int = MOE_FFN_ALL, d: Optional[int] = None, d_ff: Optional[int] = None):
-    """Grouped SwiGLU experts over rows [offsets[i], offsets[i+1]) of xp."""
+               stages: int = MOE_FFN_ALL, d: Optional[int] = None, d_ff: Optional[int] = None,
+               ws: Optional[torch.Tensor] = None):
+    """Grouped SwiGLU experts over rows [offsets[i], offsets[i+1]) of xp.
+    ws: the call's ticket-counter workspace (workspace(MOE_OP_EXPERT_FFN, ...):
+    zero-filled once, left zero by every call); a fresh one when None."""
     n_exp = offsets.numel() - 1
     ref = w13 if w13 is not None else w2
     dtype = _dt(ref) if dtype is None else dtype
@@ -216,9 +232,11 @@ def expert_ffn(offsets: torch.Tensor, max_rows: int, xp: Optional[torch.Tensor],
         _need(w2, n_exp * d * d_ff, "w2")
         _need(yp, max_rows * d, "yp")
     _need(h, max_rows * d_ff, "h")
+    if ws is None:
+        ws = workspace(MOE_OP_EXPERT_FFN, None, dtype, dev)
     st = lib().moe_expert_ffn(n_exp, _ptr(offsets), max_rows, d, d_ff, dtype, _ptr(xp), _ptr(xp_scale),
                               _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(h),
-                              _ptr(h_scale), _ptr(yp), stages, _stream())
+                              _ptr(h_scale), _ptr(yp), stages, _ptr(ws), _ws_len(ws), _stream())
     _lib.check("moe_expert_ffn", st)
     return yp, h, h_scale
 
@@ -304,6 +322,9 @@ def _ffn_bwd_ws(b: dict, max_rows: int, n_exp: int, d: int, d_ff: int, dev):
         b["d_xp"] = torch.empty((max_rows, d), dtype=bf, device=dev)
         b["dw13"] = torch.empty((n_exp, 2 * d_ff, d), dtype=torch.float32, device=dev)
         b["dw2"] = torch.empty((n_exp, d, d_ff), dtype=torch.float32, device=dev)
+    if "tickets" not in b:
+        b["tickets"] = workspace(MOE_OP_EXPERT_FFN, None, MOE_BF16, dev)
+        b["tickets_bwd"] = workspace(MOE_OP_EXPERT_FFN_BACKWARD, None, MOE_BF16, dev)
     return b
 
 
@@ -317,7 +338,8 @@ def expert_ffn_train(offsets: Optional[torch.Tensor], max_rows: int, xp, w13, w2
     _need(h, max_rows * d_ff, "h")
     _need(yp, max_rows * d, "yp")
     st = lib().moe_expert_ffn_train(n_exp, _ptr(offsets), max_rows, d, d_ff, _dt(xp), _ptr(xp), _ptr(w13), _ptr(w2),
-                                    _ptr(h), _ptr(ws["au"]), _ptr(yp), _stream())
+                                    _ptr(h), _ptr(ws["au"]), _ptr(yp), _ptr(ws["tickets"]), _ws_len(ws["tickets"]),
+                                    _stream())
     _lib.check("moe_expert_ffn_train", st)
     return yp, h
 
@@ -344,7 +366,8 @@ def expert_ffn_backward(offsets: Optional[torch.Tensor], max_rows: int, xp, w13,
     st = lib().moe_expert_ffn_backward(n_exp, _ptr(offsets), max_rows, d, d_ff, _dt(xp), _ptr(xp), _ptr(w13),
                                        _ptr(w2), _ptr(d_yp), _ptr(b["au"]), _ptr(b["h"]), _ptr(b["d_au"]),
                                        _ptr(b["d_xp"]), _ptr(b["dw13"]), _ptr(b["dw2"]),
-                                       MOE_BWD_AU_SAVED if au_saved else 0, _stream())
+                                       MOE_BWD_AU_SAVED if au_saved else 0, _ptr(b["tickets_bwd"]),
+                                       _ws_len(b["tickets_bwd"]), _stream())
     _lib.check("moe_expert_ffn_backward", st)
     return b
 
@@ -387,12 +410,12 @@ def route_backward(sh: MoeShape, x, w_gate, logits, idx, d_w, dx, logit_offset=N
     _need(dx, T * d, "dx")
     _need(dw_gate, d * E, "dw_gate")
     _need(logit_offset, E, "logit_offset")
-    wsb = lib().moe_route_backward_workspace_size(ctypes.byref(sh))
+    wsb = workspace_bytes(MOE_OP_ROUTE_BACKWARD, sh, _dt(x))
     if ws is None and wsb > 0:
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     st = lib().moe_route_backward(ctypes.byref(sh), _ptr(x), _dt(x), _ptr(w_gate), _ptr(logit_offset), _ptr(logits),
                                   _ptr(idx), _ptr(d_w), _ptr(dlogits), _ptr(dx), _ptr(dw_gate), _ptr(ws),
-                                  0 if ws is None else ws.numel() * ws.element_size(), _stream())
+                                  _ws_len(ws), _stream())
     _lib.check("moe_route_backward", st)
     return dlogits, dw_gate
 

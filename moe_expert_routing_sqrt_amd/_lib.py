@@ -21,6 +21,8 @@ MOE_ROUTE_LOGITS_IN = 1
 MOE_FFN_UP, MOE_FFN_DOWN, MOE_FFN_ALL = 1, 2, 3
 MOE_ROUTE_BLOCK = 64
 MOE_FP8_TILE = 128
+MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE = 1, 2, 3, 4
+MOE_OP_ROUTE_BACKWARD, MOE_OP_EXPERT_FFN_BACKWARD = 5, 6
 
 
 class MoeShape(ctypes.Structure):
@@ -45,13 +47,12 @@ _INT = ctypes.c_int
 SIGNATURES = {
     "moe_abi_version": (_INT, []),
     "moe_status_str": (ctypes.c_char_p, [_INT]),
-    "moe_gate_prepare": (_INT, [_I32, _I32, _P, _P, _P]),
-    "moe_route": (_INT, [ctypes.POINTER(MoeShape), _P, _INT, _P, _P, _P, _P, _P, _P, _P, _INT, _P]),
-    "moe_dispatch_workspace_size": (_SZ, [ctypes.POINTER(MoeShape), _I32, _I32]),
+    "moe_workspace_size": (_SZ, [_INT, ctypes.POINTER(MoeShape), _INT]),
+    "moe_route": (_INT, [ctypes.POINTER(MoeShape), _P, _INT, _P, _P, _P, _P, _P, _P, _P, _INT, _P, _SZ, _P]),
     "moe_dispatch": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _I32, _I32, _P, _INT, _INT,
                             _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_expert_ffn": (_INT, [_I32, _P, _I64, _I32, _I32, _INT, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                              _INT, _P]),
+                              _INT, _P, _SZ, _P]),
     "moe_combine": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _P, _INT, _P, _P, _INT, _INT, _P]),
     "moe_quantize_blocks_e4m3": (_INT, [_I64, _I32, _I32, _P, _P, _P, _P]),
     "moe_quantize_rows_e4m3": (_INT, [_I64, _I32, _P, _P, _P, _P]),
@@ -59,12 +60,11 @@ SIGNATURES = {
     "moe_route_hash": (_INT, [ctypes.POINTER(MoeShape), _P, ctypes.c_uint64, _P, _P, _P, _P, _P]),
     "moe_combine_backward": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _P, _INT, _P, _INT, _P, _P, _P]),
     "moe_expert_ffn_backward": (_INT, [_I32, _P, _I64, _I32, _I32, _INT, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                       _P, _INT, _P]),
-    "moe_expert_ffn_train": (_INT, [_I32, _P, _I64, _I32, _I32, _INT, _P, _P, _P, _P, _P, _P, _P]),
+                                       _P, _INT, _P, _SZ, _P]),
+    "moe_expert_ffn_train": (_INT, [_I32, _P, _I64, _I32, _I32, _INT, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_dispatch_backward": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _INT, _P, _P, _INT, _P]),
     "moe_route_backward": (_INT, [ctypes.POINTER(MoeShape), _P, _INT, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
-    "moe_route_backward_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MoeShape)]),
 }
 
 _lib = None

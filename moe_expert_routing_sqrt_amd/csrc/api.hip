@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <cstdint>
 
 #include "common.h"
 #include "launch.h"
@@ -31,6 +32,16 @@ int check_shape(const moe_shape* s) {
 }
 
 bool is_dtype(int t) { return t == MOE_F32 || t == MOE_BF16 || t == MOE_E4M3; }
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) == 0; }
+
+// ticket counter sets at the start of a workspace (one per persistent launch
+// of a call), 256-byte aligned
+constexpr size_t kTicketSetBytes = (kTicketBytes + 255) / 256 * 256;
+int* ticket_set(void* ws, int i) {
+  return reinterpret_cast<int*>(static_cast<char*>(ws) + static_cast<size_t>(i) * kTicketSetBytes);
+}
 
 }  // namespace
 
@@ -64,37 +75,48 @@ const char* moe_status_str(int status) {
   }
 }
 
-int moe_gate_prepare(int32_t d, int32_t E, const float* w_gate, void* w_prep, moe_stream_t stream) {
-  if (d <= 0 || E <= 0 || w_gate == nullptr || w_prep == nullptr) return MOE_ERR_INVALID_ARG;
-  return hip_status(launch_gate_prepare(d, E, w_gate, static_cast<uint16_t*>(w_prep), as_stream(stream)));
+// route workspace: the gate weight's three bf16 planes [3, E, d], then (when
+// the caller passes no logits buffer) the logits [T, E] fp32
+static size_t route_planes_bytes(const moe_shape* s) {
+  return align256(static_cast<size_t>(3) * s->E * s->d * sizeof(uint16_t));
+}
+static size_t route_ws_bytes(const moe_shape* s, bool logits_in_ws) {
+  return route_planes_bytes(s) + (logits_in_ws ? align256(static_cast<size_t>(s->T) * s->E * sizeof(float)) : 0);
 }
 
-int moe_route(const moe_shape* shape, const void* x, int x_dtype, const void* w_prep,
+int moe_route(const moe_shape* shape, const void* x, int x_dtype, const float* w_gate,
               const float* bias, const float* logit_offset, float* logits, int32_t* topk_idx,
-              float* topk_w, int32_t* block_counts, int flags, moe_stream_t stream) {
+              float* topk_w, int32_t* block_counts, int flags, void* ws, size_t ws_bytes,
+              moe_stream_t stream) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   const bool logits_in = (flags & MOE_ROUTE_LOGITS_IN) != 0;
   if ((flags & ~MOE_ROUTE_LOGITS_IN) != 0) return MOE_ERR_INVALID_ARG;
-  if (bias == nullptr || logits == nullptr || topk_idx == nullptr || topk_w == nullptr ||
-      block_counts == nullptr)
+  if (bias == nullptr || topk_idx == nullptr || topk_w == nullptr || block_counts == nullptr)
     return MOE_ERR_INVALID_ARG;
+  if (logits_in && logits == nullptr) return MOE_ERR_INVALID_ARG;
   if (!logits_in) {
-    if (x == nullptr || w_prep == nullptr) return MOE_ERR_INVALID_ARG;
+    if (x == nullptr || w_gate == nullptr) return MOE_ERR_INVALID_ARG;
     if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   }
   if (!route_select_supported(shape->E, shape->G, shape->k, shape->group_topk))
     return MOE_ERR_UNSUPPORTED;
+  if (!logits_in) {
+    if (ws == nullptr || ws_bytes < route_ws_bytes(shape, logits == nullptr) || !aligned256(ws))
+      return MOE_ERR_WORKSPACE;
+  }
   if (shape->T == 0) return MOE_OK;
   hipStream_t s = as_stream(stream);
   if (!logits_in) {
-    hipError_t e;
+    uint16_t* planes = static_cast<uint16_t*>(ws);
+    if (logits == nullptr)
+      logits = reinterpret_cast<float*>(static_cast<char*>(ws) + route_planes_bytes(shape));
+    hipError_t e = launch_gate_prepare(shape->d, shape->E, w_gate, planes, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
     if (x_dtype == MOE_BF16 && gate_gemm_bf16_supported(shape->d, shape->E))
-      e = launch_gate_gemm_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_prep),
-                                logits, shape->T, shape->d, shape->E, s);
+      e = launch_gate_gemm_bf16(static_cast<const uint16_t*>(x), planes, logits, shape->T, shape->d, shape->E, s);
     else
-      e = launch_gate_gemm_simt(x, x_dtype, static_cast<const uint16_t*>(w_prep), logits, shape->T,
-                                shape->d, shape->E, s);
+      e = launch_gate_gemm_simt(x, x_dtype, planes, logits, shape->T, shape->d, shape->E, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return hip_status(launch_route_select(logits, bias, logit_offset, topk_idx, topk_w, block_counts,
@@ -102,9 +124,8 @@ int moe_route(const moe_shape* shape, const void* x, int x_dtype, const void* w_
                                         shape->group_topk, s));
 }
 
-// dispatch workspace: per-(block, expert) base rows, then (when d % 128 == 0,
-// for the e4m3 output) the token-major scale table [d/128][T] at a 256-byte
-// aligned offset
+// dispatch workspace: per-(block, expert) base rows, then (for the e4m3
+// output) the token-major scale table [d/128][T] at a 256-byte aligned offset
 static size_t dispatch_base_bytes(const moe_shape* shape, int32_t e_begin, int32_t e_end) {
   const int64_t nblk = (shape->T + MOE_ROUTE_BLOCK - 1) / MOE_ROUTE_BLOCK;
   return static_cast<size_t>(nblk) * static_cast<size_t>(e_end - e_begin) * sizeof(int32_t);
@@ -113,9 +134,9 @@ static size_t dispatch_scale_offset(const moe_shape* shape, int32_t e_begin, int
   return (dispatch_base_bytes(shape, e_begin, e_end) + 255) / 256 * 256;
 }
 
-size_t moe_dispatch_workspace_size(const moe_shape* shape, int32_t e_begin, int32_t e_end) {
+static size_t dispatch_ws_bytes(const moe_shape* shape, int32_t e_begin, int32_t e_end, int out_dtype) {
   if (check_shape(shape) != MOE_OK || e_begin < 0 || e_end < e_begin || e_end > shape->E) return 0;
-  if (shape->d % MOE_FP8_TILE != 0) return dispatch_base_bytes(shape, e_begin, e_end);
+  if (out_dtype != MOE_E4M3 || shape->d % MOE_FP8_TILE != 0) return dispatch_base_bytes(shape, e_begin, e_end);
   return dispatch_scale_offset(shape, e_begin, e_end) +
          static_cast<size_t>(shape->d / MOE_FP8_TILE) * static_cast<size_t>(shape->T) * sizeof(float);
 }
@@ -142,7 +163,7 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const int32_t*
   const int elem = x_dtype == MOE_F32 ? 4 : 2;
   if ((shape->d * elem) % 16 != 0) return MOE_ERR_UNSUPPORTED;  // 16-byte row chunks
   if (e_end - e_begin > 256 || shape->k > 16) return MOE_ERR_UNSUPPORTED;
-  if (ws == nullptr || ws_bytes < moe_dispatch_workspace_size(shape, e_begin, e_end))
+  if (ws == nullptr || ws_bytes < dispatch_ws_bytes(shape, e_begin, e_end, out_dtype) || !aligned256(ws))
     return MOE_ERR_WORKSPACE;
   if (shape->T == 0) return MOE_OK;
   float* tok_scale = out_dtype == MOE_E4M3
@@ -158,7 +179,7 @@ int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int3
                    int32_t d_ff, int dtype, const void* xp, const float* xp_scale,
                    const void* w13, const float* w13_scale, const void* w2,
                    const float* w2_scale, void* h, float* h_scale, void* yp, int stages,
-                   moe_stream_t stream) {
+                   void* ws, size_t ws_bytes, moe_stream_t stream) {
   if (n_exp <= 0 || n_exp > kMaxExperts || offsets == nullptr || max_rows < 0 || d <= 0 ||
       d_ff <= 0 || h == nullptr)
     return MOE_ERR_INVALID_ARG;
@@ -173,22 +194,25 @@ int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int3
       return MOE_ERR_INVALID_ARG;
     if (d % 256 != 0 || d_ff % 128 != 0) return MOE_ERR_UNSUPPORTED;
   }
+  if (ws == nullptr || ws_bytes < 2 * kTicketSetBytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
   if (max_rows == 0) return MOE_OK;
   hipStream_t s = as_stream(stream);
   const bool mfma = dtype == MOE_BF16 && d % 256 == 0 && d_ff % 128 == 0 && d_ff >= 256;
+  int* const tick_up = ticket_set(ws, 0);
+  int* const tick_down = ticket_set(ws, 1);
   if (up) {
     hipError_t e;
     if (dtype == MOE_E4M3 && ffn_fp8p_supported_k(d))
       e = launch_ffn_up_fp8p(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint8_t*>(xp),
                              xp_scale, static_cast<const uint8_t*>(w13), w13_scale,
-                             static_cast<uint8_t*>(h), h_scale, s);
+                             static_cast<uint8_t*>(h), h_scale, tick_up, s);
     else if (dtype == MOE_E4M3)
       e = launch_ffn_up_fp8(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint8_t*>(xp),
                             xp_scale, static_cast<const uint8_t*>(w13), w13_scale,
                             static_cast<uint8_t*>(h), h_scale, s);
     else if (mfma)
       e = launch_ffn_up_bf16(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint16_t*>(xp),
-                             static_cast<const uint16_t*>(w13), static_cast<uint16_t*>(h), s);
+                             static_cast<const uint16_t*>(w13), static_cast<uint16_t*>(h), tick_up, s);
     else
       e = launch_ffn_simt(MOE_FFN_UP, n_exp, offsets, max_rows, d, d_ff, dtype, xp, w13, h, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
@@ -198,14 +222,14 @@ int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int3
     if (dtype == MOE_E4M3 && ffn_fp8p_supported_k(d_ff))
       e = launch_ffn_down_fp8p(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint8_t*>(h),
                                h_scale, static_cast<const uint8_t*>(w2), w2_scale,
-                               static_cast<uint16_t*>(yp), s);
+                               static_cast<uint16_t*>(yp), tick_down, s);
     else if (dtype == MOE_E4M3)
       e = launch_ffn_down_fp8(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint8_t*>(h),
                               h_scale, static_cast<const uint8_t*>(w2), w2_scale,
                               static_cast<uint16_t*>(yp), s);
     else if (mfma)
       e = launch_ffn_down_bf16(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint16_t*>(h),
-                               static_cast<const uint16_t*>(w2), static_cast<uint16_t*>(yp), s);
+                               static_cast<const uint16_t*>(w2), static_cast<uint16_t*>(yp), tick_down, s);
     else
       e = launch_ffn_simt(MOE_FFN_DOWN, n_exp, offsets, max_rows, d, d_ff, dtype, h, w2, yp, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
@@ -264,26 +288,28 @@ int moe_combine_backward(const moe_shape* shape, const int32_t* dest, const floa
 
 int moe_expert_ffn_train(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int32_t d, int32_t d_ff,
                          int dtype, const void* xp, const void* w13, const void* w2, void* h, void* au, void* yp,
-                         moe_stream_t stream) {
+                         void* ws, size_t ws_bytes, moe_stream_t stream) {
   if (n_exp < 1 || n_exp > kMaxExperts || max_rows < 0 || d < 1 || d_ff < 1) return MOE_ERR_INVALID_ARG;
   if (dtype != MOE_BF16 || !ffn_bwd_bf16_supported(d, d_ff)) return MOE_ERR_UNSUPPORTED;
   if (offsets == nullptr && n_exp != 1) return MOE_ERR_INVALID_ARG;
   if (xp == nullptr || w13 == nullptr || w2 == nullptr || h == nullptr || au == nullptr || yp == nullptr)
     return MOE_ERR_INVALID_ARG;
+  if (ws == nullptr || ws_bytes < 2 * kTicketSetBytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
   if (max_rows == 0) return MOE_OK;
   const hipStream_t s = as_stream(stream);
   hipError_t e = launch_ffn_up_bf16(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint16_t*>(xp),
-                                    static_cast<const uint16_t*>(w13), static_cast<uint16_t*>(h), s,
-                                    static_cast<uint16_t*>(au));
+                                    static_cast<const uint16_t*>(w13), static_cast<uint16_t*>(h), ticket_set(ws, 0),
+                                    s, static_cast<uint16_t*>(au));
   if (e != hipSuccess) return hip_status(e);
   return hip_status(launch_ffn_down_bf16(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint16_t*>(h),
-                                         static_cast<const uint16_t*>(w2), static_cast<uint16_t*>(yp), s));
+                                         static_cast<const uint16_t*>(w2), static_cast<uint16_t*>(yp),
+                                         ticket_set(ws, 1), s));
 }
 
 int moe_expert_ffn_backward(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int32_t d, int32_t d_ff,
                             int dtype, const void* xp, const void* w13, const void* w2, const void* d_yp,
                             void* au, void* h, void* d_au, void* d_xp, float* dw13, float* dw2, int flags,
-                            moe_stream_t stream) {
+                            void* ws, size_t ws_bytes, moe_stream_t stream) {
   if (n_exp < 1 || n_exp > kMaxExperts || max_rows < 0 || d < 1 || d_ff < 1) return MOE_ERR_INVALID_ARG;
   if ((flags & ~MOE_BWD_AU_SAVED) != 0) return MOE_ERR_INVALID_ARG;
   if (dtype != MOE_BF16 || !ffn_bwd_bf16_supported(d, d_ff)) return MOE_ERR_UNSUPPORTED;
@@ -291,6 +317,7 @@ int moe_expert_ffn_backward(int32_t n_exp, const int32_t* offsets, int64_t max_r
   if (xp == nullptr || w13 == nullptr || w2 == nullptr || d_yp == nullptr || au == nullptr || h == nullptr ||
       d_au == nullptr || d_xp == nullptr || dw13 == nullptr || dw2 == nullptr)
     return MOE_ERR_INVALID_ARG;
+  if (ws == nullptr || ws_bytes < kTicketSetBytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
   const hipStream_t s = as_stream(stream);
   const auto* X = static_cast<const uint16_t*>(xp);
   const auto* W13 = static_cast<const uint16_t*>(w13);
@@ -303,7 +330,8 @@ int moe_expert_ffn_backward(int32_t n_exp, const int32_t* offsets, int64_t max_r
   // [a | u] (kept by moe_expert_ffn_train, else recomputed), d_h = d_y W2,
   // then SwiGLU's derivative (h on the side)
   if (!(flags & MOE_BWD_AU_SAVED) &&
-      (e = launch_ffn_store_bf16(n_exp, offsets, max_rows, d, 2 * d_ff, X, W13, AU, s)) != hipSuccess)
+      (e = launch_ffn_store_bf16(n_exp, offsets, max_rows, d, 2 * d_ff, X, W13, AU, ticket_set(ws, 0), s)) !=
+          hipSuccess)
     return hip_status(e);
   if ((e = launch_ffn_dgrad_bf16(n_exp, offsets, max_rows, d, d_ff, DY, W2, H, s)) != hipSuccess)
     return hip_status(e);
@@ -331,11 +359,6 @@ int moe_dispatch_backward(const moe_shape* shape, const int32_t* dest, const voi
                                    MOE_F32, accumulate, as_stream(stream)));
 }
 
-size_t moe_route_backward_workspace_size(const moe_shape* shape) {
-  if (shape == nullptr || shape->T <= 0 || shape->d < 1 || shape->E < 1) return 0;
-  return gate_bwd_workspace_bytes(shape->T, shape->d, shape->E);
-}
-
 int moe_route_backward(const moe_shape* shape, const void* x, int x_dtype, const float* w_gate,
                        const float* logit_offset, const float* logits, const int32_t* topk_idx,
                        const float* d_topk_w, float* dlogits, float* dx, float* dw_gate, void* ws,
@@ -349,7 +372,7 @@ int moe_route_backward(const moe_shape* shape, const void* x, int x_dtype, const
       dlogits == nullptr || dx == nullptr || dw_gate == nullptr)
     return MOE_ERR_INVALID_ARG;
   const size_t need = gate_bwd_workspace_bytes(shape->T, shape->d, shape->E);
-  if (need > 0 && (ws == nullptr || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned256(ws))) return MOE_ERR_WORKSPACE;
   return hip_status(launch_gate_bwd(shape->T, shape->d, shape->E, shape->k, x, x_dtype, w_gate, logits,
                                     logit_offset, topk_idx, d_topk_w, dlogits, dx, dw_gate,
                                     static_cast<float*>(ws), as_stream(stream)));
@@ -374,6 +397,28 @@ int moe_bias_update(int64_t n_rows, int32_t E, const int32_t* counts, float gamm
   if (n_rows == 0) return MOE_OK;
   if (counts == nullptr || bias == nullptr) return MOE_ERR_INVALID_ARG;
   return hip_status(launch_bias_update(n_rows, E, counts, gamma, bias, load, as_stream(stream)));
+}
+
+size_t moe_workspace_size(int op, const moe_shape* shape, int dtype) {
+  switch (op) {
+    case MOE_OP_ROUTE:
+      if (check_shape(shape) != MOE_OK) return 0;
+      return route_ws_bytes(shape, true);
+    case MOE_OP_DISPATCH:
+      if (check_shape(shape) != MOE_OK) return 0;
+      return dispatch_ws_bytes(shape, 0, shape->E, dtype);
+    case MOE_OP_EXPERT_FFN:
+      return 2 * kTicketSetBytes;
+    case MOE_OP_COMBINE:
+      return 0;
+    case MOE_OP_ROUTE_BACKWARD:
+      if (shape == nullptr || shape->T <= 0 || shape->d < 1 || shape->E < 1) return 0;
+      return gate_bwd_workspace_bytes(shape->T, shape->d, shape->E);
+    case MOE_OP_EXPERT_FFN_BACKWARD:
+      return kTicketSetBytes;
+    default:
+      return 0;
+  }
 }
 
 }  // extern "C"

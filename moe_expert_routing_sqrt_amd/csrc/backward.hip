@@ -276,9 +276,12 @@ __device__ __forceinline__ void planes3(float v, uint16_t& hi, uint16_t& mid, ui
 // dL [T, E] -> a6 [T, 6E] = [hi | hi | mid | hi | lo | mid] and p3 [T, ld3] =
 // [hi | mid | lo | zero padding]; one thread per (row, column < E + ld3 - 3E)
 __global__ __launch_bounds__(256) void dl_planes_kernel(const float* __restrict__ dl, int64_t T, int E, int ld3,
-                                                        uint16_t* __restrict__ a6, uint16_t* __restrict__ p3) {
+                                                        uint16_t* __restrict__ a6, uint16_t* __restrict__ p3,
+                                                        int* __restrict__ tickets) {
   const int cols = E + (ld3 - 3 * E);
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.x == 0 && threadIdx.x < kTicketInts / kTicketStride)
+    tickets[threadIdx.x * kTicketStride] = 0;  // the ticket counters of the next product
   if (i >= T * cols) return;
   const int64_t t = i / cols;
   const int c = static_cast<int>(i % cols);
@@ -383,7 +386,7 @@ bool gate_bwd_mfma(int d, int E, int x_dtype) { return x_dtype == MOE_BF16 && d 
 
 struct GateMfmaWs {
   int ld3, splits, split_rows;
-  size_t a6, w6, p3, part, total;  // byte offsets into the workspace
+  size_t a6, w6, p3, part, tick, total;  // byte offsets into the workspace
 };
 
 GateMfmaWs gate_mfma_ws(int64_t T, int d, int E) {
@@ -397,7 +400,8 @@ GateMfmaWs gate_mfma_ws(int64_t T, int d, int E) {
   w.w6 = up(w.a6 + (size_t)T * 6 * E * 2);
   w.p3 = up(w.w6 + (size_t)d * 6 * E * 2);
   w.part = up(w.p3 + (size_t)T * w.ld3 * 2);
-  w.total = w.part + (size_t)w.splits * d * w.ld3 * 4;
+  w.tick = up(w.part + (size_t)w.splits * d * w.ld3 * 4);
+  w.total = w.tick + kTicketBytes;
   return w;
 }
 
@@ -425,15 +429,17 @@ hipError_t launch_gate_bwd(int64_t T, int d, int E, int k, const void* x, int x_
     uint16_t* w6 = reinterpret_cast<uint16_t*>(base + w.w6);
     uint16_t* p3 = reinterpret_cast<uint16_t*>(base + w.p3);
     float* part = reinterpret_cast<float*>(base + w.part);
+    int* tick = reinterpret_cast<int*>(base + w.tick);
     const int64_t n1 = T * (E + (w.ld3 - 3 * E));
+    // (the first work-group also clears the ticket counters of the dx product)
     hipLaunchKernelGGL(dl_planes_kernel, dim3(static_cast<unsigned>((n1 + 255) / 256)), dim3(256), 0, s, dL, T, E,
-                       w.ld3, a6, p3);
+                       w.ld3, a6, p3, tick);
     const int64_t n2 = (int64_t)d * E;
     hipLaunchKernelGGL(w_planes_kernel, dim3(static_cast<unsigned>((n2 + 255) / 256)), dim3(256), 0, s, w_gate, d,
                        E, w6);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // dx[t][c] += sum over K' = 6E of a6[t][k'] w6[c][k']
-    if ((e = launch_gemm_acc_f32(T, 6 * E, d, a6, w6, dx, s)) != hipSuccess) return e;
+    if ((e = launch_gemm_acc_f32(T, 6 * E, d, a6, w6, dx, tick, s)) != hipSuccess) return e;
     // partials[z][c][k] = sum over split z's rows t of x[t][c] p3[t][k]
     if ((e = launch_ffn_wgrad_bf16(0, nullptr, T, d, w.ld3, static_cast<const uint16_t*>(x), p3, part, s,
                                    w.split_rows)) != hipSuccess)

@@ -12,6 +12,16 @@ constexpr int kWave = 64;
 constexpr int kMaxExperts = 1024;  // per moe_expert_ffn call
 constexpr int kXcds = 8;           // MI355X: 8 accelerator complex dies, 32 CUs each
 
+// Ticket counters of one persistent grouped-GEMM launch: one tile counter per
+// XCD and a retire counter, each on its own 64-byte line, in caller-owned
+// device memory.  They must be zero when the launch starts; the last
+// work-group to retire sets them back to zero, so a set can serve the next
+// launch on the same stream.  Launches that may run at the same time need
+// distinct sets.
+constexpr int kTicketStride = 16;  // ints between counters
+constexpr int kTicketInts = (kXcds + 1) * kTicketStride;
+constexpr size_t kTicketBytes = kTicketInts * sizeof(int);
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -36,9 +36,8 @@
 // and the tile map is built once per work-group.  The epilogue stages each
 // wave's output through a private 2 KB LDS slot, 8 rows at a time, so it never
 // touches the stages that already hold the next tile.  The ticket counters
-// live in a small device array; the last work-group to retire clears them,
-// and each launch takes the next of 16 counter sets, so launches on different
-// streams do not share one (up to 16 concurrently running launches).
+// are a caller-owned set (common.h: zero at launch, cleared by the last
+// work-group to retire).
 //
 // Ragged groups: a tile covers up to 256 rows of one expert.  Wave row wm owns
 // the 32-row blocks at rows 32*wm and 128 + 32*wm, so the two waves sharing a
@@ -53,7 +52,6 @@
 // weight rows are 128 gate rows (W1) and the matching 128 up rows (W3), and
 // each wave holds the gate and up accumulators of the same 64 features.
 #include <algorithm>
-#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -89,12 +87,7 @@ static_assert(NW % 2 == 0, "a wave's DMA blocks share the swizzle parity");
 constexpr int ST_PITCH = TN * 2 + 16;   // bytes; 17 chunks of 16, so rows start on different banks
 constexpr int ST_BYTES = 8 * ST_PITCH;
 
-// ticket counters: kSlots sets of kXcds counters plus a retire counter, each
-// on its own 64-byte line
-constexpr int kSlots = 16;
-constexpr int kCtrStride = 16;
-constexpr int kSlotInts = (kXcds + 1) * kCtrStride;
-__device__ int g_tickets[kSlots * kSlotInts];
+constexpr int kCtrStride = kTicketStride;
 
 // SAVE: also [a | u]; ACC_F32: C (fp32) += A B^T, one group
 enum { MODE_SWIGLU = 0, MODE_STORE = 1, MODE_SWIGLU_SAVE = 2, MODE_ACC_F32 = 3 };
@@ -114,7 +107,7 @@ struct FfnArgs {
   int d_ff;                // SWIGLU: first up-projection row of w13
   uint16_t* C2;            // SWIGLU_SAVE: [a | u] output [rows, 2*d_ff]
   float* Cf;               // ACC_F32: fp32 output [rows, ldc], accumulated into
-  int slot;                // ticket counter set of this launch
+  int* tickets;            // this launch's ticket counter set (kTicketInts, zero)
 };
 
 __device__ __forceinline__ void uniform_tile(TileInfo& t) {
@@ -154,7 +147,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
   const int xcd = blockIdx.x % kXcds;
-  int* const tickets = g_tickets + p.slot * kSlotInts;
+  int* const tickets = p.tickets;
 
   const int n_grp = tile_map_build(p.offsets, p.n_exp, p.rows_total, BM, s_map);
   const int total = s_map[n_grp] * p.n_tiles;
@@ -564,8 +557,6 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
 #endif
 }
 
-std::atomic<unsigned> g_launches{0};
-
 template <int MODE>
 hipError_t launch(FfnArgs& a, int64_t max_rows, hipStream_t s) {
   if (a.K % (2 * BK) != 0 || a.K < 4 * BK) return hipErrorInvalidValue;
@@ -578,7 +569,7 @@ hipError_t launch(FfnArgs& a, int64_t max_rows, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
   // one work-group per CU (the LDS holds one), a multiple of the XCD count
   const int64_t grid = (std::min<int64_t>(tiles, device_cu_count()) + kXcds - 1) / kXcds * kXcds;
-  a.slot = static_cast<int>(g_launches.fetch_add(1, std::memory_order_relaxed) % kSlots);
+  if (a.tickets == nullptr) return hipErrorInvalidValue;
   hipLaunchKernelGGL((ffn_gemm_kernel<MODE>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -587,8 +578,9 @@ hipError_t launch(FfnArgs& a, int64_t max_rows, hipStream_t s) {
 
 hipError_t launch_ffn_up_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
                               int d_ff, const uint16_t* xp, const uint16_t* w13, uint16_t* h,
-                              hipStream_t s, uint16_t* au) {
+                              int* tickets, hipStream_t s, uint16_t* au) {
   FfnArgs a{};
+  a.tickets = tickets;
   a.A = xp;
   a.lda = d;
   a.B = w13;
@@ -607,8 +599,10 @@ hipError_t launch_ffn_up_bf16(int n_exp, const int32_t* offsets, int64_t max_row
 }
 
 hipError_t launch_ffn_store_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int K, int N,
-                                 const uint16_t* A, const uint16_t* B, uint16_t* C, hipStream_t s) {
+                                 const uint16_t* A, const uint16_t* B, uint16_t* C, int* tickets,
+                                 hipStream_t s) {
   FfnArgs a{};
+  a.tickets = tickets;
   a.A = A;
   a.lda = K;
   a.B = B;
@@ -624,8 +618,9 @@ hipError_t launch_ffn_store_bf16(int n_exp, const int32_t* offsets, int64_t max_
 }
 
 hipError_t launch_gemm_acc_f32(int64_t rows, int K, int N, const uint16_t* A, const uint16_t* B, float* C,
-                               hipStream_t s) {
+                               int* tickets, hipStream_t s) {
   FfnArgs a{};
+  a.tickets = tickets;
   a.A = A;
   a.lda = K;
   a.B = B;
@@ -641,8 +636,8 @@ hipError_t launch_gemm_acc_f32(int64_t rows, int K, int N, const uint16_t* A, co
 
 hipError_t launch_ffn_down_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
                                 int d_ff, const uint16_t* h, const uint16_t* w2, uint16_t* yp,
-                                hipStream_t s) {
-  return launch_ffn_store_bf16(n_exp, offsets, max_rows, d_ff, d, h, w2, yp, s);
+                                int* tickets, hipStream_t s) {
+  return launch_ffn_store_bf16(n_exp, offsets, max_rows, d_ff, d, h, w2, yp, tickets, s);
 }
 
 }  // namespace moe

@@ -42,7 +42,6 @@
 //           halves meet in LDS; codes = e4m3(h / scale), scale = amax / 448.
 //   STORE   bf16 output through each wave's staging slot.
 #include <algorithm>
-#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -76,10 +75,7 @@ constexpr int ST_BYTES = 8 * ST_PITCH;
 constexpr int H_PITCH = TN / 2 + 16;   // SWIGLU staging: 8 rows of 64 codes
 constexpr int H_BYTES = 8 * H_PITCH;
 
-constexpr int kSlots = 16;
-constexpr int kCtrStride = 16;
-constexpr int kSlotInts = (kXcds + 1) * kCtrStride;
-__device__ int g_tickets_fp8[kSlots * kSlotInts];
+constexpr int kCtrStride = kTicketStride;
 
 enum { MODE_SWIGLU = 0, MODE_STORE = 1 };
 
@@ -101,7 +97,7 @@ struct Fp8Args {
   int K;
   int n_tiles;
   int d_ff;                 // SWIGLU: first up row of w13
-  int slot;
+  int* tickets;             // this launch's ticket counter set (kTicketInts, zero)
 };
 
 typedef int i32x8v __attribute__((ext_vector_type(8)));
@@ -171,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
   const int xcd = blockIdx.x % kXcds;
-  int* const tickets = g_tickets_fp8 + p.slot * kSlotInts;
+  int* const tickets = p.tickets;
 
   const int n_grp = tile_map_build(p.offsets, p.n_exp, p.rows_total, BM, s_map);
   const int total = s_map[n_grp] * p.n_tiles;
@@ -642,8 +638,6 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
 #endif
 }
 
-std::atomic<unsigned> g_launches_fp8{0};
-
 template <int MODE>
 hipError_t launch(Fp8Args& a, int64_t max_rows, hipStream_t s) {
   if (!ffn_fp8p_supported_k(a.K)) return hipErrorInvalidValue;
@@ -653,7 +647,7 @@ hipError_t launch(Fp8Args& a, int64_t max_rows, hipStream_t s) {
   const int64_t tiles = mt * a.n_tiles;
   if (tiles <= 0) return hipSuccess;
   const int64_t grid = (std::min<int64_t>(tiles, device_cu_count()) + kXcds - 1) / kXcds * kXcds;
-  a.slot = static_cast<int>(g_launches_fp8.fetch_add(1, std::memory_order_relaxed) % kSlots);
+  if (a.tickets == nullptr) return hipErrorInvalidValue;
   hipLaunchKernelGGL((ffn_fp8_kernel<MODE>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -664,8 +658,10 @@ bool ffn_fp8p_supported_k(int K) { return K % (2 * BKB) == 0 && K >= 4 * BKB; }
 
 hipError_t launch_ffn_up_fp8p(int n_exp, const int32_t* offsets, int64_t max_rows, int d, int d_ff,
                               const uint8_t* xp, const float* xp_scale, const uint8_t* w13,
-                              const float* w13_scale, uint8_t* h, float* h_scale, hipStream_t s) {
+                              const float* w13_scale, uint8_t* h, float* h_scale, int* tickets,
+                              hipStream_t s) {
   Fp8Args a{};
+  a.tickets = tickets;
   a.A = xp;
   a.A_scale = xp_scale;
   a.lda = d;
@@ -688,8 +684,9 @@ hipError_t launch_ffn_up_fp8p(int n_exp, const int32_t* offsets, int64_t max_row
 
 hipError_t launch_ffn_down_fp8p(int n_exp, const int32_t* offsets, int64_t max_rows, int d, int d_ff,
                                 const uint8_t* h, const float* h_scale, const uint8_t* w2,
-                                const float* w2_scale, uint16_t* yp, hipStream_t s) {
+                                const float* w2_scale, uint16_t* yp, int* tickets, hipStream_t s) {
   Fp8Args a{};
+  a.tickets = tickets;
   a.A = h;
   a.A_scale = h_scale;
   a.lda = d_ff;

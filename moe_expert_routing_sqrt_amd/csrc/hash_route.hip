@@ -11,7 +11,7 @@
 // experts in increasing order, so the work per token is bounded.  Groups play
 // no part.  Gate weights are 1/k, or with logits the renormalised affinities
 // of the chosen experts (w_j = s_j / (((s_0 + s_1) + s_2) + ...)), computed by
-// the same fp32 sequence as the top-k router.
+// the same operation sequence as the top-k router (affinity.h).
 //
 // One thread per token; a work-group of 256 threads covers four 64-token route
 // blocks and writes their rows of the per-block expert histogram.

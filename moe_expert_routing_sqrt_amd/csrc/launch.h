@@ -30,16 +30,18 @@ hipError_t launch_dispatch(const int32_t* idx, const int32_t* block_counts, int6
                            int32_t* dest, int32_t* src, void* xp, float* xp_scale, int32_t* base,
                            float* tok_scale, hipStream_t s);
 
-// grouped expert FFN
+// grouped expert FFN.  `tickets`: a zeroed ticket counter set (kTicketInts
+// ints, common.h) that no concurrently running launch shares
 hipError_t launch_ffn_up_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
                               int d_ff, const uint16_t* xp, const uint16_t* w13, uint16_t* h,
-                              hipStream_t s, uint16_t* au = nullptr);
+                              int* tickets, hipStream_t s, uint16_t* au = nullptr);
 hipError_t launch_ffn_down_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
                                 int d_ff, const uint16_t* h, const uint16_t* w2, uint16_t* yp,
-                                hipStream_t s);
+                                int* tickets, hipStream_t s);
 // C [rows, N] = A [rows, K] x B_g^T with B_g [N, K] per group (plain bf16 store)
 hipError_t launch_ffn_store_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int K, int N,
-                                 const uint16_t* A, const uint16_t* B, uint16_t* C, hipStream_t s);
+                                 const uint16_t* A, const uint16_t* B, uint16_t* C, int* tickets,
+                                 hipStream_t s);
 // backward products (ffn_bwd_bf16.hip)
 bool ffn_bwd_bf16_supported(int d, int d_ff);
 hipError_t launch_ffn_dgrad_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int K, int N,
@@ -50,7 +52,7 @@ hipError_t launch_ffn_wgrad_bf16(int n_exp, const int32_t* offsets, int64_t rows
                                  int split_rows = 0);
 // C [rows, N] fp32 += A [rows, K] B [N, K]^T, bf16 operands (K % 128 == 0, K >= 256, N % 256 == 0)
 hipError_t launch_gemm_acc_f32(int64_t rows, int K, int N, const uint16_t* A, const uint16_t* B, float* C,
-                               hipStream_t s);
+                               int* tickets, hipStream_t s);
 hipError_t launch_ffn_simt(int stage, int n_exp, const int32_t* offsets, int64_t max_rows, int d,
                            int d_ff, int dtype, const void* in, const void* w, void* out,
                            hipStream_t s);
@@ -65,10 +67,11 @@ hipError_t launch_ffn_down_fp8(int n_exp, const int32_t* offsets, int64_t max_ro
 bool ffn_fp8p_supported_k(int K);
 hipError_t launch_ffn_up_fp8p(int n_exp, const int32_t* offsets, int64_t max_rows, int d, int d_ff,
                               const uint8_t* xp, const float* xp_scale, const uint8_t* w13,
-                              const float* w13_scale, uint8_t* h, float* h_scale, hipStream_t s);
+                              const float* w13_scale, uint8_t* h, float* h_scale, int* tickets,
+                              hipStream_t s);
 hipError_t launch_ffn_down_fp8p(int n_exp, const int32_t* offsets, int64_t max_rows, int d, int d_ff,
                                 const uint8_t* h, const float* h_scale, const uint8_t* w2,
-                                const float* w2_scale, uint16_t* yp, hipStream_t s);
+                                const float* w2_scale, uint16_t* yp, int* tickets, hipStream_t s);
 
 // combine
 hipError_t launch_combine(int64_t T, int k, int d, const int32_t* dest, const float* w,

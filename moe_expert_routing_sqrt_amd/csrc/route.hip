@@ -10,11 +10,12 @@
 // 64-bit keys (ordered fp32 bits << 32 | ~index): the largest key is the
 // largest value, ties to the lower index.
 //
-// Every floating-point value is produced by one fixed fp32 operation sequence
-// with no contraction (this file is compiled with -ffp-contract=off,
-// correctly rounded divide and sqrt, and fp32 denormals kept), so the result
-// is a deterministic function of the fp32 logits:
-//   s = sqrt(softplus(l)) by the fixed sequence in affinity.h
+// Every floating-point value is produced by one fixed operation sequence with
+// no contraction (this file is compiled with -ffp-contract=off, correctly
+// rounded divide and sqrt, and fp32 denormals kept), so the result is a
+// deterministic function of the fp32 logits:
+//   s = sqrt(softplus(l)) by the fixed fp64 sequence in affinity.h, rounded
+//       once to fp32 (non-decreasing in l, like the exact function)
 //   b = s + bias
 //   group score = its group_topk largest b added largest first;
 //   keep the M best groups (ties to the lower group), choose the k best b in

@@ -6,15 +6,15 @@ forward(x) = moe_route -> moe_dispatch -> moe_expert_ffn (routed: up, down)
 """
 from __future__ import annotations
 
-import ctypes
 from typing import Optional, Sequence
 
 import torch
 
 from . import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN, MOE_FFN_UP, MOE_FP8_TILE,
-               bias_update, combine, combine_backward, dispatch, dispatch_backward, expert_ffn,
-               expert_ffn_backward, expert_ffn_train, gate_prepare, lib, n_blocks, quantize_blocks_e4m3, quantize_rows_e4m3,
-               route, route_backward, route_hash, shape)
+               MOE_OP_EXPERT_FFN, MOE_OP_ROUTE, MOE_OP_ROUTE_BACKWARD, bias_update, combine, combine_backward,
+               dispatch, dispatch_backward, expert_ffn, expert_ffn_backward, expert_ffn_train, n_blocks,
+               quantize_blocks_e4m3, quantize_rows_e4m3, route, route_backward, route_hash, shape,
+               workspace, workspace_bytes)
 
 STAGES = ("route", "dispatch", "ffn_up", "ffn_down", "shared", "combine")
 
@@ -38,7 +38,13 @@ class MoELayer:
         if router not in ("topk", "hash"):
             raise ValueError("router must be 'topk' or 'hash'")
         self.router, self.hash_seed = router, hash_seed
-        self.w_prep = gate_prepare(w_gate)
+        x_dt = MOE_F32 if dtype == "f32" else MOE_BF16
+        # caller-owned workspaces, one per call site: the route's (gate-weight
+        # planes), and the ticket counters of the routed and shared expert
+        # products (zero-filled once; every call leaves them zero)
+        self.route_ws = workspace(MOE_OP_ROUTE, self.sh, x_dt, dev)
+        self.ffn_ws = workspace(MOE_OP_EXPERT_FFN, None, MOE_BF16, dev)
+        self.sh_ffn_ws = workspace(MOE_OP_EXPERT_FFN, None, MOE_BF16, dev)
 
         # expert weights in the compute format (fp8: e4m3 codes + 128x128 block scales)
         if self.dtype == MOE_E4M3:
@@ -93,7 +99,11 @@ class MoELayer:
         stream around the six stages (STAGES).  With router="hash" the experts
         come from `token_ids` (int32 [T]) and the gate weights are 1/k.
         save_for_backward: the expert FFNs also keep their pre-activations, so
-        backward() does not recompute them (bf16 top-k layer)."""
+        backward() does not recompute them (bf16 top-k layer).
+        With a local expert range (one expert-parallel rank's share) the
+        output is that share in fp32: into self.out (cleared first) when `out`
+        is None, else added to the caller's fp32 `out` (a scatter-add of this
+        rank's share into a buffer that may hold the others')."""
         self._saved = save_for_backward
         if save_for_backward:
             return self._forward_train(x, marks)
@@ -109,8 +119,8 @@ class MoELayer:
             route_hash(sh, token_ids, self.hash_seed, idx=self.idx, w=self.topk_w,
                        block_counts=self.block_counts)
         else:
-            route(sh, x, self.w_prep, self.bias, self.logit_offset, logits=self.logits, idx=self.idx,
-                  w=self.topk_w, block_counts=self.block_counts)
+            route(sh, x, self.w_gate, self.bias, self.logit_offset, logits=self.logits, idx=self.idx,
+                  w=self.topk_w, block_counts=self.block_counts, ws=self.route_ws)
         mark(1)
         self.dbufs = dispatch(sh, self.idx, self.block_counts, x, self.e_begin, self.e_end,
                               out_dtype=self.dtype if self.dtype == MOE_E4M3 else None,
@@ -119,11 +129,11 @@ class MoELayer:
         mark(2)
         expert_ffn(b["offsets"], self.max_rows, b["xp"], self.w13, self.w2, self.dtype,
                    xp_scale=b["xp_scale"], w13_scale=self.w13_s, w2_scale=self.w2_s, h=self.h,
-                   h_scale=self.h_s, yp=self.yp, stages=MOE_FFN_UP)
+                   h_scale=self.h_s, yp=self.yp, stages=MOE_FFN_UP, ws=self.ffn_ws)
         mark(3)
         expert_ffn(b["offsets"], self.max_rows, b["xp"], self.w13, self.w2, self.dtype,
                    xp_scale=b["xp_scale"], w13_scale=self.w13_s, w2_scale=self.w2_s, h=self.h,
-                   h_scale=self.h_s, yp=self.yp, stages=MOE_FFN_DOWN)
+                   h_scale=self.h_s, yp=self.yp, stages=MOE_FFN_DOWN, ws=self.ffn_ws)
         mark(4)
         ysh = None
         if self.has_shared:
@@ -132,10 +142,13 @@ class MoELayer:
                 xs, xs_scale = self._shared_quant_input(x)
             expert_ffn(self.sh_offsets, self.T, xs, self.sh_w13, self.sh_w2, self.dtype,
                        xp_scale=xs_scale, w13_scale=self.sh_w13_s, w2_scale=self.sh_w2_s,
-                       h=self.sh_h, h_scale=self.sh_h_s, yp=self.ysh, stages=MOE_FFN_ALL)
+                       h=self.sh_h, h_scale=self.sh_h_s, yp=self.ysh, stages=MOE_FFN_ALL, ws=self.sh_ffn_ws)
             ysh = self.ysh
         mark(5)
-        out = self.out if out is None else out
+        if out is None:
+            out = self.out
+            if self.local:
+                out.zero_()
         combine(sh, b["dest"], self.topk_w, self.yp, ysh, out=out, accumulate=self.local)
         mark(6)
         return out
@@ -148,8 +161,8 @@ class MoELayer:
                         "dx": torch.empty((self.T, self.d), dtype=torch.float32, device=dev),
                         "dlogits": torch.empty((self.T, self.E), dtype=torch.float32, device=dev),
                         "dw_gate": torch.empty((self.d, self.E), dtype=torch.float32, device=dev)}
-            wsb = lib().moe_route_backward_workspace_size(ctypes.byref(self.sh))
-            self.bws["gate_ws"] = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
+            wsb = workspace_bytes(MOE_OP_ROUTE_BACKWARD, self.sh, MOE_BF16)
+            self.bws["gate_ws"] = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
         return self.bws
 
     def _forward_train(self, x, marks):
@@ -162,8 +175,8 @@ class MoELayer:
 
         sh, w = self.sh, self._bwd_ws(x.device)
         mark(0)
-        route(sh, x, self.w_prep, self.bias, self.logit_offset, logits=self.logits, idx=self.idx,
-              w=self.topk_w, block_counts=self.block_counts)
+        route(sh, x, self.w_gate, self.bias, self.logit_offset, logits=self.logits, idx=self.idx,
+              w=self.topk_w, block_counts=self.block_counts, ws=self.route_ws)
         mark(1)
         self.dbufs = dispatch(sh, self.idx, self.block_counts, x, self.e_begin, self.e_end, bufs=self.dbufs)
         b = self.dbufs

@@ -53,31 +53,69 @@ FAKE = 0x1000  # never dereferenced: every case below fails its host-side check
 ])
 def test_route_rejects_bad_shapes(bad):
     sh = _sh(**bad)
-    st = L.moe_route(ctypes.byref(sh), FAKE, _lib.MOE_BF16, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None)
+    st = L.moe_route(ctypes.byref(sh), FAKE, _lib.MOE_BF16, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0,
+                     FAKE, 1 << 30, None)
     assert st == _lib.MOE_ERR_INVALID_ARG
 
 
+def _route(sh, x=FAKE, xdt=1, wg=FAKE, bias=FAKE, logits=FAKE, flags=0, ws=FAKE, wsb=1 << 30):
+    return L.moe_route(sh, x, xdt, wg, bias, None, logits, FAKE, FAKE, FAKE, flags, ws, wsb, None)
+
+
 def test_route_rejects_null_and_flags():
-    sh = _sh()
-    assert L.moe_route(None, FAKE, 1, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
-    assert L.moe_route(ctypes.byref(sh), FAKE, 1, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
-    assert L.moe_route(ctypes.byref(sh), None, 1, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
-    assert L.moe_route(ctypes.byref(sh), FAKE, 1, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, None) == -1
-    assert L.moe_route(ctypes.byref(sh), FAKE, 7, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
+    sh = ctypes.byref(_sh())
+    assert _route(None) == -1
+    assert _route(sh, bias=None) == -1
+    assert _route(sh, x=None) == -1
+    assert _route(sh, wg=None) == -1
+    assert _route(sh, flags=4) == -1
+    assert _route(sh, xdt=7) == -1
+    assert _route(sh, logits=None, flags=_lib.MOE_ROUTE_LOGITS_IN) == -1
+
+
+def test_route_workspace():
+    s = _sh(T=100, d=64, E=16)
+    sh = ctypes.byref(s)
+    need = L.moe_workspace_size(_lib.MOE_OP_ROUTE, sh, _lib.MOE_BF16)
+    planes = (3 * 16 * 64 * 2 + 255) // 256 * 256
+    assert need == planes + (100 * 16 * 4 + 255) // 256 * 256
+    assert _route(sh, ws=None) == -3
+    assert _route(sh, wsb=planes - 1) == -3                           # the planes do not fit
+    assert _route(sh, logits=None, wsb=need - 1) == -3                # nor the logits kept in ws
+    assert _route(sh, ws=FAKE + 16) == -3                             # not 256-byte aligned
+    # from given logits no workspace is used
+    s0 = _sh(T=0)
+    assert _route(ctypes.byref(s0), ws=None, wsb=0, flags=_lib.MOE_ROUTE_LOGITS_IN) == 0
+    assert _route(ctypes.byref(s0), ws=FAKE, wsb=planes) == 0
 
 
 def test_route_unsupported_and_empty():
     sh = _sh(E=320, G=5, M=2, k=4, gk=2)
-    assert L.moe_route(ctypes.byref(sh), FAKE, 1, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == -2
+    assert _route(ctypes.byref(sh)) == -2
     sh0 = _sh(T=0)
-    assert L.moe_route(ctypes.byref(sh0), FAKE, 1, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == 0
+    assert _route(ctypes.byref(sh0)) == 0
+
+
+def test_workspace_sizes():
+    ws = lambda op, s, dt=1: L.moe_workspace_size(op, ctypes.byref(s) if s is not None else None, dt)
+    v3 = _lib.MoeShape(16384, 7168, 256, 8, 4, 8, 2, 2048)
+    # dispatch: base rows per (64-token block, expert); e4m3 adds the scale table
+    assert ws(_lib.MOE_OP_DISPATCH, v3, _lib.MOE_BF16) == 256 * 256 * 4
+    assert ws(_lib.MOE_OP_DISPATCH, v3, _lib.MOE_E4M3) == 256 * 256 * 4 + 56 * 16384 * 4
+    assert ws(_lib.MOE_OP_COMBINE, v3) == 0
+    # expert products: two ticket-counter sets (9 counters on 64-byte lines each)
+    assert ws(_lib.MOE_OP_EXPERT_FFN, v3) == 2 * 768
+    assert ws(_lib.MOE_OP_EXPERT_FFN, None) == 2 * 768
+    assert ws(_lib.MOE_OP_EXPERT_FFN_BACKWARD, v3) == 768
+    assert ws(_lib.MOE_OP_ROUTE, v3) == 3 * 256 * 7168 * 2 + 16384 * 256 * 4
+    assert ws(99, v3) == 0
+    assert ws(_lib.MOE_OP_ROUTE, _lib.MoeShape(16, 64, 15, 4, 2, 4, 2, 32)) == 0   # invalid shape
 
 
 def test_dispatch_checks():
     sh = _sh()
-    ws = L.moe_dispatch_workspace_size(ctypes.byref(sh), 0, 16)
+    ws = L.moe_workspace_size(_lib.MOE_OP_DISPATCH, ctypes.byref(sh), _lib.MOE_BF16)
     assert ws == 1 * 16 * 4
-    assert L.moe_dispatch_workspace_size(ctypes.byref(sh), 4, 2) == 0
     args = lambda eb, ee, xdt, odt, scale, wsb: (ctypes.byref(sh), FAKE, FAKE, eb, ee, FAKE, xdt, odt, FAKE,
                                                 FAKE, FAKE, FAKE, FAKE, scale, FAKE, wsb, None)
     assert L.moe_dispatch(*args(0, 17, 1, 1, None, ws)) == -1
@@ -92,16 +130,21 @@ def test_dispatch_checks():
 
 
 def test_expert_ffn_checks():
-    f = L.moe_expert_ffn
-    assert f(0, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3, None) == -1
-    assert f(2000, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3, None) == -1
-    assert f(4, None, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3, None) == -1
-    assert f(4, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 0, None) == -1
-    assert f(4, FAKE, 10, 64, 32, 1, None, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 1, None) == -1
-    assert f(4, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, None, None, FAKE, None, FAKE, 2, None) == -1
-    assert f(4, FAKE, 10, 256, 128, 2, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3, None) == -1
-    assert f(4, FAKE, 10, 200, 128, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, None) == -2
-    assert f(4, FAKE, 0, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3, None) == 0
+    W = L.moe_workspace_size(_lib.MOE_OP_EXPERT_FFN, None, 1)
+    f = lambda *a, ws=FAKE, wsb=W: L.moe_expert_ffn(*a, ws, wsb, None)
+    assert f(0, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3) == -1
+    assert f(2000, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3) == -1
+    assert f(4, None, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3) == -1
+    assert f(4, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 0) == -1
+    assert f(4, FAKE, 10, 64, 32, 1, None, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 1) == -1
+    assert f(4, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, None, None, FAKE, None, FAKE, 2) == -1
+    assert f(4, FAKE, 10, 256, 128, 2, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3) == -1
+    assert f(4, FAKE, 10, 200, 128, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3) == -2
+    assert f(4, FAKE, 10, 512, 256, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3, ws=None) == -3
+    assert f(4, FAKE, 10, 512, 256, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3, wsb=W - 1) == -3
+    assert f(4, FAKE, 10, 512, 256, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3,
+             ws=FAKE + 64) == -3
+    assert f(4, FAKE, 0, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3) == 0
 
 
 def test_combine_checks():
@@ -116,8 +159,6 @@ def test_combine_checks():
 
 
 def test_prep_checks():
-    assert L.moe_gate_prepare(0, 16, FAKE, FAKE, None) == -1
-    assert L.moe_gate_prepare(64, 16, None, FAKE, None) == -1
     assert L.moe_quantize_blocks_e4m3(1, 100, 128, FAKE, FAKE, FAKE, None) == -2
     assert L.moe_quantize_blocks_e4m3(1, 128, 128, None, FAKE, FAKE, None) == -1
     assert L.moe_quantize_blocks_e4m3(0, 128, 128, FAKE, FAKE, FAKE, None) == 0
@@ -164,27 +205,34 @@ def test_backward_checks():
     assert L.moe_combine_backward(sh(k=17), bad, bad, bad, BF, bad, BF, bad, bad, None) == _lib.MOE_ERR_UNSUPPORTED
     assert L.moe_combine_backward(sh(), None, bad, bad, BF, bad, BF, bad, bad, None) == _lib.MOE_ERR_INVALID_ARG
     # expert FFN backward
+    WB = L.moe_workspace_size(_lib.MOE_OP_EXPERT_FFN_BACKWARD, None, BF)
+    fb = lambda *a, ws=FAKE, wsb=WB: L.moe_expert_ffn_backward(*a, ws, wsb, None)
     args = [bad] * 10
-    assert L.moe_expert_ffn_backward(0, bad, 8, 256, 256, BF, *args, 0, None) == _lib.MOE_ERR_INVALID_ARG
-    assert L.moe_expert_ffn_backward(2, None, 8, 256, 256, BF, *args, 0, None) == _lib.MOE_ERR_INVALID_ARG
-    assert L.moe_expert_ffn_backward(1, None, 8, 256, 256, BF, *args, 2, None) == _lib.MOE_ERR_INVALID_ARG
-    assert L.moe_expert_ffn_backward(1, None, 8, 256, 256, F, *args, 0, None) == _lib.MOE_ERR_UNSUPPORTED
-    assert L.moe_expert_ffn_backward(1, None, 8, 256, 128, BF, *args, 0, None) == _lib.MOE_ERR_UNSUPPORTED
-    assert L.moe_expert_ffn_backward(1, None, 8, 200, 256, BF, *args, 0, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert fb(0, bad, 8, 256, 256, BF, *args, 0) == _lib.MOE_ERR_INVALID_ARG
+    assert fb(2, None, 8, 256, 256, BF, *args, 0) == _lib.MOE_ERR_INVALID_ARG
+    assert fb(1, None, 8, 256, 256, BF, *args, 2) == _lib.MOE_ERR_INVALID_ARG
+    assert fb(1, None, 8, 256, 256, F, *args, 0) == _lib.MOE_ERR_UNSUPPORTED
+    assert fb(1, None, 8, 256, 128, BF, *args, 0) == _lib.MOE_ERR_UNSUPPORTED
+    assert fb(1, None, 8, 200, 256, BF, *args, 0) == _lib.MOE_ERR_UNSUPPORTED
+    assert fb(1, None, 8, 256, 256, BF, *args, 0, ws=None) == _lib.MOE_ERR_WORKSPACE
+    assert fb(1, None, 8, 256, 256, BF, *args, 0, wsb=WB - 1) == _lib.MOE_ERR_WORKSPACE
     for i in range(10):
         a = list(args)
         a[i] = None
-        assert L.moe_expert_ffn_backward(1, None, 8, 256, 256, BF, *a, 0, None) == _lib.MOE_ERR_INVALID_ARG
+        assert fb(1, None, 8, 256, 256, BF, *a, 0) == _lib.MOE_ERR_INVALID_ARG
     # training forward
+    WT = L.moe_workspace_size(_lib.MOE_OP_EXPERT_FFN, None, BF)
+    ft = lambda *a, ws=FAKE, wsb=WT: L.moe_expert_ffn_train(*a, ws, wsb, None)
     targs = [bad] * 6
-    assert L.moe_expert_ffn_train(1, None, 0, 256, 256, BF, *targs, None) == _lib.MOE_OK
-    assert L.moe_expert_ffn_train(2, None, 8, 256, 256, BF, *targs, None) == _lib.MOE_ERR_INVALID_ARG
-    assert L.moe_expert_ffn_train(1, None, 8, 256, 128, BF, *targs, None) == _lib.MOE_ERR_UNSUPPORTED
-    assert L.moe_expert_ffn_train(1, None, 8, 256, 256, F, *targs, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert ft(1, None, 0, 256, 256, BF, *targs) == _lib.MOE_OK
+    assert ft(2, None, 8, 256, 256, BF, *targs) == _lib.MOE_ERR_INVALID_ARG
+    assert ft(1, None, 8, 256, 128, BF, *targs) == _lib.MOE_ERR_UNSUPPORTED
+    assert ft(1, None, 8, 256, 256, F, *targs) == _lib.MOE_ERR_UNSUPPORTED
+    assert ft(1, None, 8, 256, 256, BF, *targs, wsb=WT - 1) == _lib.MOE_ERR_WORKSPACE
     for i in range(6):
         a = list(targs)
         a[i] = None
-        assert L.moe_expert_ffn_train(1, None, 8, 256, 256, BF, *a, None) == _lib.MOE_ERR_INVALID_ARG
+        assert ft(1, None, 8, 256, 256, BF, *a) == _lib.MOE_ERR_INVALID_ARG
     # dispatch backward
     assert L.moe_dispatch_backward(sh(0), None, None, BF, None, None, 0, None) == _lib.MOE_OK
     assert L.moe_dispatch_backward(sh(), bad, bad, BF, None, bad, 2, None) == _lib.MOE_ERR_INVALID_ARG
@@ -200,12 +248,13 @@ def test_backward_checks():
     assert L.moe_route_backward(sh(), bad, BF, None, None, bad, bad, bad, bad, bad, bad,
                                 None, 0, None) == _lib.MOE_ERR_INVALID_ARG
     big = ctypes.byref(_lib.MoeShape(16384, 7168, 256, 8, 4, 8, 2, 2048))
-    need = L.moe_route_backward_workspace_size(big)
+    need = L.moe_workspace_size(_lib.MOE_OP_ROUTE_BACKWARD, big, BF)
     # the larger of the two paths: 16 fp32 K-parts of dW_g, or the bf16-plane
     # path (dlogits as 6 and 3 planes, W_g as 6 planes, 8 row splits of fp32
-    # [d, 3E] partials)
+    # [d, 3E] partials, one ticket-counter set)
     T, d, E = 16384, 7168, 256
-    assert need == max(16 * d * E * 4, T * 6 * E * 2 + d * 6 * E * 2 + T * 3 * E * 2 + 8 * d * 3 * E * 4)
-    assert L.moe_route_backward(big, bad, BF, bad, None, bad, bad, bad, bad, bad, bad, bad, need - 1,
+    assert need == max(16 * d * E * 4,
+                       T * 6 * E * 2 + d * 6 * E * 2 + T * 3 * E * 2 + 8 * d * 3 * E * 4 + 9 * 64)
+    assert L.moe_route_backward(big, bad, BF, bad, None, bad, bad, bad, bad, bad, bad, FAKE, need - 1,
                                 None) == _lib.MOE_ERR_WORKSPACE
-    assert L.moe_route_backward_workspace_size(sh(T=1000)) == 0
+    assert L.moe_workspace_size(_lib.MOE_OP_ROUTE_BACKWARD, sh(T=1000), BF) == 0

@@ -1,11 +1,12 @@
 """The persistent expert products under concurrency and graph capture.
 
-Their work-groups take tiles from device-side ticket counters; each launch
-uses the next of 16 counter sets and leaves it cleared.  These tests run
-launches on four streams at once and replay a captured layer forward, and
-require every result to equal the same computation run alone, bit for bit
-(each tile is computed by one work-group in a fixed K order, so the schedule
-cannot change a value)."""
+Their work-groups take tiles from ticket counters in the caller's workspace
+(zero-filled once; every call leaves it zero).  These tests run launches on
+four streams at once, each stream with its own workspace, replay two captured
+graphs concurrently on two streams, and replay a captured layer forward; every
+result must equal the same computation run alone, bit for bit (each tile is
+computed by one work-group in a fixed K order, so the schedule cannot change a
+value)."""
 import numpy as np
 import pytest
 import torch
@@ -36,10 +37,10 @@ def _case(seed, d, d_ff, dtype, dev):
     return off, rows, args
 
 
-def _run(off, rows, args):
+def _run(off, rows, args, ws=None, h=None, h_scale=None, yp=None):
     yp, h, hs = M.expert_ffn(off, rows, args["xp"], args["w13"], args["w2"], args["dtype"],
                              xp_scale=args.get("xp_scale"), w13_scale=args.get("w13_scale"),
-                             w2_scale=args.get("w2_scale"))
+                             w2_scale=args.get("w2_scale"), ws=ws, h=h, h_scale=h_scale, yp=yp)
     return yp
 
 
@@ -53,18 +54,62 @@ def test_expert_ffn_on_four_streams(dtype):
     torch.cuda.synchronize()
     streams = [torch.cuda.Stream() for _ in cases]
     main = torch.cuda.current_stream()
+    wss = [M.workspace(M.MOE_OP_EXPERT_FFN, None, dtype, dev) for _ in cases]
     outs = [[] for _ in cases]
     for s in streams:
         s.wait_stream(main)
     for rep in range(3):
         for i, (c, s) in enumerate(zip(cases, streams)):
             with torch.cuda.stream(s):
-                outs[i].append(_run(*c))
+                outs[i].append(_run(*c, ws=wss[i]))
     torch.cuda.synchronize()
     for i, c in enumerate(cases):
         rows = c[1]
         for y in outs[i]:
             assert torch.equal(y[:rows], ref[i][:rows]), i
+
+
+@pytest.mark.parametrize("dtype", [M.MOE_BF16, M.MOE_E4M3])
+def test_two_graphs_replayed_concurrently(dtype):
+    """Two captures of the same expert products, each with its own workspace
+    and buffers, replayed at the same time on two streams (three rounds, eager
+    work between them): every replay equals the eager result."""
+    dev = need_gpu()
+    print(f"two graphs on two streams, dtype={dtype}", flush=True)
+    d, d_ff = 1024, 512
+    off, rows, args = _case(21, d, d_ff, dtype, dev)
+    ref = _run(off, rows, args).clone()
+    torch.cuda.synchronize()
+    store = torch.uint8 if dtype == M.MOE_E4M3 else torch.bfloat16
+    bufs = []
+    for _ in range(2):
+        ws = M.workspace(M.MOE_OP_EXPERT_FFN, None, dtype, dev)
+        h = torch.empty((rows, d_ff), dtype=store, device=dev)
+        hs = torch.empty((d_ff // 128, rows), dtype=torch.float32, device=dev) if dtype == M.MOE_E4M3 else None
+        yp = torch.empty((rows, d), dtype=torch.bfloat16, device=dev)
+        bufs.append((ws, h, hs, yp))
+    torch.cuda.synchronize()
+    graphs = []
+    for ws, h, hs, yp in bufs:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            _run(off, rows, args, ws=ws, h=h, h_scale=hs, yp=yp)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in graphs]
+    for rep in range(3):
+        for _, _, _, yp in bufs:
+            yp.zero_()
+        _run(off, rows, args)                      # eager work between the replays
+        main = torch.cuda.current_stream()
+        for s in streams:
+            s.wait_stream(main)
+        for g, s in zip(graphs, streams):
+            with torch.cuda.stream(s):
+                g.replay()
+        torch.cuda.synchronize()
+        for i, (_, _, _, yp) in enumerate(bufs):
+            assert torch.equal(yp[:rows], ref[:rows]), (rep, i)
 
 
 def test_layer_forward_graph_replay():

@@ -45,8 +45,7 @@ def test_gate_logits_tolerance(name, T):
     cfg, inp, o = router_inputs(name, T)
     print(f"route S1 {name} T={cfg.T}", flush=True)
     sh = moe_shape(cfg)
-    w_prep = M.gate_prepare(inp["w_gate"])
-    L, idx, w, bc = M.route(sh, inp["x"], w_prep, inp["bias"], inp["logit_offset"])
+    L, idx, w, bc = M.route(sh, inp["x"], inp["w_gate"], inp["bias"], inp["logit_offset"])
     torch.cuda.synchronize()
     err = logits_row_err(host(L), o["L"])
     print(f"  worst-row logit error {err:.3e}")
@@ -57,14 +56,18 @@ def test_gate_logits_tolerance(name, T):
     assert np.array_equal(host(w).view(np.uint32), gw.view(np.uint32))
 
 
-def test_gate_prepare_planes_exact():
+def test_logits_kept_in_workspace():
+    """logits = NULL: the route keeps them in its workspace; the selection is
+    the same as with a logits buffer."""
     dev = need_gpu()
-    cfg, inp, o = router_inputs("v3")
-    w_prep = M.gate_prepare(inp["w_gate"])
+    cfg, inp, o = router_inputs("flash")
+    sh = moe_shape(cfg)
+    ws = M.workspace(M.MOE_OP_ROUTE, sh, M.MOE_BF16, dev)
+    L, idx, w, bc = M.route(sh, inp["x"], inp["w_gate"], inp["bias"], ws=ws)
+    L2, idx2, w2, bc2 = M.route(sh, inp["x"], inp["w_gate"], inp["bias"], ws=ws, keep_logits=False)
     torch.cuda.synchronize()
-    p = host(w_prep).astype(np.float32)           # [3, E, d] bf16 values
-    s = (p[0] + p[1]) + p[2]
-    assert np.array_equal(s, o["w_gate"].T)
+    assert L2 is None
+    assert torch.equal(idx, idx2) and torch.equal(w, w2) and torch.equal(bc, bc2)
 
 
 def _special_logits(rng, T, E):
@@ -90,6 +93,66 @@ def test_affinity_bitexact_all_experts_selected():
     idx, w, _ = _route_in(cfg, L, bias, None, dev)
     assert np.array_equal(idx, idx_o)
     assert np.array_equal(w.view(np.uint32), w_o.view(np.uint32))
+
+
+def _dense_affinity_logits():
+    """About 1M fp32 logits: a strided sweep over every fp32 in [-200, 88],
+    runs of consecutive values at the places where the affinity's evaluation
+    changes form or rounds close to a boundary (0, +-2^-14, the fp32 midpoint
+    crossing near -8.5e-9, +-1, +-20, +-87, +-150), and special values (rows
+    are 16 neighbours of the list, so no row has only zero affinities, for
+    which the weights would be 0/0)."""
+    lo, hi = np.float32(-200.0).view(np.uint32), np.float32(88.0).view(np.uint32)
+    neg = np.arange(0x80000000, int(lo) + 1, 4099, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    pos = np.arange(0, int(hi) + 1, 4099, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    runs = []
+    for c in (0.0, 2.0 ** -14, -(2.0 ** -14), -8.5e-9, 1.0, -1.0, 20.0, -20.0, 87.0, -87.0, 150.0, -150.0):
+        b = np.int64(np.float32(c).view(np.uint32))
+        runs.append((b + np.arange(-8192, 8192)).astype(np.uint32).view(np.float32))
+    sp = np.array([0.0, -0.0, 1e-30, -1e-30, 1.4e-45, -1.4e-45, 300.0, -300.0, 301.0, -301.0, 3.4e38,
+                   -3.4e38, 1e30, -1e30], dtype=np.float32)
+    l = np.concatenate([neg, pos] + runs + [sp])
+    l = l[np.isfinite(l)]
+    return l
+
+
+def test_affinity_bitexact_dense():
+    """Every expert selected (k = E, M = G, zero bias): the order of each
+    token's experts and the bits of w = s_j / sum(s) follow every affinity
+    bit, over about a million logits chosen across the whole fp32 range."""
+    dev = need_gpu()
+    l = _dense_affinity_logits()
+    E = 16
+    T = -(-l.size // E)
+    L = np.resize(l, T * E).reshape(T, E).astype(np.float32)
+    cfg = C.TINY.with_(T=T, k=E, M=4)
+    bias = np.zeros(E, np.float32)
+    idx_o, w_o = OR.route_from_logits(L, bias, cfg.G, cfg.M, cfg.k, cfg.gk)
+    idx, w, _ = _route_in(cfg, L, bias, None, dev)
+    assert np.array_equal(idx, idx_o)
+    assert np.array_equal(w.view(np.uint32), w_o.view(np.uint32))
+
+
+def test_affinity_monotone_on_gpu():
+    """Each token's 16 logits are consecutive fp32 values in ascending order;
+    with every expert selected, the GPU's weight w_e = s_e / S must not
+    decrease with e (the exact affinity is increasing)."""
+    dev = need_gpu()
+    E = 16
+    starts = np.concatenate([np.linspace(-200, 80, 20000, dtype=np.float32),
+                             np.float32(np.linspace(-1e-7, 1e-7, 4000)),
+                             np.float32([2.0 ** -14, -(2.0 ** -14), -8.5e-9])])
+    base = starts.view(np.uint32).astype(np.int64)
+    neg = starts < 0
+    step = np.where(neg, -1, 1)[:, None] * np.arange(E)[None, :]
+    L = (base[:, None] + step).astype(np.uint32).view(np.float32)
+    L = np.sort(L, axis=1)
+    T = L.shape[0]
+    cfg = C.TINY.with_(T=T, k=E, M=4)
+    idx, w, _ = _route_in(cfg, L, np.zeros(E, np.float32), None, dev)
+    we = np.zeros((T, E), np.float32)
+    np.put_along_axis(we, idx.astype(np.int64), w, axis=1)
+    assert np.all(np.diff(we.astype(np.float64), axis=1) >= 0)
 
 
 @pytest.mark.parametrize("E,G,M,k", [(16, 4, 2, 4), (64, 8, 4, 6), (256, 8, 4, 8), (256, 8, 1, 3),
@@ -118,10 +181,9 @@ def test_route_deterministic_repeat():
     dev = need_gpu()
     cfg, inp, o = router_inputs("v3")
     sh = moe_shape(cfg)
-    w_prep = M.gate_prepare(inp["w_gate"])
     outs = []
     for _ in range(3):
-        L, idx, w, bc = M.route(sh, inp["x"], w_prep, inp["bias"])
+        L, idx, w, bc = M.route(sh, inp["x"], inp["w_gate"], inp["bias"])
         outs.append((L.clone(), idx.clone(), w.clone(), bc.clone()))
     torch.cuda.synchronize()
     for rep in outs[1:]:
