@@ -56,6 +56,7 @@ extern "C" {
 #define MOE_ERR_UNSUPPORTED (-2)  /* valid, but not a shape/dtype this library runs */
 #define MOE_ERR_WORKSPACE (-3)    /* workspace smaller than *_workspace_size() */
 #define MOE_ERR_HIP (-4)          /* a kernel launch failed */
+#define MOE_ERR_SCRATCH (-5)      /* moe_dispatch_noalloc: the call needs more than its static scratch */
 
 /* element types */
 #define MOE_F32 0
@@ -195,6 +196,30 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const int32_t*
                  int32_t e_begin, int32_t e_end, const void* x, int x_dtype, int out_dtype,
                  int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src, void* xp,
                  float* xp_scale, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_dispatch_noalloc - moe_dispatch without a workspace argument, for
+ * callers that cannot allocate device memory (code under graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, outputs
+ * and checks as moe_dispatch; the workspace is a static array the library
+ * holds on each device (8 MiB, MOE_DISPATCH_NOALLOC_SCRATCH bytes), so the
+ * call allocates nothing.  A call whose workspace need
+ * (moe_workspace_size(MOE_OP_DISPATCH, ...) for its expert range and output
+ * type) exceeds it returns MOE_ERR_SCRATCH before anything is launched: with
+ * 256 local experts that allows T up to 524288 for a bf16 or fp32 output, and
+ * T up to about 34900 for the e4m3 output at d = 7168 (V3 shapes, T = 16384,
+ * need 3.9 MiB).
+ * Nothing in it needs to start at zero.  Every call on a device shares that
+ * device's array and it keeps the last call's contents: calls that may
+ * execute at the same time on one device (other streams, concurrent graph
+ * replays) race on it and must use moe_dispatch with distinct workspaces.
+ * The array belongs to the current device (the device of `stream`).
+ */
+#define MOE_DISPATCH_NOALLOC_SCRATCH 8388608  /* 8 MiB */
+int moe_dispatch_noalloc(const moe_shape* shape, const int32_t* topk_idx, const int32_t* block_counts,
+                         int32_t e_begin, int32_t e_end, const void* x, int x_dtype, int out_dtype,
+                         int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src, void* xp,
+                         float* xp_scale, moe_stream_t stream);
 
 /*
  * moe_expert_ffn - grouped SwiGLU experts (mastering-deepseek-v4 Exp08,

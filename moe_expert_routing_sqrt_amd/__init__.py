@@ -8,6 +8,7 @@ library is missing, or a tensor is not on the GPU, calls raise.
     route(shape, x, w_gate, bias)            -> logits, topk_idx, topk_w, block_counts
     route_hash(shape, token_ids, seed)       -> topk_idx, topk_w, block_counts
     dispatch(shape, topk_idx, block_counts, x) -> counts, offsets, dest, src, xp, xp_scale
+    dispatch_noalloc(...)                    the same, its workspace in the library's static scratch
     expert_ffn(offsets, max_rows, xp, w13, w2) -> yp
     combine(shape, dest, topk_w, yp, ysh)    -> out
     bias_update(block_counts, bias, gamma)   -> load (bias updated in place)
@@ -28,7 +29,8 @@ from ._lib import (MOE_BF16, MOE_BWD_AU_SAVED, MOE_E4M3, MOE_F32, MOE_FFN_ALL, M
                    MOE_OP_EXPERT_FFN_BACKWARD, MOE_OP_ROUTE, MOE_OP_ROUTE_BACKWARD, MOE_ROUTE_BLOCK,
                    MOE_ROUTE_LOGITS_IN, MoeError, MoeShape)
 
-__all__ = ["shape", "workspace_bytes", "workspace", "route", "route_hash", "dispatch", "combine_backward",
+__all__ = ["shape", "workspace_bytes", "workspace", "route", "route_hash", "dispatch", "dispatch_noalloc",
+           "combine_backward",
            "expert_ffn_train",
            "expert_ffn_backward", "dispatch_backward", "route_backward", "expert_ffn", "combine",
            "quantize_blocks_e4m3", "quantize_rows_e4m3", "bias_update", "MoELayer", "MoeError", "lib"]
@@ -198,6 +200,37 @@ def dispatch(sh: MoeShape, idx: torch.Tensor, block_counts: torch.Tensor, x: tor
                             _ptr(b["src"]), _ptr(b["xp"]), _ptr(b["xp_scale"]), _ptr(b["ws"]),
                             b["ws"].numel(), _stream())
     _lib.check("moe_dispatch", st)
+    return b
+
+
+def dispatch_noalloc(sh: MoeShape, idx: torch.Tensor, block_counts: torch.Tensor, x: torch.Tensor,
+                     bufs: dict, e_begin: int = 0, e_end: Optional[int] = None,
+                     out_dtype: Optional[int] = None) -> dict:
+    """moe_dispatch_noalloc into caller-given output buffers (`bufs` with
+    counts, offsets, dest, src, xp and, for e4m3, xp_scale, as dispatch()
+    returns them): the call allocates nothing, its workspace is the library's
+    static scratch."""
+    e_end = sh.E if e_end is None else e_end
+    n = e_end - e_begin
+    T, k, d = sh.T, sh.k, sh.d
+    x_dtype = _dt(x)
+    out_dtype = x_dtype if out_dtype is None else out_dtype
+    b = bufs
+    _need(b["counts"], n, "counts")
+    _need(b["offsets"], n + 1, "offsets")
+    _need(b["dest"], T * k, "dest")
+    _need(b["src"], T * k, "src")
+    _need(b["xp"], T * k * d, "xp")
+    _need(x, T * d, "x")
+    _need(idx, T * k, "topk_idx")
+    _need(block_counts, n_blocks(T) * sh.E, "block_counts")
+    xs = b.get("xp_scale") if out_dtype == MOE_E4M3 else None
+    if out_dtype == MOE_E4M3:
+        _need(xs, T * k * (d // MOE_FP8_TILE), "xp_scale")
+    st = lib().moe_dispatch_noalloc(ctypes.byref(sh), _ptr(idx), _ptr(block_counts), e_begin, e_end, _ptr(x),
+                                    x_dtype, out_dtype, _ptr(b["counts"]), _ptr(b["offsets"]), _ptr(b["dest"]),
+                                    _ptr(b["src"]), _ptr(b["xp"]), _ptr(xs), _stream())
+    _lib.check("moe_dispatch_noalloc", st)
     return b
 
 

@@ -15,6 +15,8 @@ MOE_ERR_INVALID_ARG = -1
 MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
+MOE_ERR_SCRATCH = -5
+MOE_DISPATCH_NOALLOC_SCRATCH = 8 << 20
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_BWD_AU_SAVED = 1
 MOE_ROUTE_LOGITS_IN = 1
@@ -53,6 +55,8 @@ SIGNATURES = {
                             _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_expert_ffn": (_INT, [_I32, _P, _I64, _I32, _I32, _INT, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                               _INT, _P, _SZ, _P]),
+    "moe_dispatch_noalloc": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _I32, _I32, _P, _INT, _INT,
+                                    _P, _P, _P, _P, _P, _P, _P]),
     "moe_combine": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _P, _INT, _P, _P, _INT, _INT, _P]),
     "moe_quantize_blocks_e4m3": (_INT, [_I64, _I32, _I32, _P, _P, _P, _P]),
     "moe_quantize_rows_e4m3": (_INT, [_I64, _I32, _P, _P, _P, _P]),

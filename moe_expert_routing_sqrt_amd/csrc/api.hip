@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -13,7 +14,35 @@
 
 using namespace moe;
 
+// Workspace of moe_dispatch_noalloc, held by the library: one copy per device,
+// at that device's own address, for the life of the process.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for
+// the device symbol); it uses the device address hipGetSymbolAddress returns.
+static constexpr size_t kScratchBytes = size_t{8} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+static_assert(kScratchBytes == MOE_DISPATCH_NOALLOC_SCRATCH, "the header states the scratch size");
+
 namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];  // device address of `scratch`, per device (under the mutex)
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current.
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kScratchDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
@@ -71,6 +100,7 @@ const char* moe_status_str(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_SCRATCH: return "needs more than the library's static scratch buffer";
     default: return "unknown status";
   }
 }
@@ -141,10 +171,11 @@ static size_t dispatch_ws_bytes(const moe_shape* shape, int32_t e_begin, int32_t
          static_cast<size_t>(shape->d / MOE_FP8_TILE) * static_cast<size_t>(shape->T) * sizeof(float);
 }
 
-int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const int32_t* block_counts,
-                 int32_t e_begin, int32_t e_end, const void* x, int x_dtype, int out_dtype,
-                 int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src, void* xp,
-                 float* xp_scale, void* ws, size_t ws_bytes, moe_stream_t stream) {
+// Argument checks of moe_dispatch before any workspace is looked at.
+static int dispatch_check(const moe_shape* shape, const int32_t* topk_idx, const int32_t* block_counts,
+                          int32_t e_begin, int32_t e_end, const void* x, int x_dtype, int out_dtype,
+                          int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src, void* xp,
+                          float* xp_scale) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (e_begin < 0 || e_end <= e_begin || e_end > shape->E) return MOE_ERR_INVALID_ARG;
@@ -163,9 +194,13 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const int32_t*
   const int elem = x_dtype == MOE_F32 ? 4 : 2;
   if ((shape->d * elem) % 16 != 0) return MOE_ERR_UNSUPPORTED;  // 16-byte row chunks
   if (e_end - e_begin > 256 || shape->k > 16) return MOE_ERR_UNSUPPORTED;
-  if (ws == nullptr || ws_bytes < dispatch_ws_bytes(shape, e_begin, e_end, out_dtype) || !aligned256(ws))
-    return MOE_ERR_WORKSPACE;
-  if (shape->T == 0) return MOE_OK;
+  return MOE_OK;
+}
+
+static int dispatch_launch(const moe_shape* shape, const int32_t* topk_idx, const int32_t* block_counts,
+                           int32_t e_begin, int32_t e_end, const void* x, int x_dtype, int out_dtype,
+                           int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src, void* xp,
+                           float* xp_scale, void* ws, moe_stream_t stream) {
   float* tok_scale = out_dtype == MOE_E4M3
                          ? reinterpret_cast<float*>(static_cast<char*>(ws) + dispatch_scale_offset(shape, e_begin, e_end))
                          : nullptr;
@@ -173,6 +208,36 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const int32_t*
                                     e_end, x, x_dtype, out_dtype, shape->d, counts, offsets, dest,
                                     src, xp, xp_scale, static_cast<int32_t*>(ws), tok_scale,
                                     as_stream(stream)));
+}
+
+int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const int32_t* block_counts,
+                 int32_t e_begin, int32_t e_end, const void* x, int x_dtype, int out_dtype,
+                 int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src, void* xp,
+                 float* xp_scale, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  const int st = dispatch_check(shape, topk_idx, block_counts, e_begin, e_end, x, x_dtype, out_dtype, counts,
+                                offsets, dest, src, xp, xp_scale);
+  if (st != MOE_OK) return st;
+  if (ws == nullptr || ws_bytes < dispatch_ws_bytes(shape, e_begin, e_end, out_dtype) || !aligned256(ws))
+    return MOE_ERR_WORKSPACE;
+  if (shape->T == 0) return MOE_OK;
+  return dispatch_launch(shape, topk_idx, block_counts, e_begin, e_end, x, x_dtype, out_dtype, counts, offsets,
+                         dest, src, xp, xp_scale, ws, stream);
+}
+
+int moe_dispatch_noalloc(const moe_shape* shape, const int32_t* topk_idx, const int32_t* block_counts,
+                         int32_t e_begin, int32_t e_end, const void* x, int x_dtype, int out_dtype,
+                         int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src, void* xp,
+                         float* xp_scale, moe_stream_t stream) {
+  const int st = dispatch_check(shape, topk_idx, block_counts, e_begin, e_end, x, x_dtype, out_dtype, counts,
+                                offsets, dest, src, xp, xp_scale);
+  if (st != MOE_OK) return st;
+  if (dispatch_ws_bytes(shape, e_begin, e_end, out_dtype) > kScratchBytes) return MOE_ERR_SCRATCH;
+  if (shape->T == 0) return MOE_OK;
+  void* ws = nullptr;
+  const int sa = scratch_address(&ws);
+  if (sa != MOE_OK) return sa;
+  return dispatch_launch(shape, topk_idx, block_counts, e_begin, e_end, x, x_dtype, out_dtype, counts, offsets,
+                         dest, src, xp, xp_scale, ws, stream);
 }
 
 int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int32_t d,

@@ -258,3 +258,26 @@ def test_backward_checks():
     assert L.moe_route_backward(big, bad, BF, bad, None, bad, bad, bad, bad, bad, bad, FAKE, need - 1,
                                 None) == _lib.MOE_ERR_WORKSPACE
     assert L.moe_workspace_size(_lib.MOE_OP_ROUTE_BACKWARD, sh(T=1000), BF) == 0
+
+
+def test_dispatch_noalloc_host_checks():
+    """Argument and size checks on the host, before the static scratch (or
+    anything on a device) is touched."""
+    f = L.moe_dispatch_noalloc
+    big = _lib.MoeShape(65536, 7168, 256, 8, 4, 8, 2, 2048)
+    # e4m3 output: 56 x 65536 fp32 scales alone exceed the 8 MiB scratch
+    assert f(ctypes.byref(big), FAKE, FAKE, 0, 256, FAKE, 1, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+             None) == _lib.MOE_ERR_SCRATCH
+    assert _lib.MOE_DISPATCH_NOALLOC_SCRATCH == 8 << 20
+    need = L.moe_workspace_size(_lib.MOE_OP_DISPATCH, ctypes.byref(big), _lib.MOE_E4M3)
+    assert need > _lib.MOE_DISPATCH_NOALLOC_SCRATCH
+    sh = _sh()
+    assert f(ctypes.byref(sh), None, FAKE, 0, 16, FAKE, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+             None) == _lib.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(sh), FAKE, FAKE, 0, 17, FAKE, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+             None) == _lib.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(sh), FAKE, FAKE, 0, 16, FAKE, 1, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+             None) == _lib.MOE_ERR_INVALID_ARG          # e4m3 needs scales
+    sh0 = _sh(T=0)
+    assert f(ctypes.byref(sh0), FAKE, FAKE, 0, 16, FAKE, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+             None) == _lib.MOE_OK
