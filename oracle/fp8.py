@@ -12,18 +12,24 @@ code, and saturates at +-448; a tile's scale is fp32(amax / 448), or 1 when the
 tile is all zeros; the element code is e4m3(fp32(x / scale)); the sign bit
 follows the sign of the input, so small negatives become -0 (code 0x80).
 
-The conversion here is the definition itself: the nearest of the 127 finite
+to_e4m3 is the conversion's definition itself: the nearest of the 127 finite
 non-negative e4m3 values, found by a sorted-table search, ties broken to the
-even code.
+even code.  The tile and block quantisers round through to_e4m3_cast instead:
+the same conversion by torch's CPU float8_e4m3fn cast (a library routine,
+hundreds of times faster on the 29M-element expert matrices), after clamping
+to +-448 as the saturating reading asks (the cast alone turns magnitudes from
+464 up into NaN).
 
-Pins (tests/test_oracle_fp8.py): matches torch's float8_e4m3fn cast on every
-fp32 in a dense sweep of |v| <= 448 and on every midpoint between e4m3 values;
-every e4m3 value round-trips; relative error <= 2^-4 for results in the
-normal range.
+Pins (tests/test_oracle_fp8.py): to_e4m3 matches torch's float8_e4m3fn cast on
+every fp32 in a dense sweep of |v| <= 448 and on every midpoint between e4m3
+values, to_e4m3_cast matches to_e4m3 on those and on saturating inputs, and
+the quantisers give the same codes with either; every e4m3 value round-trips;
+relative error <= 2^-4 for results in the normal range.
 """
 from __future__ import annotations
 
 import numpy as np
+import torch
 
 E4M3_MAX = 448.0
 
@@ -59,6 +65,13 @@ def to_e4m3(v):
     return (code | np.where(neg, 0x80, 0).astype(np.uint8)).astype(np.uint8)
 
 
+def to_e4m3_cast(v):
+    """fp32 array -> e4m3fn codes by torch's cast after saturation to +-448
+    (the same codes as to_e4m3)."""
+    v = np.clip(np.asarray(v, dtype=np.float32), np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    return torch.from_numpy(np.ascontiguousarray(v)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
 def from_e4m3(codes):
     c = np.asarray(codes, dtype=np.uint8)
     mag = _TABLE[np.minimum(c & 0x7F, 0x7E)]
@@ -71,7 +84,7 @@ def tile_scale(amax):
     return np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
 
 
-def quantize_rows(x, tile=128):
+def quantize_rows(x, tile=128, cast=to_e4m3_cast):
     """Per-row 1 x tile quantisation of x [n, c] (c % tile == 0).
     Returns codes [n, c] uint8 and scales [n, c/tile] fp32."""
     x = np.asarray(x, dtype=np.float32)
@@ -79,11 +92,11 @@ def quantize_rows(x, tile=128):
     xt = x.reshape(n, c // tile, tile)
     amax = np.abs(xt).max(axis=2)
     scale = tile_scale(amax)
-    q = to_e4m3((xt / scale[:, :, None]).astype(np.float32))
+    q = cast((xt / scale[:, :, None]).astype(np.float32))
     return q.reshape(n, c), scale
 
 
-def quantize_blocks(w, block=128):
+def quantize_blocks(w, block=128, cast=to_e4m3_cast):
     """128 x 128 block quantisation of w [r, c].  Returns codes [r, c] and
     scales [r/block, c/block] fp32."""
     w = np.asarray(w, dtype=np.float32)
@@ -91,7 +104,7 @@ def quantize_blocks(w, block=128):
     wb = w.reshape(r // block, block, c // block, block)
     amax = np.abs(wb).max(axis=(1, 3))
     scale = tile_scale(amax)
-    q = to_e4m3((wb / scale[:, None, :, None]).astype(np.float32))
+    q = cast((wb / scale[:, None, :, None]).astype(np.float32))
     return q.reshape(r, c), scale
 
 

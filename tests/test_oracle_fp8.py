@@ -24,6 +24,33 @@ def test_matches_torch_on_midpoints():
     assert np.array_equal(Q.to_e4m3(v), _torch_codes(v))
 
 
+def test_cast_equals_definition():
+    # the library cast the quantisers round through gives the definition's codes
+    t = Q.e4m3_table()
+    mids = ((t[1:] + t[:-1]) / 2).astype(np.float32)
+    top = np.float32(448.0).view(np.uint32)
+    sweep = np.arange(0, top + 1, 13, dtype=np.uint32).view(np.float32)
+    sat = np.array([448.0, 448.00003, 463.9, 464.0, 479.9, 480.0, 1e6, 3.4e38, -0.0, 1e-30, -1e-30],
+                   dtype=np.float32)
+    v = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, 1000), sweep, sat])
+    v = np.concatenate([v, -v])
+    assert np.array_equal(Q.to_e4m3_cast(v), Q.to_e4m3(v))
+
+
+def test_quantisers_same_with_either_rounding():
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((37, 512)) * np.exp(rng.uniform(-8, 8, size=(37, 1)))).astype(np.float32)
+    x[3, :128] = 0.0
+    a, sa = Q.quantize_rows(x)
+    b, sb = Q.quantize_rows(x, cast=Q.to_e4m3)
+    assert np.array_equal(a, b) and np.array_equal(sa, sb)
+    w = (0.02 * rng.standard_normal((256, 384))).astype(np.float32)
+    w[:128, 128:256] = 0.0
+    a, sa = Q.quantize_blocks(w)
+    b, sb = Q.quantize_blocks(w, cast=Q.to_e4m3)
+    assert np.array_equal(a, b) and np.array_equal(sa, sb)
+
+
 def test_round_trip_and_format():
     t = Q.e4m3_table()
     assert t[-1] == 448.0 and t[1] == 2.0 ** -9 and t[8] == 2.0 ** -6
