@@ -1,11 +1,15 @@
 """GPU parity: the MoE layer backward against the oracle (oracle/backward.py).
 
 Stage by stage at small ragged sizes, end to end through the stage calls
-(routing driven by the oracle's logits, so the selection is identical), and
-sampled experts at the 16K-token size.  Bars: combine's d_yp within one bf16
+(routing driven by the oracle's logits, so the selection is identical), and at
+the 16K-token size a sampled expert and a 256-token gradient subset (dx,
+d_topk_w, dW_g, two experts' weight gradients).  Bars: combine's d_yp within one bf16
 ulp of the fp64 product (it is one rounded product), fp32 sums within 1e-5
 relative, bf16 expert products within 2e-2 relative (max over the tensor,
 relative to its largest entry), as for the forward FFN."""
+import concurrent.futures as cf
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -246,6 +250,91 @@ def test_layer_backward_v3_sampled_expert():
     print(f"  expert {e}: {hi - lo} rows, errors {errs}")
     assert max(errs) <= 2e-2
     del ex, r, b
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_layer_backward_v3_token_subset():
+    """16K-token size, the gradient of a loss that depends on 256 sampled
+    tokens only (grad_out zero on every other token), through the stage calls
+    with the oracle's routing: dx of every token (exactly zero outside the
+    sample), d_topk_w and dx of the sample, dW_g, and the weight gradients of
+    the two experts the sample reaches most, against the oracle run on the
+    sample alone."""
+    dev = need_gpu()
+    cfg = C.get("v3")
+    print("backward v3 token subset", flush=True)
+    inp = gen.make_router(cfg, device=dev)
+    ex = gen.make_experts(cfg, device=dev)
+    x = inp["x"]
+    xh, wg = host(x), host(inp["w_gate"])
+    L = OR.gate_logits(xh, wg)
+    ridx, rw = OR.route_from_logits(L, host(inp["bias"]), cfg.G, cfg.M, cfg.k, cfg.gk)
+    sh = M.shape(cfg.T, cfg.d, cfg.E, cfg.G, cfg.M, cfg.k, cfg.d_ff, cfg.gk)
+    Ld = dev_f32(L, dev)
+    _, idx, w, bc = M.route(sh, None, None, inp["bias"], None, logits=Ld, logits_in=True)
+    b = M.dispatch(sh, idx, bc, x)
+    rows = cfg.T * cfg.k
+    yp, _, _ = M.expert_ffn(b["offsets"], rows, b["xp"], ex["w13"], ex["w2"])
+    S = np.sort(np.random.default_rng(3).choice(cfg.T, 256, replace=False))
+    mask = torch.zeros((cfg.T, 1), device=dev)
+    mask[torch.from_numpy(S).to(dev)] = 1.0
+    g = (gen.normal((cfg.T, cfg.d), 1.0, dev, 0, 98) * mask).to(torch.bfloat16)
+    d_yp, d_w = M.combine_backward(sh, b["dest"], w, yp, g)
+    r = M.expert_ffn_backward(b["offsets"], rows, b["xp"], ex["w13"], ex["w2"], d_yp)
+    s = M.expert_ffn_backward(None, cfg.T, x, ex["sh_w13"], ex["sh_w2"], g)
+    dx = M.dispatch_backward(sh, b["dest"], r["d_xp"], d_extra=s["d_xp"])
+    _, dWg = M.route_backward(sh, x, inp["w_gate"], Ld, idx, d_w, dx)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx), ridx)
+    dx_h = host(dx)
+    outside = np.ones(cfg.T, bool)
+    outside[S] = False
+    assert np.all(dx_h[outside] == 0.0)
+
+    # oracle on the sample, one expert at a time
+    xs, gs = xh[S], host(g)[S]
+    users = {}
+    for i, t in enumerate(S):
+        for j in range(cfg.k):
+            users.setdefault(int(ridx[t, j]), []).append((i, j))
+    top2 = sorted(users, key=lambda e: (-len(users[e]), e))[:2]
+
+    def part(item):
+        e, uses = item
+        w13, w2 = host(ex["w13"][e]), host(ex["w2"][e])
+        ii = [i for i, _ in uses]
+        wj = np.array([float(rw[S[i], j]) for i, j in uses])[:, None]
+        y, _ = OF.expert_forward(xs[ii], w13, w2)
+        d_wj = np.sum(gs[ii].astype(np.float64) * y, axis=1)            # <g_t, y_e(x_t)>
+        dX, dW13, dW2 = OB.expert_backward(xs[ii], w13, w2, wj * gs[ii])
+        return e, uses, d_wj, dX, (dW13, dW2) if e in top2 else None
+
+    r_dw = np.zeros((S.size, cfg.k))
+    r_dx = np.zeros((S.size, cfg.d))
+    r_wg = {}
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with cf.ThreadPoolExecutor(workers) as pool:
+        for n_done, (e, uses, d_wj, dX, wgrads) in enumerate(pool.map(part, sorted(users.items()))):
+            if n_done % 32 == 31:
+                print(f"  oracle: {n_done + 1} of {len(users)} experts", flush=True)
+            for (i, j), v in zip(uses, d_wj):
+                r_dw[i, j] = v
+            np.add.at(r_dx, [i for i, _ in uses], dX)
+            if wgrads is not None:
+                r_wg[e] = wgrads
+    dXs, _, _ = OB.expert_backward(xs, host(ex["sh_w13"][0]), host(ex["sh_w2"][0]), gs)
+    r_dxg, r_dWg, _ = OB.gate_backward(xs, wg, L[S], ridx[S], r_dw)
+    r_dx = r_dx + dXs + r_dxg
+    errs = {"dx": rel_max_err(dx_h[S], r_dx), "d_w": rel_max_err(host(d_w)[S], r_dw),
+            "dWg": rel_max_err(host(dWg), r_dWg)}
+    for e in top2:
+        errs[f"dw13[{e}]"] = rel_max_err(host(r["dw13"][e]), r_wg[e][0])
+        errs[f"dw2[{e}]"] = rel_max_err(host(r["dw2"][e]), r_wg[e][1])
+    print(f"  {S.size} tokens reach {len(users)} experts;", {k_: f"{v:.2e}" for k_, v in errs.items()})
+    for k_, v in errs.items():
+        assert v <= 2e-2, (k_, v)
+    del ex, r, s, b
     torch.cuda.empty_cache()
 
 

@@ -1,16 +1,26 @@
 """GPU parity for the fp8 workload: e4m3 quantisation (bit-exact against the
 oracle's definition), fp8 dispatch, the e4m3 grouped FFN and the fp8 layer.
 
-The workload's expert weights are e4m3 with fp32 128x128 block scales; the
-activation quantisation inside dispatch and the re-quantisation of h between
-the two products are steps of the method.  So FFN/layer outputs must be within
-6e-2 relative max error of the oracle's fp64 result on the bf16 activations and
-the (dequantised) e4m3 weights, the oracle quantising the weights itself.  Two
-more comparisons: against the oracle's full quantise-dequantise emulation
-(only accumulation order and h-rounding decisions differ: <= 2e-2) and, as a
-sanity bound, against fully unquantised fp32 weights (<= 1e-1; four e4m3
-roundings of ~3% rms each put that error near 6%)."""
+Two references, one rule each, applied to every case alike:
+  * the oracle's emulation of the whole fp8 method (activations quantised per
+    1x128 tile, weights per 128x128 block, h re-quantised per 1x128 tile;
+    everything else in fp64): the kernel differs from it only in accumulation
+    order and in the rounding decisions of h that land on a different e4m3
+    code, so every output must be within 2e-2 relative max error of it and
+    inside an elementwise bound derived from those two effects (one e4m3 code
+    step of every h element through |W2|, the bf16 rounding of the output,
+    and fp32 accumulation);
+  * the workload's own tolerance, 6e-2 relative max error, as a statistic
+    over a layer output of the fp8 workload (V3 shapes, a sample of at least
+    256 tokens): against the oracle's fp64 layer on the bf16 activations and
+    the e4m3 weights (dequantised), the oracle quantising the weights itself.
+The FFN kernel cases also print their error against the e4m3-weight and the
+fully unquantised references, for information: a single-row output measured
+6.13e-2 against the first (its max |ref| is small next to the quantisation
+noise of its own activations), and every case 6-8% against the second (four
+e4m3 roundings of ~3% rms each)."""
 import concurrent.futures as cf
+import os
 
 import numpy as np
 import pytest
@@ -90,6 +100,39 @@ def _deq_blocks(w):
     return Q.dequant_blocks(*Q.quantize_blocks(w))
 
 
+def _code_step(codes, scale, tile=128):
+    """Per element of an e4m3 row-quantised matrix: the larger distance from its
+    value to a neighbouring code's value, times its tile scale (how far one
+    rounding decision that lands on another code moves it)."""
+    vals = Q.e4m3_table()
+    c = (codes & 0x7F).astype(np.int64)
+    up = vals[np.minimum(c + 1, 126)] - vals[c]
+    down = vals[c] - vals[np.maximum(c - 1, 0)]
+    step = np.maximum(up, down)
+    n, cols = codes.shape
+    return (step.reshape(n, cols // tile, tile) * np.asarray(scale, np.float64)[:, :, None]).reshape(n, cols)
+
+
+def _emulate(xh, offsets, d13, d2):
+    """The oracle's fp8 method on the rows of each group: returns the output
+    and the elementwise bound on a kernel's distance from it."""
+    xd = Q.dequant_rows(*Q.quantize_rows(xh))
+    emu = np.zeros((xh.shape[0], d2[0].shape[0]))
+    bound = np.zeros_like(emu)
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        h = OF.expert_hidden(xd[lo:hi], d13[e]).astype(np.float32)
+        hq, hs = Q.quantize_rows(h)
+        hd = Q.dequant_rows(hq, hs)
+        w2a = np.abs(d2[e])
+        emu[lo:hi] = hd @ d2[e].T
+        bound[lo:hi] = (_code_step(hq, hs) @ w2a.T + 2.0 ** -8 * np.abs(emu[lo:hi])
+                        + 1e-5 * (np.abs(hd) @ w2a.T))
+    return emu, bound
+
+
 def _fp8_ffn_case(counts, d, d_ff, seed):
     dev = need_gpu()
     g = torch.Generator(device=dev).manual_seed(seed)
@@ -110,16 +153,17 @@ def _fp8_ffn_case(counts, d, d_ff, seed):
     d2 = np.stack([_deq_blocks(w2h[e]) for e in range(n_exp)])
     ref, _ = OF.grouped_ffn(xh, offsets, d13, d2)           # the workload's e4m3 weights
     raw, _ = OF.grouped_ffn(xh, offsets, w13h, w2h)         # fully unquantised
-    # emulation: the oracle's own quantisation of x and h as well
-    xd = Q.dequant_rows(*Q.quantize_rows(xh))
-    emu = np.zeros_like(ref)
-    for e in range(n_exp):
-        lo, hi = int(offsets[e]), int(offsets[e + 1])
-        if hi == lo:
-            continue
-        h = OF.expert_hidden(xd[lo:hi], d13[e]).astype(np.float32)
-        emu[lo:hi] = Q.dequant_rows(*Q.quantize_rows(h)) @ d2[e].T
-    return host(yp)[: int(offsets[-1])], ref, emu, raw
+    emu, bound = _emulate(xh, offsets, d13, d2)
+    return host(yp)[: int(offsets[-1])], ref, emu, raw, bound
+
+
+def _check_ffn(got, ref, emu, raw, bound):
+    e_ref, e_emu, e_raw = rel_max_err(got, ref), rel_max_err(got, emu), rel_max_err(got, raw)
+    over = np.abs(got - emu) / np.maximum(bound, 1e-30)
+    print(f"  vs emulation {e_emu:.3e} (elementwise: worst {over.max():.2f} of the bound)  "
+          f"[information: vs e4m3 weights {e_ref:.3e}, vs unquantised {e_raw:.3e}]")
+    assert e_emu <= 2e-2
+    assert np.all(np.abs(got - emu) <= bound)
 
 
 @pytest.mark.parametrize("d,d_ff", [(512, 512), (1024, 768), (768, 256), (256, 512)])
@@ -129,32 +173,20 @@ def test_fp8_ffn_widths(d, d_ff):
     and below it (256, taken by the other kernel), with ragged groups."""
     counts = [0, 1, 127, 128, 129, 300, 0, 5]
     print(f"fp8 ffn d={d} d_ff={d_ff} {counts}", flush=True)
-    got, ref, emu, raw = _fp8_ffn_case(counts, d, d_ff, seed=d + d_ff)
-    e_ref, e_emu, e_raw = rel_max_err(got, ref), rel_max_err(got, emu), rel_max_err(got, raw)
-    print(f"  vs e4m3 weights {e_ref:.3e}  vs emulation {e_emu:.3e}  vs unquantised {e_raw:.3e}")
-    assert e_emu <= 2e-2
-    assert e_ref <= 6e-2
-    assert e_raw <= 1e-1
+    _check_ffn(*_fp8_ffn_case(counts, d, d_ff, seed=d + d_ff))
 
 
 @pytest.mark.parametrize("counts", [[0, 1, 127, 128, 129, 300, 0, 5], [513, 0, 0, 255], [1]])
 def test_fp8_ffn_ragged(counts):
     print(f"fp8 ffn {counts}", flush=True)
-    got, ref, emu, raw = _fp8_ffn_case(counts, 1024, 256, seed=sum(counts) + len(counts))
-    e_ref, e_emu, e_raw = rel_max_err(got, ref), rel_max_err(got, emu), rel_max_err(got, raw)
-    print(f"  vs e4m3 weights {e_ref:.3e}  vs emulation {e_emu:.3e}  vs unquantised {e_raw:.3e}")
-    assert e_emu <= 2e-2
-    # The tolerances are statistics of a whole output (max error over max
-    # value); a group of a handful of rows is an edge case for the tile logic,
-    # checked by the emulation bound alone.
-    if sum(counts) >= 64:
-        assert e_ref <= 6e-2
-        assert e_raw <= 1e-1
+    _check_ffn(*_fp8_ffn_case(counts, 1024, 256, seed=sum(counts) + len(counts)))
 
 
+@pytest.mark.timeout(900)
 def test_fp8_layer_v3_sampled_tokens():
     """V3 shapes, fp8 expert GEMMs (routed and shared) at full size, in the
-    benchmark's launch configuration; sampled tokens against the oracle."""
+    benchmark's launch configuration: 256 sampled tokens (plus the last one)
+    against the oracle, every expert they reach quantised by the oracle."""
     dev = need_gpu()
     cfg, inp, o = router_inputs("v3_fp8")
     print("fp8 layer v3 (sampled tokens)", flush=True)
@@ -167,25 +199,48 @@ def test_fp8_layer_v3_sampled_tokens():
     bad = set(np.nonzero((idx_g != o["idx"]).any(1))[0].tolist())
     assert len(bad) <= cfg.T // 1000
     rng = np.random.default_rng(1)
-    toks = [int(t) for t in rng.choice(cfg.T, 2, replace=False) if int(t) not in bad]
+    toks = sorted({int(t) for t in rng.choice(cfg.T, 257, replace=False)} | {cfg.T - 1})
+    toks = [t for t in toks if t not in bad][:257]
+    assert len(toks) >= 256
     out = host(out_d[torch.tensor(toks, device=dev)])
-    need = sorted({int(e) for t in toks for e in o["idx"][t]})
-    # the oracle quantises the weights it needs itself (one expert per thread)
-    with cf.ThreadPoolExecutor(8) as pool:
-        d13 = dict(zip(need, pool.map(lambda e: _deq_blocks(host(ex["w13"][e])), need)))
-        d2 = dict(zip(need, pool.map(lambda e: _deq_blocks(host(ex["w2"][e])), need)))
-        sh13, sh2 = pool.map(_deq_blocks, [host(ex["sh_w13"][0]), host(ex["sh_w2"][0])])
-    refs = []
+    xs = o["x"][toks]
+    xd = Q.dequant_rows(*Q.quantize_rows(xs))
+    pos = {t: i for i, t in enumerate(toks)}
+    users = {}
     for t in toks:
-        x = o["x"][t:t + 1]
-        y, _ = OF.expert_forward(x, sh13, sh2)
         for j in range(cfg.k):
-            e = int(o["idx"][t, j])
-            ye, _ = OF.expert_forward(x, d13[e], d2[e])
-            y = y + float(o["w"][t, j]) * ye
-        refs.append(y[0])
-    err = rel_max_err(out, np.stack(refs))
-    print(f"  tokens {toks} rel max err vs e4m3 weights {err:.3e}")
-    assert err <= 6e-2
+            users.setdefault(int(o["idx"][t, j]), []).append((pos[t], float(o["w"][t, j])))
+    print(f"  {len(toks)} tokens reach {len(users)} experts", flush=True)
+    n = len(toks)
+
+    def expert_part(item):
+        # one expert at a time (its fp32 weights are 176 MB): the oracle
+        # quantises them, then evaluates its tokens in fp64, as the reference
+        # (bf16 activations) and as the emulation (e4m3 activations and h)
+        e, uses = item
+        w13 = host(ex["w13"][e]) if e >= 0 else host(ex["sh_w13"][0])
+        w2 = host(ex["w2"][e]) if e >= 0 else host(ex["sh_w2"][0])
+        d13, d2 = _deq_blocks(w13), _deq_blocks(w2)
+        rows = [i for i, _ in uses]
+        wts = np.array([w for _, w in uses])[:, None]
+        y_ref, _ = OF.expert_forward(xs[rows], d13, d2)
+        h = OF.expert_hidden(xd[rows], d13).astype(np.float32)
+        y_emu = Q.dequant_rows(*Q.quantize_rows(h)) @ d2.T
+        return rows, wts * y_ref, wts * y_emu
+
+    work = sorted(users.items()) + [(-1, [(i, 1.0) for i in range(n)])]   # -1: the shared expert
+    ref = np.zeros((n, cfg.d))
+    emu = np.zeros((n, cfg.d))
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with cf.ThreadPoolExecutor(workers) as pool:
+        for i, (rows, yr, ye) in enumerate(pool.map(expert_part, work)):
+            np.add.at(ref, rows, yr)
+            np.add.at(emu, rows, ye)
+            if i % 32 == 31:
+                print(f"  oracle: {i + 1} of {len(work)} experts", flush=True)
+    e_ref, e_emu = rel_max_err(out, ref), rel_max_err(out, emu)
+    print(f"  {n} tokens: rel max err vs e4m3 weights {e_ref:.3e}, vs emulation {e_emu:.3e}")
+    assert e_ref <= 6e-2
+    assert e_emu <= 2e-2
     del layer, ex
     torch.cuda.empty_cache()
