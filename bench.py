@@ -180,7 +180,23 @@ def backward_bench(a, cfg, layer, x, ev, torch, alg, rows):
             "flops_note": "12*d*d_ff per row: d_h + d_x + dW2 + dW13 (the training forward keeps [a|u])"}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, inp, ex, S, ids=None):
+    """The oracle on the host: route and dispatch on all T tokens (logits in
+    fp64 BLAS, selection and the stable permutation in numpy), the expert FFNs
+    and the combine on the first S tokens (streaming one expert's weights at a
+    time); each stage's seconds per token from its own token count, the layer
+    rate from their sum."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info, threadpool_limits
@@ -188,7 +204,9 @@ def cpu_baseline(cfg, inp, ex, S, ids=None):
     from oracle import combine as OC, dispatch as OD, ffn as OF, hash_route as OH, route as OR
 
     S = min(S, cfg.T)
-    x = inp["x"][:S].float().cpu().numpy()
+    T = cfg.T
+    x_all = inp["x"].float().cpu().numpy()
+    x = x_all[:S]
     wg = inp["w_gate"].cpu().numpy()
     bias = inp["bias"].cpu().numpy()
     off = None if inp["logit_offset"] is None else inp["logit_offset"].cpu().numpy()
@@ -201,48 +219,57 @@ def cpu_baseline(cfg, inp, ex, S, ids=None):
     f = lambda t: t.float().numpy()
     st = {}
 
-    def route_dispatch():
+    def route_all():
         if ids is None:
-            _, idx_, w_ = OR.route(x, wg, bias, cfg.G, cfg.M, cfg.k, cfg.gk, off)
+            _, idx_, w_ = OR.route(x_all, wg, bias, cfg.G, cfg.M, cfg.k, cfg.gk, off)
         else:
-            idx_, w_ = OH.hash_route(ids[:S], cfg.E, cfg.k, HASH_SEED)
-        ta = time.perf_counter()
-        disp = OD.dispatch(idx_, cfg.E, cfg.e_begin, cfg.e_end)
-        return idx_, w_, disp, ta
+            idx_, w_ = OH.hash_route(ids, cfg.E, cfg.k, HASH_SEED)
+        return idx_, w_
 
     t0 = time.perf_counter()
-    idx, w, (counts, offsets, dest, src), t1 = route_dispatch()
-    xp = OD.pack(x, src)
+    idx, w = route_all()
+    t1 = time.perf_counter()
+    _, _, _, src_all = OD.dispatch(idx, cfg.E, cfg.e_begin, cfg.e_end)
+    OD.pack(x_all, src_all)
     t2 = time.perf_counter()
-    yp, _ = OF.grouped_ffn(xp, offsets, None, None, weight_fn=lambda i: (f(w13_h[i]), f(w2_h[i])))
+    # the FFN and combine on the first S tokens' pairs
+    counts, offsets, dest, src = OD.dispatch(idx[:S], cfg.E, cfg.e_begin, cfg.e_end)
+    xp = OD.pack(x, src)
     t3 = time.perf_counter()
+    yp, _ = OF.grouped_ffn(xp, offsets, None, None, weight_fn=lambda i: (f(w13_h[i]), f(w2_h[i])))
+    t4 = time.perf_counter()
     ysh = None
     if not cfg.local:
         ysh, _ = OF.expert_forward(x, f(sh13), f(sh2))
-    t4 = time.perf_counter()
-    if cfg.local:
-        out = OC.combine(yp, dest, w, out_init=np.zeros((S, cfg.d)))
-    else:
-        out = OC.combine(yp, dest, w, ysh=ysh)
     t5 = time.perf_counter()
-    t = t5 - t0
-    for name, a, b in (("route", t0, t1), ("dispatch", t1, t2), ("routed_experts", t2, t3),
-                       ("shared_expert", t3, t4), ("combine", t4, t5)):
-        st[name] = {"seconds": b - a, "tokens_per_s": S / max(b - a, 1e-9)}
+    if cfg.local:
+        OC.combine(yp, dest, w[:S], out_init=np.zeros((S, cfg.d)))
+    else:
+        OC.combine(yp, dest, w[:S], ysh=ysh)
+    t6 = time.perf_counter()
+    per_tok = {"route": (t1 - t0) / T, "dispatch": (t2 - t1) / T, "routed_experts": (t4 - t3) / S,
+               "shared_expert": (t5 - t4) / S, "combine": (t6 - t5) / S}
+    ntok = {"route": T, "dispatch": T, "routed_experts": S, "shared_expert": S, "combine": S}
+    for name, spt in per_tok.items():
+        st[name] = {"seconds": spt * ntok[name], "tokens": ntok[name], "tokens_per_s": 1.0 / max(spt, 1e-12)}
     # route and dispatch again on one core
     with threadpool_limits(1):
         u0 = time.perf_counter()
-        _, _, (_, _, _, src1), u1 = route_dispatch()
-        OD.pack(x, src1)
+        idx1, _ = route_all()
+        u1 = time.perf_counter()
+        _, _, _, src1 = OD.dispatch(idx1, cfg.E, cfg.e_begin, cfg.e_end)
+        OD.pack(x_all, src1)
         u2 = time.perf_counter()
-    st["route_one_core"] = {"seconds": u1 - u0, "tokens_per_s": S / max(u1 - u0, 1e-9)}
-    st["dispatch_one_core"] = {"seconds": u2 - u1, "tokens_per_s": S / max(u2 - u1, 1e-9)}
+    st["route_one_core"] = {"seconds": u1 - u0, "tokens": T, "tokens_per_s": T / max(u1 - u0, 1e-9)}
+    st["dispatch_one_core"] = {"seconds": u2 - u1, "tokens": T, "tokens_per_s": T / max(u2 - u1, 1e-9)}
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": S / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {S} of the {cfg.T} tokens, whole layer (route, dispatch, all routed "
-                      f"experts they reach, shared expert, combine) in fp64 numpy; {t:.1f} s; "
-                      f"host affinity {len(os.sched_getaffinity(0))} cpus",
-            "seconds": t, "stages": st}
+    total = t6 - t0
+    return {"value": 1.0 / sum(per_tok.values()), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_affinity_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"route and dispatch on all {T} tokens; expert FFNs, shared expert and combine on "
+                      f"the first {S} tokens (every routed expert they reach), fp64 numpy; value = 1 / sum "
+                      f"of the stages' seconds per token; {total:.1f} s in all",
+            "seconds": total, "stages": st}
 
 
 def up_variants(torch, M, cfg, layer, x, ids):
@@ -351,6 +378,37 @@ def main():
     nblk = layer.block_counts.shape[0]
     bu_bytes = nblk * cfg.E * 4 + cfg.E * 4 * 3
 
+    # route selection alone (affinities, group and expert selection, weights,
+    # block histogram) from the step's logits, back to back
+    sel_us = None
+    if a.router == "topk":
+        sel_idx, sel_w, sel_bc = (torch.empty_like(layer.idx), torch.empty_like(layer.topk_w),
+                                  torch.empty_like(layer.block_counts))
+        rs0, rs1 = ev(), ev()
+        rs0.record()
+        for _ in range(reps):
+            M.route(layer.sh, None, None, layer.bias, layer.logit_offset, logits=layer.logits, logits_in=True,
+                    idx=sel_idx, w=sel_w, block_counts=sel_bc)
+        rs1.record()
+        torch.cuda.synchronize()
+        sel_us = rs0.elapsed_time(rs1) / reps * 1e3
+        assert torch.equal(sel_idx, layer.idx)
+
+    # this GPU's row of the expert-parallel send matrix: packed rows per
+    # destination group (the slice of the group-ordered buffer each group's
+    # owner would receive), and rows per local expert
+    cnt = layer.dbufs["counts"].cpu().tolist()
+    gsz = cfg.E // cfg.G
+    per_group = [0] * cfg.G
+    for i, c in enumerate(cnt):
+        per_group[(cfg.e_begin + i) // gsz] += c
+    srt = sorted(cnt)
+    send_row = {"rows_per_group": per_group, "local_experts": [cfg.e_begin, cfg.e_end],
+                "rows_per_expert": {"min": srt[0], "median": srt[len(srt) // 2], "max": srt[-1],
+                                    "max_over_mean": srt[-1] / max(sum(srt) / len(srt), 1e-9)}}
+    if len(cnt) <= 8:
+        send_row["rows_per_expert"]["all"] = cnt
+
     names = ("route", "dispatch", "ffn_up", "ffn_down", "shared", "combine")
     st_ms = {n: sum(m[i].elapsed_time(m[i + 1]) for m in marks) / a.steps for i, n in enumerate(names)}
     rows = int(layer.dbufs["offsets"][-1].item())
@@ -358,8 +416,18 @@ def main():
     peak_mm = PEAK_FP8_TFLOPS if cfg.dtype == "fp8" else PEAK_BF16_TFLOPS
     tf = lambda flops, ms: flops / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
     gbs = lambda byts, ms: byts / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+    if a.router == "topk":
+        sel_ms = sel_us * 1e-3
+        gate_ms = max(st_ms["route"] - sel_ms, 1e-9)
+        route_stage = {"ms": st_ms["route"], "gate_ms": gate_ms, "gate_tflops": tf(alg["route_flops"], gate_ms),
+                       "gate_frac_mfma": tf(alg["route_flops"], gate_ms) / PEAK_BF16_TFLOPS,
+                       "select_us": sel_us, "select_bytes": alg["route_select_bytes"],
+                       "select_gb_s": gbs(alg["route_select_bytes"], sel_ms),
+                       "select_frac_hbm": gbs(alg["route_select_bytes"], sel_ms) / PEAK_HBM_GBS,
+                       "note": "gate_ms = route stage minus the selection timed alone (the weight planes' "
+                               "preparation counts with the gate product); gate_tflops on 2*T*d*E useful flops"}
     stages = {
-        "route": ({"ms": st_ms["route"], "gate_tflops": tf(alg["route_flops"], st_ms["route"])}
+        "route": (route_stage
                   if a.router == "topk" else
                   {"ms": st_ms["route"], "kind": "hash router",
                    "bytes": cfg.T * 4 + cfg.T * cfg.k * 8 + ((cfg.T + 63) // 64) * cfg.E * 4}),
@@ -403,6 +471,7 @@ def main():
                      "algorithmic_bytes_per_launch": alg["ffn_up_bytes"](rows)},
         "gemm_mfma_frac": tf(gemm_flops, gemm_ms) / peak_mm,
         "stages": stages,
+        "send_matrix_row": send_row,
         "after_step": {"bias_update": {"us": bu_us, "bytes": bu_bytes, "gb_s": bu_bytes / (bu_us * 1e-6) / 1e9,
                                        "bound": "latency (one work-group)"}},
     }

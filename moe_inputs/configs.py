@@ -90,11 +90,16 @@ V3_SKEW_EP0 = MoEConfig(
     skew=True, local=(0, 4),
     description="one expert-parallel rank's 4 experts under Zipf(1.2) routing skew, fp32 scatter-add output")
 
+V3_SKEW_EP63 = MoEConfig(
+    name="v3_skew_ep63", T=16384, d=7168, E=256, G=8, k=8, M=4, d_ff=2048, dtype="bf16",
+    skew=True, local=(252, 256),
+    description="the coldest expert-parallel rank's 4 experts (252-255) under the same Zipf(1.2) skew")
+
 V3_FP8 = MoEConfig(
     name="v3_fp8", T=16384, d=7168, E=256, G=8, k=8, M=4, d_ff=2048, dtype="fp8",
     description="V3 shapes with e4m3 activations (1x128 fp32 scales) and weights (128x128 fp32 scales)")
 
-CONFIGS = {c.name: c for c in (TINY, FLASH, V3, V3_SKEW_EP0, V3_FP8)}
+CONFIGS = {c.name: c for c in (TINY, FLASH, V3, V3_SKEW_EP0, V3_SKEW_EP63, V3_FP8)}
 
 
 def get(name: str) -> MoEConfig:

@@ -13,6 +13,7 @@ import os
 import numpy as np
 import pytest
 import torch
+from threadpoolctl import threadpool_limits
 
 import moe_expert_routing_sqrt_amd as M
 from moe_inputs import configs as C, generate as gen
@@ -314,7 +315,8 @@ def test_layer_backward_v3_token_subset():
     r_dx = np.zeros((S.size, cfg.d))
     r_wg = {}
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
-    with cf.ThreadPoolExecutor(workers) as pool:
+    # (one BLAS thread per worker: the pool is the parallelism)
+    with threadpool_limits(1), cf.ThreadPoolExecutor(workers) as pool:
         for n_done, (e, uses, d_wj, dX, wgrads) in enumerate(pool.map(part, sorted(users.items()))):
             if n_done % 32 == 31:
                 print(f"  oracle: {n_done + 1} of {len(users)} experts", flush=True)

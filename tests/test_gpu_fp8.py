@@ -25,6 +25,7 @@ import os
 import numpy as np
 import pytest
 import torch
+from threadpoolctl import threadpool_limits
 
 import moe_expert_routing_sqrt_amd as M
 from moe_inputs import configs as C, generate as gen
@@ -232,7 +233,8 @@ def test_fp8_layer_v3_sampled_tokens():
     ref = np.zeros((n, cfg.d))
     emu = np.zeros((n, cfg.d))
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
-    with cf.ThreadPoolExecutor(workers) as pool:
+    # (one BLAS thread per worker: the pool is the parallelism)
+    with threadpool_limits(1), cf.ThreadPoolExecutor(workers) as pool:
         for i, (rows, yr, ye) in enumerate(pool.map(expert_part, work)):
             np.add.at(ref, rows, yr)
             np.add.at(emu, rows, ye)

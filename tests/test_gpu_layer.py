@@ -19,6 +19,7 @@ import os
 import numpy as np
 import pytest
 import torch
+from threadpoolctl import threadpool_limits
 
 import moe_expert_routing_sqrt_amd as M
 from moe_inputs import configs as C, generate as gen
@@ -99,7 +100,8 @@ def _oracle_tokens(cfg, o, ex, toks, dev):
         work.append((-1, [(i, 1.0) for i in range(len(toks))]))
     out = np.zeros((len(toks), cfg.d))
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
-    with cf.ThreadPoolExecutor(workers) as pool:
+    # (one BLAS thread per worker: the pool is the parallelism)
+    with threadpool_limits(1), cf.ThreadPoolExecutor(workers) as pool:
         for i, (rows, y) in enumerate(pool.map(part, work)):
             np.add.at(out, rows, y)
             if i % 32 == 31:
@@ -152,7 +154,7 @@ def _forward_with_oracle_routing(layer, cfg, o, x, dev):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["v3", "v3_skew_ep0"])
+@pytest.mark.parametrize("name", ["v3", "v3_skew_ep0", "v3_skew_ep63"])
 def test_layer_v3_sampled_tokens(name):
     """Full V3 size (and one expert-parallel rank's share under skew): 1024
     sampled tokens plus the last one; the flipped tokens are listed and
