@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=512, help="tokens the CPU oracle runs (0: skip)")
     ap.add_argument("--router", default="topk", choices=("topk", "hash"),
                     help="topk: the affinity router; hash: experts from a hash of synthetic token ids")
+    ap.add_argument("--shared", default="merged", choices=("merged", "separate"),
+                    help="merged: the shared expert is one more group of the routed expert launches; "
+                         "separate: a call of its own after them")
     ap.add_argument("--backward", action="store_true",
                     help="also time forward+backward steps (bf16 top-k workload) and report the backward")
     ap.add_argument("--copy-probe", action="store_true",
@@ -83,10 +86,12 @@ def workload_name(cfg, router="topk") -> str:
     return s
 
 
-def algorithmic(cfg):
+def algorithmic(cfg, merged=False):
     """Per-launch algorithmic work of each stage: the bytes the method must move
-    or the FLOPs it must compute, padding and re-reads excluded."""
+    or the FLOPs it must compute, padding and re-reads excluded.  merged: the
+    shared expert's rows are one more group of the routed expert launches."""
     T, d, E, k, d_ff = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    ms = T if merged else 0          # shared-expert rows inside the expert launches
     P = T * k if not cfg.local else None
     act = 4 if cfg.dtype == "f32" else 2
     # packed-row bytes: e4m3 codes plus one fp32 scale per 128 columns for fp8
@@ -96,13 +101,16 @@ def algorithmic(cfg):
         "route_flops": 2 * T * d * E,
         "route_select_bytes": T * E * 4 + E * 4 + T * k * 8 + ((T + 63) // 64) * E * 4,
         "dispatch_bytes": lambda rows: T * d * act + rows * packed + 12 * T * k,
-        "ffn_up_flops": lambda rows: 4 * d * d_ff * rows,
-        # packed rows in, the local experts' W1/W3 once, h out (+ scales for fp8)
-        "ffn_up_bytes": lambda rows: rows * packed + (cfg.e_end - cfg.e_begin) * 2 * d_ff * d * wbytes
-        + rows * (d_ff + 4 * (d_ff // 128) if cfg.dtype == "fp8" else d_ff * act)
-        + ((cfg.e_end - cfg.e_begin) * 2 * d_ff * d // (128 * 128) * 4 if cfg.dtype == "fp8" else 0),
-        "ffn_down_flops": lambda rows: 2 * d * d_ff * rows,
-        "shared_flops": 6 * d * d_ff * T,
+        "ffn_up_flops": lambda rows: 4 * d * d_ff * (rows + ms),
+        # rows in (packed, and the shared expert's own when merged), each
+        # expert's W1/W3 once, h out (+ scales for fp8)
+        "ffn_up_bytes": lambda rows: (rows + ms) * packed
+        + (cfg.e_end - cfg.e_begin + (1 if merged else 0)) * 2 * d_ff * d * wbytes
+        + (rows + ms) * (d_ff + 4 * (d_ff // 128) if cfg.dtype == "fp8" else d_ff * act)
+        + ((cfg.e_end - cfg.e_begin + (1 if merged else 0)) * 2 * d_ff * d // (128 * 128) * 4
+           if cfg.dtype == "fp8" else 0),
+        "ffn_down_flops": lambda rows: 2 * d * d_ff * (rows + ms),
+        "shared_flops": 0 if merged else 6 * d * d_ff * T,
         "combine_bytes": lambda rows: rows * d * act + 8 * T * k + (T * d * act if not cfg.local else 0)
         + T * d * (4 * 2 if cfg.local else act),
         "pairs": P,
@@ -333,7 +341,8 @@ def main():
     layer = M.MoELayer(cfg.T, cfg.d, cfg.E, cfg.G, cfg.M, cfg.k, cfg.d_ff, cfg.dtype, inp["w_gate"],
                        inp["bias"], ex["w13"], ex["w2"], ex["sh_w13"], ex["sh_w2"],
                        logit_offset=inp["logit_offset"], e_begin=cfg.e_begin, e_end=cfg.e_end,
-                       group_topk=cfg.gk, router=a.router, hash_seed=HASH_SEED)
+                       group_topk=cfg.gk, router=a.router, hash_seed=HASH_SEED,
+                       merge_shared=a.shared == "merged")
     x = inp["x"]
     ids = gen.token_ids(cfg, device=dev) if a.router == "hash" else None
     torch.cuda.synchronize()
@@ -412,7 +421,8 @@ def main():
     names = ("route", "dispatch", "ffn_up", "ffn_down", "shared", "combine")
     st_ms = {n: sum(m[i].elapsed_time(m[i + 1]) for m in marks) / a.steps for i, n in enumerate(names)}
     rows = int(layer.dbufs["offsets"][-1].item())
-    alg = algorithmic(cfg)
+    merged = bool(getattr(layer, "merge_shared", False))
+    alg = algorithmic(cfg, merged)
     peak_mm = PEAK_FP8_TFLOPS if cfg.dtype == "fp8" else PEAK_BF16_TFLOPS
     tf = lambda flops, ms: flops / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
     gbs = lambda byts, ms: byts / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
@@ -434,14 +444,17 @@ def main():
         "dispatch": {"ms": st_ms["dispatch"], "gb_s": gbs(alg["dispatch_bytes"](rows), st_ms["dispatch"])},
         "ffn_up": {"ms": st_ms["ffn_up"], "tflops": tf(alg["ffn_up_flops"](rows), st_ms["ffn_up"])},
         "ffn_down": {"ms": st_ms["ffn_down"], "tflops": tf(alg["ffn_down_flops"](rows), st_ms["ffn_down"])},
-        "shared": {"ms": st_ms["shared"], "tflops": tf(alg["shared_flops"] if layer.has_shared else 0,
-                                                        st_ms["shared"])},
+        "shared": ({"ms": st_ms["shared"], "merged": "the shared expert's tiles run in the ffn_up and "
+                                                      "ffn_down launches (counted there)"} if merged else
+                   {"ms": st_ms["shared"], "tflops": tf(alg["shared_flops"] if layer.has_shared else 0,
+                                                        st_ms["shared"])}),
         "combine": {"ms": st_ms["combine"], "gb_s": gbs(alg["combine_bytes"](rows), st_ms["combine"])},
     }
     for s in ("dispatch", "combine"):
         stages[s]["frac_hbm"] = stages[s]["gb_s"] / PEAK_HBM_GBS
     for s in ("ffn_up", "ffn_down", "shared"):
-        stages[s]["frac_mfma"] = stages[s]["tflops"] / peak_mm
+        if "tflops" in stages[s]:
+            stages[s]["frac_mfma"] = stages[s]["tflops"] / peak_mm
     gemm_ms = st_ms["ffn_up"] + st_ms["ffn_down"] + st_ms["shared"]
     gemm_flops = alg["ffn_up_flops"](rows) + alg["ffn_down_flops"](rows) + (alg["shared_flops"] if layer.has_shared else 0)
     up = stages["ffn_up"]
@@ -462,7 +475,9 @@ def main():
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02^2) weights, U(-0.1,0.1) bias)",
         "config": {"workload": workload_name(cfg, a.router), "router": a.router, "T": cfg.T, "d": cfg.d, "E": cfg.E, "G": cfg.G,
                    "k": cfg.k, "M": cfg.M, "d_ff": cfg.d_ff, "routed_rows": rows},
-        "roofline": {"kernel": "routed up-projection GEMM + SwiGLU (moe_expert_ffn MOE_FFN_UP)",
+        "roofline": {"kernel": ("expert up-projection GEMM + SwiGLU, the routed experts and the shared expert in "
+                                "one launch (moe_expert_ffn MOE_FFN_UP, shared expert as moe_ffn_extra)" if merged else
+                                "routed up-projection GEMM + SwiGLU (moe_expert_ffn MOE_FFN_UP)"),
                      "bound": "mfma", "achieved": up["tflops"], "peak": peak_mm, "unit": "TFLOP/s",
                      "frac": up["tflops"] / peak_mm,
                      "traffic": None if up_traffic is None else up_traffic["bytes"],

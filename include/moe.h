@@ -222,6 +222,35 @@ int moe_dispatch_noalloc(const moe_shape* shape, const int32_t* topk_idx, const 
                          float* xp_scale, moe_stream_t stream);
 
 /*
+ * moe_ffn_extra - one more group for moe_expert_ffn with buffers of its own:
+ * the shared expert (mastering-deepseek-v4 "MoE + Expert-Parallel Overlap
+ * (Exp08)", Implemented: shared experts are always active), computed with
+ * the routed experts so its tiles fill the same launches.  Its rows are its
+ * own (typically the T unpermuted token rows); types and layouts are the
+ * routed groups':
+ *   x [rows, d]   (+ x_scale [d/128, rows] for e4m3)   up-projection input
+ *   w13 [2*d_ff, d] (+ w13_scale [2*d_ff/128, d/128]), w2 [d, d_ff]
+ *                 (+ w2_scale [d/128, d_ff/128])
+ *   h [rows, d_ff] (+ h_scale [d_ff/128, rows])          intermediate
+ *   y [rows, d]                                          down-projection output
+ * The bf16 matrix-core products take it into the routed launches (its tiles
+ * after the routed ones); the other paths compute it in launches of its own
+ * that follow on the stream.  Results are the same either way.
+ */
+typedef struct moe_ffn_extra {
+  int64_t rows;
+  const void* x;
+  const float* x_scale;
+  const void* w13;
+  const float* w13_scale;
+  const void* w2;
+  const float* w2_scale;
+  void* h;
+  float* h_scale;
+  void* y;
+} moe_ffn_extra;
+
+/*
  * moe_expert_ffn - grouped SwiGLU experts (mastering-deepseek-v4 Exp08,
  * Implemented: shared always-active experts plus fine-grained routed ones;
  * 6*d*d_ff flops per token-expert pair, i.e. three d x d_ff matrices).
@@ -245,6 +274,8 @@ int moe_dispatch_noalloc(const moe_shape* shape, const int32_t* topk_idx, const 
  *             h_scale [d_ff/128, max_rows] for e4m3 (block-major)
  *   yp        [max_rows, d] out: fp32 for MOE_F32, bf16 otherwise
  *   stages    MOE_FFN_UP, MOE_FFN_DOWN or MOE_FFN_ALL
+ *   extra     NULL, or one more group with its own buffers (moe_ffn_extra;
+ *             rows = 0: none), for the stages asked for
  *   ws        moe_workspace_size(MOE_OP_EXPERT_FFN, ...) bytes: the ticket
  *             counters the persistent products schedule their tiles with (one
  *             set for the up and one for the down product).  It must be
@@ -263,7 +294,7 @@ int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int3
                    int32_t d_ff, int dtype, const void* xp, const float* xp_scale,
                    const void* w13, const float* w13_scale, const void* w2,
                    const float* w2_scale, void* h, float* h_scale, void* yp, int stages,
-                   void* ws, size_t ws_bytes, moe_stream_t stream);
+                   const moe_ffn_extra* extra, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
  * moe_combine - out[t] = ysh[t] + sum_j topk_w[t,j] * yp[dest[t,j]]

@@ -27,7 +27,7 @@ from . import _lib
 from ._lib import (MOE_BF16, MOE_BWD_AU_SAVED, MOE_E4M3, MOE_F32, MOE_FFN_ALL, MOE_FFN_DOWN,  # noqa: F401
                    MOE_FFN_UP, MOE_FP8_TILE, MOE_OP_COMBINE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN,
                    MOE_OP_EXPERT_FFN_BACKWARD, MOE_OP_ROUTE, MOE_OP_ROUTE_BACKWARD, MOE_ROUTE_BLOCK,
-                   MOE_ROUTE_LOGITS_IN, MoeError, MoeShape)
+                   MOE_ROUTE_LOGITS_IN, MoeError, MoeFfnExtra, MoeShape)
 
 __all__ = ["shape", "workspace_bytes", "workspace", "route", "route_hash", "dispatch", "dispatch_noalloc",
            "combine_backward",
@@ -238,10 +238,13 @@ def expert_ffn(offsets: torch.Tensor, max_rows: int, xp: Optional[torch.Tensor],
                dtype: Optional[int] = None, xp_scale=None, w13_scale=None, w2_scale=None,
                h: Optional[torch.Tensor] = None, h_scale=None, yp: Optional[torch.Tensor] = None,
                stages: int = MOE_FFN_ALL, d: Optional[int] = None, d_ff: Optional[int] = None,
-               ws: Optional[torch.Tensor] = None):
+               ws: Optional[torch.Tensor] = None, extra: Optional[dict] = None):
     """Grouped SwiGLU experts over rows [offsets[i], offsets[i+1]) of xp.
     ws: the call's ticket-counter workspace (workspace(MOE_OP_EXPERT_FFN, ...):
-    zero-filled once, left zero by every call); a fresh one when None."""
+    zero-filled once, left zero by every call); a fresh one when None.
+    extra: one more group with buffers of its own (the shared expert), a dict
+    with rows, x, w13, w2, h, y (and x_scale, w13_scale, w2_scale, h_scale
+    for e4m3): moe_ffn_extra."""
     n_exp = offsets.numel() - 1
     ref = w13 if w13 is not None else w2
     dtype = _dt(ref) if dtype is None else dtype
@@ -267,9 +270,20 @@ def expert_ffn(offsets: torch.Tensor, max_rows: int, xp: Optional[torch.Tensor],
     _need(h, max_rows * d_ff, "h")
     if ws is None:
         ws = workspace(MOE_OP_EXPERT_FFN, None, dtype, dev)
+    ex = None
+    if extra is not None:
+        r = int(extra["rows"])
+        if stages & MOE_FFN_UP:
+            _need(extra["x"], r * d, "extra x")
+        if stages & MOE_FFN_DOWN:
+            _need(extra["y"], r * d, "extra y")
+        _need(extra["h"], r * d_ff, "extra h")
+        ex = MoeFfnExtra(r, *[_ptr(extra.get(k)) for k in ("x", "x_scale", "w13", "w13_scale", "w2", "w2_scale",
+                                                              "h", "h_scale", "y")])
     st = lib().moe_expert_ffn(n_exp, _ptr(offsets), max_rows, d, d_ff, dtype, _ptr(xp), _ptr(xp_scale),
                               _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(h),
-                              _ptr(h_scale), _ptr(yp), stages, _ptr(ws), _ws_len(ws), _stream())
+                              _ptr(h_scale), _ptr(yp), stages, None if ex is None else ctypes.byref(ex),
+                              _ptr(ws), _ws_len(ws), _stream())
     _lib.check("moe_expert_ffn", st)
     return yp, h, h_scale
 

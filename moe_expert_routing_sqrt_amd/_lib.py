@@ -33,6 +33,14 @@ class MoeShape(ctypes.Structure):
                 ("group_topk", ctypes.c_int32), ("d_ff", ctypes.c_int32)]
 
 
+class MoeFfnExtra(ctypes.Structure):
+    """moe_ffn_extra: one more expert-FFN group with buffers of its own."""
+    _fields_ = [("rows", ctypes.c_int64), ("x", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
+                ("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("w2_scale", ctypes.c_void_p), ("h", ctypes.c_void_p), ("h_scale", ctypes.c_void_p),
+                ("y", ctypes.c_void_p)]
+
+
 class MoeError(RuntimeError):
     def __init__(self, fn, status, msg):
         super().__init__(f"{fn} failed: {msg} ({status})")
@@ -54,7 +62,7 @@ SIGNATURES = {
     "moe_dispatch": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _I32, _I32, _P, _INT, _INT,
                             _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_expert_ffn": (_INT, [_I32, _P, _I64, _I32, _I32, _INT, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                              _INT, _P, _SZ, _P]),
+                              _INT, ctypes.POINTER(MoeFfnExtra), _P, _SZ, _P]),
     "moe_dispatch_noalloc": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _I32, _I32, _P, _INT, _INT,
                                     _P, _P, _P, _P, _P, _P, _P]),
     "moe_combine": (_INT, [ctypes.POINTER(MoeShape), _P, _P, _P, _INT, _P, _P, _INT, _INT, _P]),
@@ -82,14 +90,16 @@ def header_functions(path: str = HEADER):
 
 
 def load():
-    """Load the library; raises if it has not been built (no fallback path)."""
+    """Load the library (the in-tree build, or the file MOE_MI355X_LIB names);
+    raises if it is missing (no fallback path)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with "
+    path = os.environ.get("MOE_MI355X_LIB") or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
                           "`python -m moe_expert_routing_sqrt_amd.build` (hipcc, gfx950)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype = res

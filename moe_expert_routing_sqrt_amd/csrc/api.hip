@@ -244,7 +244,7 @@ int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int3
                    int32_t d_ff, int dtype, const void* xp, const float* xp_scale,
                    const void* w13, const float* w13_scale, const void* w2,
                    const float* w2_scale, void* h, float* h_scale, void* yp, int stages,
-                   void* ws, size_t ws_bytes, moe_stream_t stream) {
+                   const moe_ffn_extra* extra, void* ws, size_t ws_bytes, moe_stream_t stream) {
   if (n_exp <= 0 || n_exp > kMaxExperts || offsets == nullptr || max_rows < 0 || d <= 0 ||
       d_ff <= 0 || h == nullptr)
     return MOE_ERR_INVALID_ARG;
@@ -259,45 +259,69 @@ int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int3
       return MOE_ERR_INVALID_ARG;
     if (d % 256 != 0 || d_ff % 128 != 0) return MOE_ERR_UNSUPPORTED;
   }
+  if (extra != nullptr && extra->rows < 0) return MOE_ERR_INVALID_ARG;
+  const bool has_x = extra != nullptr && extra->rows > 0;
+  if (has_x) {
+    if (extra->h == nullptr || (up && (extra->x == nullptr || extra->w13 == nullptr)) ||
+        (down && (extra->w2 == nullptr || extra->y == nullptr)))
+      return MOE_ERR_INVALID_ARG;
+    if (dtype == MOE_E4M3 && (extra->h_scale == nullptr || (up && (extra->x_scale == nullptr ||
+                                                                    extra->w13_scale == nullptr)) ||
+                              (down && extra->w2_scale == nullptr)))
+      return MOE_ERR_INVALID_ARG;
+  }
   if (ws == nullptr || ws_bytes < 2 * kTicketSetBytes || !aligned256(ws)) return MOE_ERR_WORKSPACE;
-  if (max_rows == 0) return MOE_OK;
+  if (max_rows == 0 && !has_x) return MOE_OK;
   hipStream_t s = as_stream(stream);
   const bool mfma = dtype == MOE_BF16 && d % 256 == 0 && d_ff % 128 == 0 && d_ff >= 256;
   int* const tick_up = ticket_set(ws, 0);
   int* const tick_down = ticket_set(ws, 1);
-  if (up) {
-    hipError_t e;
+  // The bf16 matrix-core products take the extra group into their launches;
+  // every other path runs it after the routed groups as one group of its own
+  // (no offsets), reusing the ticket sets in stream order.
+  const moe_ffn_extra* merged = mfma && has_x ? extra : nullptr;
+  auto up_launch = [&](int n, const int32_t* off, int64_t rows, const void* x_, const float* xs_, const void* w13_,
+                       const float* w13s_, void* h_, float* hs_) -> hipError_t {
     if (dtype == MOE_E4M3 && ffn_fp8p_supported_k(d))
-      e = launch_ffn_up_fp8p(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint8_t*>(xp),
-                             xp_scale, static_cast<const uint8_t*>(w13), w13_scale,
-                             static_cast<uint8_t*>(h), h_scale, tick_up, s);
-    else if (dtype == MOE_E4M3)
-      e = launch_ffn_up_fp8(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint8_t*>(xp),
-                            xp_scale, static_cast<const uint8_t*>(w13), w13_scale,
-                            static_cast<uint8_t*>(h), h_scale, s);
-    else if (mfma)
-      e = launch_ffn_up_bf16(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint16_t*>(xp),
-                             static_cast<const uint16_t*>(w13), static_cast<uint16_t*>(h), tick_up, s);
-    else
-      e = launch_ffn_simt(MOE_FFN_UP, n_exp, offsets, max_rows, d, d_ff, dtype, xp, w13, h, s);
-    if (e != hipSuccess) return MOE_ERR_HIP;
+      return launch_ffn_up_fp8p(n, off, rows, d, d_ff, static_cast<const uint8_t*>(x_), xs_,
+                                static_cast<const uint8_t*>(w13_), w13s_, static_cast<uint8_t*>(h_), hs_, tick_up, s);
+    if (dtype == MOE_E4M3)
+      return launch_ffn_up_fp8(n, off, rows, d, d_ff, static_cast<const uint8_t*>(x_), xs_,
+                               static_cast<const uint8_t*>(w13_), w13s_, static_cast<uint8_t*>(h_), hs_, s);
+    if (mfma)
+      return launch_ffn_up_bf16(n, off, rows, d, d_ff, static_cast<const uint16_t*>(x_),
+                                static_cast<const uint16_t*>(w13_), static_cast<uint16_t*>(h_), tick_up, s, nullptr,
+                                merged);
+    return launch_ffn_simt(MOE_FFN_UP, n, off, rows, d, d_ff, dtype, x_, w13_, h_, s);
+  };
+  auto down_launch = [&](int n, const int32_t* off, int64_t rows, const void* h_, const float* hs_, const void* w2_,
+                         const float* w2s_, void* y_) -> hipError_t {
+    if (dtype == MOE_E4M3 && ffn_fp8p_supported_k(d_ff))
+      return launch_ffn_down_fp8p(n, off, rows, d, d_ff, static_cast<const uint8_t*>(h_), hs_,
+                                  static_cast<const uint8_t*>(w2_), w2s_, static_cast<uint16_t*>(y_), tick_down, s);
+    if (dtype == MOE_E4M3)
+      return launch_ffn_down_fp8(n, off, rows, d, d_ff, static_cast<const uint8_t*>(h_), hs_,
+                                 static_cast<const uint8_t*>(w2_), w2s_, static_cast<uint16_t*>(y_), s);
+    if (mfma)
+      return launch_ffn_down_bf16(n, off, rows, d, d_ff, static_cast<const uint16_t*>(h_),
+                                  static_cast<const uint16_t*>(w2_), static_cast<uint16_t*>(y_), tick_down, s, merged);
+    return launch_ffn_simt(MOE_FFN_DOWN, n, off, rows, d, d_ff, dtype, h_, w2_, y_, s);
+  };
+  const bool routed = max_rows > 0 || merged != nullptr;
+  const bool separate = has_x && merged == nullptr;
+  if (up) {
+    if (routed && up_launch(n_exp, offsets, max_rows, xp, xp_scale, w13, w13_scale, h, h_scale) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (separate && up_launch(1, nullptr, extra->rows, extra->x, extra->x_scale, extra->w13, extra->w13_scale,
+                              extra->h, extra->h_scale) != hipSuccess)
+      return MOE_ERR_HIP;
   }
   if (down) {
-    hipError_t e;
-    if (dtype == MOE_E4M3 && ffn_fp8p_supported_k(d_ff))
-      e = launch_ffn_down_fp8p(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint8_t*>(h),
-                               h_scale, static_cast<const uint8_t*>(w2), w2_scale,
-                               static_cast<uint16_t*>(yp), tick_down, s);
-    else if (dtype == MOE_E4M3)
-      e = launch_ffn_down_fp8(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint8_t*>(h),
-                              h_scale, static_cast<const uint8_t*>(w2), w2_scale,
-                              static_cast<uint16_t*>(yp), s);
-    else if (mfma)
-      e = launch_ffn_down_bf16(n_exp, offsets, max_rows, d, d_ff, static_cast<const uint16_t*>(h),
-                               static_cast<const uint16_t*>(w2), static_cast<uint16_t*>(yp), tick_down, s);
-    else
-      e = launch_ffn_simt(MOE_FFN_DOWN, n_exp, offsets, max_rows, d, d_ff, dtype, h, w2, yp, s);
-    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (routed && down_launch(n_exp, offsets, max_rows, h, h_scale, w2, w2_scale, yp) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (separate && down_launch(1, nullptr, extra->rows, extra->h, extra->h_scale, extra->w2, extra->w2_scale,
+                                extra->y) != hipSuccess)
+      return MOE_ERR_HIP;
   }
   return MOE_OK;
 }

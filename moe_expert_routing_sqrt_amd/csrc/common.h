@@ -129,17 +129,24 @@ struct TileInfo {
   int rows;     // valid rows in the tile (1..BM)
 };
 
-// s_pre: LDS scratch of kMapInts ints: the groups' row-tile prefix (n + 1
-// ints), then a copy of the offsets at s_pre + kMaxExperts + 1.
-constexpr int kMapInts = 2 * (kMaxExperts + 1);
+// s_pre: LDS scratch of kMapInts ints: the groups' row-tile prefix (up to
+// kMaxExperts + 2 ints: the groups of the offsets and one extra group), then
+// a copy of the row offsets at s_pre + kMapStride.
+constexpr int kMapStride = kMaxExperts + 2;
+constexpr int kMapInts = 2 * kMapStride;
+
+__device__ __forceinline__ const int* tile_map_offsets(const int* s_pre) { return s_pre + kMapStride; }
 
 // Builds the map in s_pre (ends with a work-group barrier); returns the number
-// of groups (1 when offsets is nullptr: one group of rows_total rows).  Must be
+// of groups (1 when offsets is nullptr: one group of rows_total rows).  With
+// extra_rows > 0 (and offsets given) one more group of that many rows follows
+// the n_exp groups: its rows are numbered on from offsets[n_exp].  Must be
 // called by all threads.
 __device__ __forceinline__ int tile_map_build(const int* __restrict__ offsets, int n_exp,
-                                              int64_t rows_total, int BM, int* s_pre) {
+                                              int64_t rows_total, int BM, int* s_pre,
+                                              int64_t extra_rows = 0) {
   const int tid = threadIdx.x;
-  int* const s_off = s_pre + kMaxExperts + 1;
+  int* const s_off = s_pre + kMapStride;
   if (offsets == nullptr) {
     n_exp = 1;
     if (tid == 0) {
@@ -173,6 +180,14 @@ __device__ __forceinline__ int tile_map_build(const int* __restrict__ offsets, i
     }
   }
   __syncthreads();
+  if (offsets != nullptr && extra_rows > 0) {
+    if (tid == 0) {
+      s_off[n_exp + 1] = s_off[n_exp] + static_cast<int>(extra_rows);
+      s_pre[n_exp + 1] = s_pre[n_exp] + static_cast<int>((extra_rows + BM - 1) / BM);
+    }
+    __syncthreads();
+    return n_exp + 1;
+  }
   return n_exp;
 }
 
@@ -180,7 +195,7 @@ __device__ __forceinline__ int tile_map_build(const int* __restrict__ offsets, i
 // with s_pre[g_lo] * n_tiles <= L (0 when nothing better is known).
 __device__ __forceinline__ void tile_map_decode(int L, int n_grp, int BM, int n_tiles,
                                                 const int* s_pre, int g_lo, TileInfo& ti) {
-  const int* const s_off = s_pre + kMaxExperts + 1;
+  const int* const s_off = s_pre + kMapStride;
   int g = g_lo;
   if (s_pre[g + 1] * n_tiles <= L) {
     int lo = g + 1, hi = n_grp;  // invariant: s_pre[lo]*nt <= L < s_pre[hi]*nt
@@ -219,9 +234,25 @@ __device__ __forceinline__ bool map_tile(const int* __restrict__ offsets, int n_
   return true;
 }
 
-// upper bound on the row tiles of a grouped launch
-inline int64_t max_row_tiles(int64_t max_rows, int n_exp, int BM) {
-  return (max_rows + BM - 1) / BM + (n_exp > 1 ? n_exp : 0);
+// Persistent launches deal the logical tiles to the XCDs in chunks of ch
+// tiles, round robin: the i-th ticket of XCD x is tile
+// ((i / ch) * kXcds + x) * ch + i % ch.  A chunk is one XCD's worth of
+// concurrently running tiles (32 CUs), which share weight and activation tiles
+// in its L2; dealing whole chunks round robin spreads every part of the tile
+// order (e.g. a trailing dense group) over all XCDs.  A launch of fewer than
+// kXcds * 32 tiles uses ch = ceil(total / kXcds), one chunk per XCD.
+constexpr int kChunkTiles = 32;
+__device__ __forceinline__ int xcd_chunk(int total) {
+  return max(1, min(kChunkTiles, (total + kXcds - 1) / kXcds));
+}
+__device__ __forceinline__ int xcd_tile(int i, int xcd, int ch) {
+  return ((i / ch) * kXcds + xcd) * ch + i % ch;
+}
+
+// upper bound on the row tiles of a grouped launch (plus an extra group of
+// extra_rows rows)
+inline int64_t max_row_tiles(int64_t max_rows, int n_exp, int BM, int64_t extra_rows = 0) {
+  return (max_rows + BM - 1) / BM + (n_exp > 1 ? n_exp : 0) + (extra_rows + BM - 1) / BM;
 }
 
 }  // namespace moe

@@ -108,6 +108,12 @@ struct FfnArgs {
   uint16_t* C2;            // SWIGLU_SAVE: [a | u] output [rows, 2*d_ff]
   float* Cf;               // ACC_F32: fp32 output [rows, ldc], accumulated into
   int* tickets;            // this launch's ticket counter set (kTicketInts, zero)
+  // an extra group after the n_exp groups of the offsets, with its own
+  // buffers (the shared expert of the layer); x_rows = 0: none
+  const uint16_t* Ax;      // [x_rows, K] activation rows
+  const uint16_t* Bx;      // its weights [*, K]
+  uint16_t* Cx;            // [x_rows, ldc] output
+  int64_t x_rows;
 };
 
 __device__ __forceinline__ void uniform_tile(TileInfo& t) {
@@ -149,17 +155,15 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
   const int xcd = blockIdx.x % kXcds;
   int* const tickets = p.tickets;
 
-  const int n_grp = tile_map_build(p.offsets, p.n_exp, p.rows_total, BM, s_map);
+  const int n_grp = tile_map_build(p.offsets, p.n_exp, p.rows_total, BM, s_map, p.x_rows);
   const int total = s_map[n_grp] * p.n_tiles;
-  const int per = (total + kXcds - 1) / kXcds;
-  const int l_begin = xcd * per;
-  const int l_end = min(total, l_begin + per);
+  const int ch = xcd_chunk(total);
   int tick_reg = 0;  // thread 0: the counter value fetched for the next tile
-  if (tid == 0) s_tick = l_begin + atomicAdd(&tickets[xcd * kCtrStride], 1);
+  if (tid == 0) s_tick = xcd_tile(atomicAdd(&tickets[xcd * kCtrStride], 1), xcd, ch);
   __syncthreads();
   const int l_first = __builtin_amdgcn_readfirstlane(s_tick);
 
-  if (l_first < l_end) {
+  if (l_first < total) {
     const int nsteps = p.K / BK;
     TileInfo ti, tn;
     tile_map_decode(l_first, n_grp, BM, p.n_tiles, s_map, 0, ti);
@@ -206,13 +210,23 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
     struct Src {
       const char* a;  // activation row of the tile's first row
       const char* b;  // the tile's first weight row
+      uint16_t* c;    // output row of the tile's first row
       int rows;
     };
     auto src_of = [&](const TileInfo& t) __attribute__((always_inline)) {
       Src x;
-      x.a = reinterpret_cast<const char*>(p.A + (int64_t)t.row0 * p.lda);
       const int64_t w0 = (int64_t)t.n_tile * (SWI ? BN / 2 : BN);
-      x.b = reinterpret_cast<const char*>(p.B + (int64_t)t.group * p.b_group_stride + w0 * p.K);
+      if (p.x_rows > 0 && t.group == p.n_exp) {
+        // the extra group: its own buffers, rows counted from its first
+        const int64_t r0 = t.row0 - tile_map_offsets(s_map)[p.n_exp];
+        x.a = reinterpret_cast<const char*>(p.Ax + r0 * p.lda);
+        x.b = reinterpret_cast<const char*>(p.Bx + w0 * p.K);
+        x.c = p.Cx + r0 * p.ldc;
+      } else {
+        x.a = reinterpret_cast<const char*>(p.A + (int64_t)t.row0 * p.lda);
+        x.b = reinterpret_cast<const char*>(p.B + (int64_t)t.group * p.b_group_stride + w0 * p.K);
+        x.c = p.C + (int64_t)t.row0 * p.ldc;
+      }
       x.rows = t.rows;
       return x;
     };
@@ -235,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
     // that tile.
     auto retarget = [&]() __attribute__((always_inline)) {
       const int l_next = __builtin_amdgcn_readfirstlane(s_tick);
-      nx = l_next < l_end;
+      nx = l_next < total;
       if (nx) {
         tile_map_decode(l_next, n_grp, BM, p.n_tiles, s_map, ti.group, tn);
         uniform_tile(tn);
@@ -253,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
       if (tid == 0) tick_reg = atomicAdd(&tickets[xcd * kCtrStride + zero], 1);
     };
     auto publish_ticket = [&]() __attribute__((always_inline)) {
-      if (tid == 0) s_tick = l_begin + tick_reg;
+      if (tid == 0) s_tick = xcd_tile(tick_reg, xcd, ch);
     };
 
     f32x16 acc[RM][RN];
@@ -450,7 +464,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
             const int r = lane >> 3, c = lane & 7;
             if (rb + r < ti.rows) {
               const uint4 val = *reinterpret_cast<const uint4*>(st + r * ST_PITCH + c * 16);
-              *reinterpret_cast<uint4*>(p.C + (grow0 + r) * p.ldc + col0 + wn * (TN / 2) + c * 8) = val;
+              *reinterpret_cast<uint4*>(cur.c + (int64_t)(rb + r) * p.ldc + col0 + wn * (TN / 2) + c * 8) = val;
             }
           } else {
             // 8 rows x 256 B: two chunks per lane
@@ -460,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
               const int r = q >> 4, c = q & 15;
               if (rb + r < ti.rows) {
                 const uint4 val = *reinterpret_cast<const uint4*>(st + r * ST_PITCH + c * 16);
-                *reinterpret_cast<uint4*>(p.C + (grow0 + r) * p.ldc + col0 + wn * TN + c * 8) = val;
+                *reinterpret_cast<uint4*>(cur.c + (int64_t)(rb + r) * p.ldc + col0 + wn * TN + c * 8) = val;
               }
             }
           }
@@ -564,7 +578,7 @@ hipError_t launch(FfnArgs& a, int64_t max_rows, hipStream_t s) {
   constexpr bool swi = MODE == MODE_SWIGLU || MODE == MODE_SWIGLU_SAVE;
   const int64_t b_rows = swi ? 2 * (int64_t)a.d_ff : (int64_t)a.n_tiles * BN;
   if ((int64_t)BM * a.lda * 2 >= (1LL << 31) || b_rows * a.K * 2 >= (1LL << 31)) return hipErrorInvalidValue;
-  const int64_t mt = max_row_tiles(max_rows, a.offsets == nullptr ? 1 : a.n_exp, BM);
+  const int64_t mt = max_row_tiles(max_rows, a.offsets == nullptr ? 1 : a.n_exp, BM, a.x_rows);
   const int64_t tiles = mt * a.n_tiles;
   if (tiles <= 0) return hipSuccess;
   // one work-group per CU (the LDS holds one), a multiple of the XCD count
@@ -578,9 +592,16 @@ hipError_t launch(FfnArgs& a, int64_t max_rows, hipStream_t s) {
 
 hipError_t launch_ffn_up_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
                               int d_ff, const uint16_t* xp, const uint16_t* w13, uint16_t* h,
-                              int* tickets, hipStream_t s, uint16_t* au) {
+                              int* tickets, hipStream_t s, uint16_t* au, const moe_ffn_extra* extra) {
   FfnArgs a{};
   a.tickets = tickets;
+  if (extra != nullptr && extra->rows > 0) {
+    if (offsets == nullptr || au != nullptr) return hipErrorInvalidValue;
+    a.Ax = static_cast<const uint16_t*>(extra->x);
+    a.Bx = static_cast<const uint16_t*>(extra->w13);
+    a.Cx = static_cast<uint16_t*>(extra->h);
+    a.x_rows = extra->rows;
+  }
   a.A = xp;
   a.lda = d;
   a.B = w13;
@@ -636,8 +657,28 @@ hipError_t launch_gemm_acc_f32(int64_t rows, int K, int N, const uint16_t* A, co
 
 hipError_t launch_ffn_down_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
                                 int d_ff, const uint16_t* h, const uint16_t* w2, uint16_t* yp,
-                                int* tickets, hipStream_t s) {
-  return launch_ffn_store_bf16(n_exp, offsets, max_rows, d_ff, d, h, w2, yp, tickets, s);
+                                int* tickets, hipStream_t s, const moe_ffn_extra* extra) {
+  if (extra == nullptr || extra->rows == 0)
+    return launch_ffn_store_bf16(n_exp, offsets, max_rows, d_ff, d, h, w2, yp, tickets, s);
+  if (offsets == nullptr) return hipErrorInvalidValue;
+  FfnArgs a{};
+  a.tickets = tickets;
+  a.A = h;
+  a.lda = d_ff;
+  a.B = w2;
+  a.b_group_stride = (int64_t)d * d_ff;
+  a.C = yp;
+  a.ldc = d;
+  a.offsets = offsets;
+  a.n_exp = n_exp;
+  a.rows_total = max_rows;
+  a.K = d_ff;
+  a.n_tiles = d / BN;
+  a.Ax = static_cast<const uint16_t*>(extra->h);
+  a.Bx = static_cast<const uint16_t*>(extra->w2);
+  a.Cx = static_cast<uint16_t*>(extra->y);
+  a.x_rows = extra->rows;
+  return launch<MODE_STORE>(a, max_rows, s);
 }
 
 }  // namespace moe

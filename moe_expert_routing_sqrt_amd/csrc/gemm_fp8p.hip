@@ -171,15 +171,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
 
   const int n_grp = tile_map_build(p.offsets, p.n_exp, p.rows_total, BM, s_map);
   const int total = s_map[n_grp] * p.n_tiles;
-  const int per = (total + kXcds - 1) / kXcds;
-  const int l_begin = xcd * per;
-  const int l_end = min(total, l_begin + per);
+  const int ch = xcd_chunk(total);
   int tick_reg = 0;
-  if (tid == 0) s_tick = l_begin + atomicAdd(&tickets[xcd * kCtrStride], 1);
+  if (tid == 0) s_tick = xcd_tile(atomicAdd(&tickets[xcd * kCtrStride], 1), xcd, ch);
   __syncthreads();
   const int l_first = __builtin_amdgcn_readfirstlane(s_tick);
 
-  if (l_first < l_end) {
+  if (l_first < total) {
     const int nsteps = p.K / BKB;
     TileInfo ti, tn;
     tile_map_decode(l_first, n_grp, BM, p.n_tiles, s_map, 0, ti);
@@ -267,7 +265,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
     };
     auto retarget = [&]() __attribute__((always_inline)) {
       const int l_next = __builtin_amdgcn_readfirstlane(s_tick);
-      nx = l_next < l_end;
+      nx = l_next < total;
       if (nx) {
         tile_map_decode(l_next, n_grp, BM, p.n_tiles, s_map, ti.group, tn);
         uniform_tile(tn);
@@ -280,7 +278,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_fp8_kernel(const Fp8Args p) {
       if (tid == 0) tick_reg = atomicAdd(&tickets[xcd * kCtrStride + zero], 1);
     };
     auto publish_ticket = [&]() __attribute__((always_inline)) {
-      if (tid == 0) s_tick = l_begin + tick_reg;
+      if (tid == 0) s_tick = xcd_tile(tick_reg, xcd, ch);
     };
     auto slot_of = [&](int kk) __attribute__((always_inline)) { return (sc_base + kk) & (SC_SLOTS - 1); };
 

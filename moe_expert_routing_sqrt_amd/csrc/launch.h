@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe.h"
+
 namespace moe {
 
 // compute units of the current device (cached per device; 256 if the query fails)
@@ -32,12 +34,16 @@ hipError_t launch_dispatch(const int32_t* idx, const int32_t* block_counts, int6
 
 // grouped expert FFN.  `tickets`: a zeroed ticket counter set (kTicketInts
 // ints, common.h) that no concurrently running launch shares
+// `extra`: one more group after the n_exp groups of the offsets, with its own
+// buffers (bf16: x, w13, h for the up-projection; h, w2, y for the down),
+// computed in the same launch; NULL or rows = 0: none
 hipError_t launch_ffn_up_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
                               int d_ff, const uint16_t* xp, const uint16_t* w13, uint16_t* h,
-                              int* tickets, hipStream_t s, uint16_t* au = nullptr);
+                              int* tickets, hipStream_t s, uint16_t* au = nullptr,
+                              const moe_ffn_extra* extra = nullptr);
 hipError_t launch_ffn_down_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,
                                 int d_ff, const uint16_t* h, const uint16_t* w2, uint16_t* yp,
-                                int* tickets, hipStream_t s);
+                                int* tickets, hipStream_t s, const moe_ffn_extra* extra = nullptr);
 // C [rows, N] = A [rows, K] x B_g^T with B_g [N, K] per group (plain bf16 store)
 hipError_t launch_ffn_store_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int K, int N,
                                  const uint16_t* A, const uint16_t* B, uint16_t* C, int* tickets,

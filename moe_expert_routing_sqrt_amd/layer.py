@@ -25,7 +25,7 @@ class MoELayer:
                  sh_w13: Optional[torch.Tensor] = None, sh_w2: Optional[torch.Tensor] = None,
                  logit_offset: Optional[torch.Tensor] = None, e_begin: int = 0,
                  e_end: Optional[int] = None, group_topk: Optional[int] = None,
-                 router: str = "topk", hash_seed: int = 0):
+                 router: str = "topk", hash_seed: int = 0, merge_shared: bool = True):
         dev = bias.device
         self.sh = shape(T, d, E, G, M, k, d_ff, group_topk)
         self.T, self.d, self.E, self.k, self.d_ff = T, d, E, k, d_ff
@@ -58,6 +58,9 @@ class MoELayer:
             self.sh_w13, self.sh_w2 = sh_w13, sh_w2
             self.sh_w13_s = self.sh_w2_s = None
         self.has_shared = sh_w13 is not None and not self.local
+        # the shared expert as one more group of the routed expert launches
+        # (moe_ffn_extra); False: a call of its own after them
+        self.merge_shared = merge_shared and self.has_shared
 
         act = torch.float32 if self.dtype == MOE_F32 else torch.bfloat16
         store = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.uint8}[self.dtype]
@@ -127,16 +130,23 @@ class MoELayer:
                               bufs=self.dbufs)
         b = self.dbufs
         mark(2)
+        extra = None
+        if self.merge_shared:
+            xs, xs_scale = x, None
+            if self.dtype == MOE_E4M3:
+                xs, xs_scale = self._shared_quant_input(x)
+            extra = dict(rows=self.T, x=xs, x_scale=xs_scale, w13=self.sh_w13, w13_scale=self.sh_w13_s,
+                         w2=self.sh_w2, w2_scale=self.sh_w2_s, h=self.sh_h, h_scale=self.sh_h_s, y=self.ysh)
         expert_ffn(b["offsets"], self.max_rows, b["xp"], self.w13, self.w2, self.dtype,
                    xp_scale=b["xp_scale"], w13_scale=self.w13_s, w2_scale=self.w2_s, h=self.h,
-                   h_scale=self.h_s, yp=self.yp, stages=MOE_FFN_UP, ws=self.ffn_ws)
+                   h_scale=self.h_s, yp=self.yp, stages=MOE_FFN_UP, ws=self.ffn_ws, extra=extra)
         mark(3)
         expert_ffn(b["offsets"], self.max_rows, b["xp"], self.w13, self.w2, self.dtype,
                    xp_scale=b["xp_scale"], w13_scale=self.w13_s, w2_scale=self.w2_s, h=self.h,
-                   h_scale=self.h_s, yp=self.yp, stages=MOE_FFN_DOWN, ws=self.ffn_ws)
+                   h_scale=self.h_s, yp=self.yp, stages=MOE_FFN_DOWN, ws=self.ffn_ws, extra=extra)
         mark(4)
-        ysh = None
-        if self.has_shared:
+        ysh = self.ysh if self.merge_shared else None
+        if self.has_shared and not self.merge_shared:
             xs, xs_scale = x, None
             if self.dtype == MOE_E4M3:
                 xs, xs_scale = self._shared_quant_input(x)

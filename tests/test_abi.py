@@ -131,7 +131,7 @@ def test_dispatch_checks():
 
 def test_expert_ffn_checks():
     W = L.moe_workspace_size(_lib.MOE_OP_EXPERT_FFN, None, 1)
-    f = lambda *a, ws=FAKE, wsb=W: L.moe_expert_ffn(*a, ws, wsb, None)
+    f = lambda *a, ws=FAKE, wsb=W, ex=None: L.moe_expert_ffn(*a, ex, ws, wsb, None)
     assert f(0, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3) == -1
     assert f(2000, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3) == -1
     assert f(4, None, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3) == -1
@@ -145,6 +145,20 @@ def test_expert_ffn_checks():
     assert f(4, FAKE, 10, 512, 256, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3,
              ws=FAKE + 64) == -3
     assert f(4, FAKE, 0, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3) == 0
+    # the extra group (shared expert): its buffers are checked like the routed ones
+    good = dict(rows=16, x=FAKE, w13=FAKE, w2=FAKE, h=FAKE, y=FAKE)
+    ex = lambda **kw: ctypes.byref(_lib.MoeFfnExtra(**{**good, **kw}))
+    assert f(4, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3,
+             ex=ex(rows=-1)) == -1
+    for k in ("x", "w13", "w2", "h", "y"):
+        assert f(4, FAKE, 10, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3,
+                 ex=ex(**{k: None})) == -1, k
+    # e4m3 needs the extra group's scales too
+    assert f(4, FAKE, 10, 256, 128, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3,
+             ex=ex()) == -1
+    # rows = 0 is no extra group: an empty call stays a no-op
+    assert f(4, FAKE, 0, 64, 32, 1, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 3,
+             ex=ex(rows=0)) == 0
 
 
 def test_combine_checks():

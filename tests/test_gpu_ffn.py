@@ -111,3 +111,78 @@ def test_ffn_v3_sampled_experts():
         assert err <= 2e-2
     del ex
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3", "f32"])
+@pytest.mark.parametrize("counts,x_rows", [([0, 1, 300, 257, 129], 700), ([0, 0, 0], 513), ([64, 200], 1)])
+def test_extra_group_equals_separate_call(dtype, counts, x_rows):
+    """The shared expert as the extra group of the routed call (moe_ffn_extra):
+    the routed outputs and the extra group's h and y bit-identical to two
+    separate calls (bf16 on the matrix cores: one launch per product holding
+    both; the other paths: launches of its own), including a call with no
+    routed rows."""
+    dev = need_gpu()
+    print(f"ffn extra group {dtype} {counts} + {x_rows}", flush=True)
+    g = torch.Generator(device=dev).manual_seed(sum(counts) + x_rows)
+    d, d_ff = (1024, 512) if dtype != "f32" else (320, 96)
+    n = len(counts)
+    off = dev_i32(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), dev)
+    rows = max(int(sum(counts)), 1)
+    x = torch.randn((rows, d), generator=g, device=dev).to(torch.bfloat16)
+    xs = torch.randn((x_rows, d), generator=g, device=dev).to(torch.bfloat16)
+    w13 = 0.05 * torch.randn((n, 2 * d_ff, d), generator=g, device=dev)
+    w2 = 0.05 * torch.randn((n, d, d_ff), generator=g, device=dev)
+    s13 = 0.05 * torch.randn((1, 2 * d_ff, d), generator=g, device=dev)
+    s2 = 0.05 * torch.randn((1, d, d_ff), generator=g, device=dev)
+    sc = {}
+    if dtype == "e4m3":
+        x, sc["xp_scale"] = M.quantize_rows_e4m3(x)
+        xs, sc["x_scale"] = M.quantize_rows_e4m3(xs)
+        w13, sc["w13_scale"] = M.quantize_blocks_e4m3(w13)
+        w2, sc["w2_scale"] = M.quantize_blocks_e4m3(w2)
+        s13, sc["s13"] = M.quantize_blocks_e4m3(s13)
+        s2, sc["s2"] = M.quantize_blocks_e4m3(s2)
+        dt = M.MOE_E4M3
+    else:
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        x, xs, w13, w2, s13, s2 = (t.to(tdt) for t in (x, xs, w13, w2, s13, s2))
+        dt = M.MOE_BF16 if dtype == "bf16" else M.MOE_F32
+    # reference: two separate calls
+    ref_y, ref_h, ref_hs = M.expert_ffn(off, rows, x, w13, w2, dt, xp_scale=sc.get("xp_scale"),
+                                        w13_scale=sc.get("w13_scale"), w2_scale=sc.get("w2_scale"))
+    ref_ys, ref_hx, ref_hxs = M.expert_ffn(dev_i32([0, x_rows], dev), x_rows, xs, s13, s2, dt,
+                                           xp_scale=sc.get("x_scale"), w13_scale=sc.get("s13"),
+                                           w2_scale=sc.get("s2"))
+    # one call with the extra group
+    store = {M.MOE_E4M3: torch.uint8, M.MOE_BF16: torch.bfloat16, M.MOE_F32: torch.float32}[dt]
+    ydt = torch.float32 if dt == M.MOE_F32 else torch.bfloat16
+    ex = dict(rows=x_rows, x=xs, x_scale=sc.get("x_scale"), w13=s13[0], w13_scale=sc.get("s13"), w2=s2[0],
+              w2_scale=sc.get("s2"), h=torch.empty((x_rows, d_ff), dtype=store, device=dev),
+              h_scale=(torch.empty((d_ff // 128, x_rows), dtype=torch.float32, device=dev)
+                       if dt == M.MOE_E4M3 else None),
+              y=torch.empty((x_rows, d), dtype=ydt, device=dev))
+    y, h, hs = M.expert_ffn(off, rows, x, w13, w2, dt, xp_scale=sc.get("xp_scale"), w13_scale=sc.get("w13_scale"),
+                            w2_scale=sc.get("w2_scale"), extra=ex)
+    torch.cuda.synchronize()
+    r = int(sum(counts))
+    assert torch.equal(y[:r], ref_y[:r]) and torch.equal(h[:r], ref_h[:r])
+    assert torch.equal(ex["y"], ref_ys) and torch.equal(ex["h"], ref_hx)
+    if dt == M.MOE_E4M3:
+        assert torch.equal(ex["h_scale"], ref_hxs)
+
+
+def test_layer_merged_shared_equals_separate():
+    """MoELayer with the shared expert merged into the routed launches gives
+    the same output, bit for bit, as with a call of its own."""
+    dev = need_gpu()
+    cfg = C.get("flash").with_(T=1024, d=1024, E=16, G=4, k=4, M=2, d_ff=512)
+    inp = gen.make_router(cfg, device=dev)
+    ex = gen.make_experts(cfg, device=dev)
+    outs = []
+    for merge in (True, False):
+        layer = M.MoELayer(cfg.T, cfg.d, cfg.E, cfg.G, cfg.M, cfg.k, cfg.d_ff, cfg.dtype, inp["w_gate"],
+                           inp["bias"], ex["w13"], ex["w2"], ex["sh_w13"], ex["sh_w2"], group_topk=cfg.gk,
+                           merge_shared=merge)
+        outs.append(layer.forward(inp["x"]).clone())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
