@@ -166,8 +166,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
   if (l_first < total) {
     const int nsteps = p.K / BK;
     TileInfo ti, tn;
+    // the extra group's rows are counted from its own first row
+    const int x_row0 = p.x_rows > 0 ? tile_map_offsets(s_map)[p.n_exp] : 0;
+    auto localize = [&](TileInfo& t) __attribute__((always_inline)) {
+      if (p.x_rows > 0 && t.group == p.n_exp) t.row0 -= x_row0;
+    };
     tile_map_decode(l_first, n_grp, BM, p.n_tiles, s_map, 0, ti);
     uniform_tile(ti);
+    localize(ti);
     bool nx = false;  // a next tile exists (known from step nsteps-2 on)
 
     // Direct-to-LDS loads: one instruction moves 64 lanes x 16 B into 1 KB of
@@ -210,23 +216,15 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
     struct Src {
       const char* a;  // activation row of the tile's first row
       const char* b;  // the tile's first weight row
-      uint16_t* c;    // output row of the tile's first row
       int rows;
     };
     auto src_of = [&](const TileInfo& t) __attribute__((always_inline)) {
       Src x;
       const int64_t w0 = (int64_t)t.n_tile * (SWI ? BN / 2 : BN);
-      if (p.x_rows > 0 && t.group == p.n_exp) {
-        // the extra group: its own buffers, rows counted from its first
-        const int64_t r0 = t.row0 - tile_map_offsets(s_map)[p.n_exp];
-        x.a = reinterpret_cast<const char*>(p.Ax + r0 * p.lda);
-        x.b = reinterpret_cast<const char*>(p.Bx + w0 * p.K);
-        x.c = p.Cx + r0 * p.ldc;
-      } else {
-        x.a = reinterpret_cast<const char*>(p.A + (int64_t)t.row0 * p.lda);
-        x.b = reinterpret_cast<const char*>(p.B + (int64_t)t.group * p.b_group_stride + w0 * p.K);
-        x.c = p.C + (int64_t)t.row0 * p.ldc;
-      }
+      const bool ext = p.x_rows > 0 && t.group == p.n_exp;  // the extra group: its own buffers
+      x.a = reinterpret_cast<const char*>((ext ? p.Ax : p.A) + (int64_t)t.row0 * p.lda);
+      x.b = reinterpret_cast<const char*>(ext ? p.Bx + w0 * p.K
+                                              : p.B + (int64_t)t.group * p.b_group_stride + w0 * p.K);
       x.rows = t.rows;
       return x;
     };
@@ -253,6 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
       if (nx) {
         tile_map_decode(l_next, n_grp, BM, p.n_tiles, s_map, ti.group, tn);
         uniform_tile(tn);
+        localize(tn);
         nxt = src_of(tn);
       }
     };
@@ -417,6 +416,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
       constexpr int OUT_COLS = SWI ? BN / 2 : BN;
       const int64_t col0 = (int64_t)ti.n_tile * OUT_COLS;
       const int lr0 = 4 * (lane >> 5);
+      uint16_t* const cb = p.x_rows > 0 && ti.group == p.n_exp ? p.Cx : p.C;  // output buffer of the tile
       if constexpr (MODE == MODE_ACC_F32) {
         // fp32 read-modify-write straight from the registers: for a fixed
         // register the 32 lanes of a half-wave cover 128 contiguous bytes
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
             const int r = lane >> 3, c = lane & 7;
             if (rb + r < ti.rows) {
               const uint4 val = *reinterpret_cast<const uint4*>(st + r * ST_PITCH + c * 16);
-              *reinterpret_cast<uint4*>(cur.c + (int64_t)(rb + r) * p.ldc + col0 + wn * (TN / 2) + c * 8) = val;
+              *reinterpret_cast<uint4*>(cb + (grow0 + r) * p.ldc + col0 + wn * (TN / 2) + c * 8) = val;
             }
           } else {
             // 8 rows x 256 B: two chunks per lane
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
               const int r = q >> 4, c = q & 15;
               if (rb + r < ti.rows) {
                 const uint4 val = *reinterpret_cast<const uint4*>(st + r * ST_PITCH + c * 16);
-                *reinterpret_cast<uint4*>(cur.c + (int64_t)(rb + r) * p.ldc + col0 + wn * TN + c * 8) = val;
+                *reinterpret_cast<uint4*>(cb + (grow0 + r) * p.ldc + col0 + wn * TN + c * 8) = val;
               }
             }
           }
