@@ -27,7 +27,7 @@ PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 HASH_SEED = 7
 
-# HBM traffic of the routed up-projection launch, per launch, from two
+# HBM traffic of the up-projection launch (the dominant kernel), per launch, from two
 # rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over
 #   python3 bench.py [--workload W] --steps 2 --warmup 1 --cpu-sample 0 --copy-probe
 # Each counter is scaled by what it reads for the copy probe (a plain 2 GiB
@@ -39,14 +39,18 @@ _SHARED_SOURCES = ("moe_expert_routing_sqrt_amd/csrc/gemm_common.h",
                    "moe_expert_routing_sqrt_amd/csrc/common.h",
                    "moe_expert_routing_sqrt_amd/build.py")
 TRAFFIC = {
+    # the bf16 up-projection launch with the shared expert inside it
     "v3": {"sources": ("moe_expert_routing_sqrt_amd/csrc/ffn_bf16.hip",) + _SHARED_SOURCES,
-           "sources_sha256": "23cf24a5e55cfb4ef500be7805ed0550240ecd14a608aa5a728a97b5c461a077",
-           "fetch_kib": 18642588.6, "fetch_scale": 1.99997,
-           "write_kib": 524627.8, "write_scale": 1.0},
+           "sources_sha256": "b4645d78893de762c82ed6cffd81e04c9e2ff51e1c8bb881d7ced387a2bcdbce",
+           "merged": True,
+           "fetch_kib": 21045893.2, "fetch_scale": 1.99997,
+           "write_kib": 590195.8, "write_scale": 1.0},
+    # the e4m3 routed up-projection launch (the shared expert has launches of its own)
     "v3_fp8": {"sources": ("moe_expert_routing_sqrt_amd/csrc/gemm_fp8p.hip",) + _SHARED_SOURCES,
-               "sources_sha256": "d66ee96f45d1a738a35ef06a243694d553fee477e2f3d1d052995c4258c0b504",
-               "fetch_kib": 10636418.9, "fetch_scale": 1.99997,
-               "write_kib": 274533.6, "write_scale": 1.0},
+               "sources_sha256": "4cc3618b4d22b2f59997c40d8e92991931b96b5290f009352ea7abc875b08f12",
+               "merged": False,
+               "fetch_kib": 10694486.7, "fetch_scale": 1.99997,
+               "write_kib": 275932.4, "write_scale": 1.0},
 }
 
 
@@ -128,10 +132,10 @@ def sources_digest(sources) -> str:
     return h.hexdigest()
 
 
-def traffic(cfg, up_bytes):
-    """Counter-measured HBM bytes per routed up-projection launch, or None."""
+def traffic(cfg, up_bytes, merged):
+    """Counter-measured HBM bytes per up-projection launch, or None."""
     rec = TRAFFIC.get(cfg.name)
-    if rec is None or rec["sources_sha256"] != sources_digest(rec["sources"]):
+    if rec is None or rec["sources_sha256"] != sources_digest(rec["sources"]) or rec["merged"] != merged:
         return None
     fetch = rec["fetch_kib"] * 1024 * rec["fetch_scale"]
     write = rec["write_kib"] * 1024 * rec["write_scale"]
@@ -458,7 +462,7 @@ def main():
     gemm_ms = st_ms["ffn_up"] + st_ms["ffn_down"] + st_ms["shared"]
     gemm_flops = alg["ffn_up_flops"](rows) + alg["ffn_down_flops"](rows) + (alg["shared_flops"] if layer.has_shared else 0)
     up = stages["ffn_up"]
-    up_traffic = traffic(cfg, alg["ffn_up_bytes"](rows))
+    up_traffic = traffic(cfg, alg["ffn_up_bytes"](rows), merged)
     result = {
         "metric": METRIC,
         "value": cfg.T / (ms_per_step * 1e-3),

@@ -278,8 +278,10 @@ int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int3
   int* const tick_down = ticket_set(ws, 1);
   // The bf16 matrix-core products take the extra group into their launches;
   // every other path runs it after the routed groups as one group of its own
-  // (no offsets), reusing the ticket sets in stream order.
-  const moe_ffn_extra* merged = mfma && has_x ? extra : nullptr;
+  // (no offsets), reusing the ticket sets in stream order.  (The e4m3
+  // persistent kernel has no registers left for a second set of buffers.)
+  const moe_ffn_extra* merged_up = mfma && has_x ? extra : nullptr;
+  const moe_ffn_extra* merged_down = merged_up;
   auto up_launch = [&](int n, const int32_t* off, int64_t rows, const void* x_, const float* xs_, const void* w13_,
                        const float* w13s_, void* h_, float* hs_) -> hipError_t {
     if (dtype == MOE_E4M3 && ffn_fp8p_supported_k(d))
@@ -291,7 +293,7 @@ int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int3
     if (mfma)
       return launch_ffn_up_bf16(n, off, rows, d, d_ff, static_cast<const uint16_t*>(x_),
                                 static_cast<const uint16_t*>(w13_), static_cast<uint16_t*>(h_), tick_up, s, nullptr,
-                                merged);
+                                off != nullptr ? merged_up : nullptr);
     return launch_ffn_simt(MOE_FFN_UP, n, off, rows, d, d_ff, dtype, x_, w13_, h_, s);
   };
   auto down_launch = [&](int n, const int32_t* off, int64_t rows, const void* h_, const float* hs_, const void* w2_,
@@ -304,22 +306,23 @@ int moe_expert_ffn(int32_t n_exp, const int32_t* offsets, int64_t max_rows, int3
                                  static_cast<const uint8_t*>(w2_), w2s_, static_cast<uint16_t*>(y_), s);
     if (mfma)
       return launch_ffn_down_bf16(n, off, rows, d, d_ff, static_cast<const uint16_t*>(h_),
-                                  static_cast<const uint16_t*>(w2_), static_cast<uint16_t*>(y_), tick_down, s, merged);
+                                  static_cast<const uint16_t*>(w2_), static_cast<uint16_t*>(y_), tick_down, s,
+                                  off != nullptr ? merged_down : nullptr);
     return launch_ffn_simt(MOE_FFN_DOWN, n, off, rows, d, d_ff, dtype, h_, w2_, y_, s);
   };
-  const bool routed = max_rows > 0 || merged != nullptr;
-  const bool separate = has_x && merged == nullptr;
   if (up) {
-    if (routed && up_launch(n_exp, offsets, max_rows, xp, xp_scale, w13, w13_scale, h, h_scale) != hipSuccess)
+    if ((max_rows > 0 || merged_up != nullptr) &&
+        up_launch(n_exp, offsets, max_rows, xp, xp_scale, w13, w13_scale, h, h_scale) != hipSuccess)
       return MOE_ERR_HIP;
-    if (separate && up_launch(1, nullptr, extra->rows, extra->x, extra->x_scale, extra->w13, extra->w13_scale,
+    if (has_x && merged_up == nullptr && up_launch(1, nullptr, extra->rows, extra->x, extra->x_scale, extra->w13, extra->w13_scale,
                               extra->h, extra->h_scale) != hipSuccess)
       return MOE_ERR_HIP;
   }
   if (down) {
-    if (routed && down_launch(n_exp, offsets, max_rows, h, h_scale, w2, w2_scale, yp) != hipSuccess)
+    if ((max_rows > 0 || merged_down != nullptr) &&
+        down_launch(n_exp, offsets, max_rows, h, h_scale, w2, w2_scale, yp) != hipSuccess)
       return MOE_ERR_HIP;
-    if (separate && down_launch(1, nullptr, extra->rows, extra->h, extra->h_scale, extra->w2, extra->w2_scale,
+    if (has_x && merged_down == nullptr && down_launch(1, nullptr, extra->rows, extra->h, extra->h_scale, extra->w2, extra->w2_scale,
                                 extra->y) != hipSuccess)
       return MOE_ERR_HIP;
   }

@@ -59,8 +59,11 @@ class MoELayer:
             self.sh_w13_s = self.sh_w2_s = None
         self.has_shared = sh_w13 is not None and not self.local
         # the shared expert as one more group of the routed expert launches
-        # (moe_ffn_extra); False: a call of its own after them
-        self.merge_shared = merge_shared and self.has_shared
+        # (moe_ffn_extra) where the library computes it inside them (bf16
+        # matrix-core products); otherwise, or with merge_shared=False, a call
+        # of its own after them
+        mfma = self.dtype == MOE_BF16 and d % 256 == 0 and d_ff % 128 == 0 and d_ff >= 256
+        self.merge_shared = merge_shared and self.has_shared and mfma
 
         act = torch.float32 if self.dtype == MOE_F32 else torch.bfloat16
         store = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.uint8}[self.dtype]
@@ -132,11 +135,7 @@ class MoELayer:
         mark(2)
         extra = None
         if self.merge_shared:
-            xs, xs_scale = x, None
-            if self.dtype == MOE_E4M3:
-                xs, xs_scale = self._shared_quant_input(x)
-            extra = dict(rows=self.T, x=xs, x_scale=xs_scale, w13=self.sh_w13, w13_scale=self.sh_w13_s,
-                         w2=self.sh_w2, w2_scale=self.sh_w2_s, h=self.sh_h, h_scale=self.sh_h_s, y=self.ysh)
+            extra = dict(rows=self.T, x=x, w13=self.sh_w13, w2=self.sh_w2, h=self.sh_h, y=self.ysh)
         expert_ffn(b["offsets"], self.max_rows, b["xp"], self.w13, self.w2, self.dtype,
                    xp_scale=b["xp_scale"], w13_scale=self.w13_s, w2_scale=self.w2_s, h=self.h,
                    h_scale=self.h_s, yp=self.yp, stages=MOE_FFN_UP, ws=self.ffn_ws, extra=extra)
