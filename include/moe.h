@@ -112,7 +112,8 @@ const char* moe_status_str(int status);
  *          depend on it)
  *   dtype  MOE_OP_ROUTE: x's type; MOE_OP_DISPATCH: the output type (the
  *          e4m3 output needs a per-token scale table); otherwise ignored
- * MOE_OP_ROUTE covers a call with logits = NULL (the larger case);
+ * MOE_OP_ROUTE covers a call with logits = NULL (the larger case; with
+ * bf16 x and a split gate product both cases need the same);
  * MOE_OP_DISPATCH covers any expert range.  Returns 0 for an invalid shape
  * or op.
  */
@@ -154,9 +155,15 @@ size_t moe_workspace_size(int op, const moe_shape* shape, int dtype);
  * group_topk <= 4; k <= 16.  The matrix-core gate product needs bf16 x,
  * d % 64 == 0 and E % 64 == 0 (else fp32 vector products, same planes).
  *   ws            moe_workspace_size(MOE_OP_ROUTE, shape, x_dtype) bytes: the
- *                 planes [3, E, d] bf16 (rewritten by every call), then the
- *                 logits when `logits` is NULL.  Unused with LOGITS_IN (may be
- *                 NULL).
+ *                 planes [3, E, d] bf16 (rewritten by every call); for bf16 x
+ *                 with E % 256 == 0 the gate product runs split over its
+ *                 reduction (the 3*d/64 plane-and-column steps) into S <= 8
+ *                 fp32 partial products [S, T, E] that the selection sums in
+ *                 order (((p0 + p1) + p2) + ...), with S chosen from T, d and E
+ *                 alone, so the workspace then also holds the split's counters
+ *                 and, for S > 1, the partial products; otherwise the logits
+ *                 when `logits` is NULL.  Nothing in it needs to start at
+ *                 zero.  Unused with LOGITS_IN (may be NULL).
  */
 int moe_route(const moe_shape* shape, const void* x, int x_dtype, const float* w_gate,
               const float* bias, const float* logit_offset, float* logits, int32_t* topk_idx,

@@ -110,8 +110,22 @@ const char* moe_status_str(int status) {
 static size_t route_planes_bytes(const moe_shape* s) {
   return align256(static_cast<size_t>(3) * s->E * s->d * sizeof(uint16_t));
 }
-static size_t route_ws_bytes(const moe_shape* s, bool logits_in_ws) {
-  return route_planes_bytes(s) + (logits_in_ws ? align256(static_cast<size_t>(s->T) * s->E * sizeof(float)) : 0);
+// route workspace: the planes; for the split gate product (bf16 x) its ticket
+// set and offsets, then its S partial products when S > 1; the logits when
+// the caller keeps none and they are not the one partial product
+static size_t route_split_bytes() { return align256((kTicketInts + kMaxGateSplits + 1) * sizeof(int)); }
+static int route_splits(const moe_shape* s, int x_dtype) {
+  return x_dtype == MOE_BF16 ? gate_split_count(s->T, s->d, s->E) : 0;
+}
+static size_t route_ws_bytes(const moe_shape* s, bool logits_in_ws, int x_dtype) {
+  const size_t logits_bytes = align256(static_cast<size_t>(s->T) * s->E * sizeof(float));
+  size_t b = route_planes_bytes(s);
+  const int S = route_splits(s, x_dtype);
+  if (S >= 1) {
+    b += route_split_bytes();
+    if (S > 1) return b + S * logits_bytes;
+  }
+  return b + (logits_in_ws ? logits_bytes : 0);
 }
 
 int moe_route(const moe_shape* shape, const void* x, int x_dtype, const float* w_gate,
@@ -132,25 +146,47 @@ int moe_route(const moe_shape* shape, const void* x, int x_dtype, const float* w
   if (!route_select_supported(shape->E, shape->G, shape->k, shape->group_topk))
     return MOE_ERR_UNSUPPORTED;
   if (!logits_in) {
-    if (ws == nullptr || ws_bytes < route_ws_bytes(shape, logits == nullptr) || !aligned256(ws))
+    if (ws == nullptr || ws_bytes < route_ws_bytes(shape, logits == nullptr, x_dtype) || !aligned256(ws))
       return MOE_ERR_WORKSPACE;
   }
   if (shape->T == 0) return MOE_OK;
   hipStream_t s = as_stream(stream);
+  const float* parts = logits;  // what the selection reads
+  int nparts = 1;
+  float* logits_out = nullptr;
   if (!logits_in) {
-    uint16_t* planes = static_cast<uint16_t*>(ws);
-    if (logits == nullptr)
-      logits = reinterpret_cast<float*>(static_cast<char*>(ws) + route_planes_bytes(shape));
-    hipError_t e = launch_gate_prepare(shape->d, shape->E, w_gate, planes, s);
+    char* w = static_cast<char*>(ws);
+    uint16_t* planes = reinterpret_cast<uint16_t*>(w);
+    w += route_planes_bytes(shape);
+    const int S = route_splits(shape, x_dtype);
+    int* split = nullptr;
+    if (S >= 1) {
+      split = reinterpret_cast<int*>(w);
+      w += route_split_bytes();
+    }
+    float* out = logits != nullptr ? logits : reinterpret_cast<float*>(w);
+    hipError_t e = launch_gate_prepare(shape->d, shape->E, w_gate, planes, s, split, S, shape->T);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    if (x_dtype == MOE_BF16 && gate_gemm_bf16_supported(shape->d, shape->E))
-      e = launch_gate_gemm_bf16(static_cast<const uint16_t*>(x), planes, logits, shape->T, shape->d, shape->E, s);
-    else
-      e = launch_gate_gemm_simt(x, x_dtype, planes, logits, shape->T, shape->d, shape->E, s);
+    if (S >= 1) {
+      // S > 1: partial products in the workspace, summed (and written to the
+      // caller's logits) by the selection
+      float* dst = S > 1 ? reinterpret_cast<float*>(w) : out;
+      e = launch_gate_split_bf16(static_cast<const uint16_t*>(x), planes, dst, shape->T, shape->d, shape->E, S,
+                                 split + kTicketInts, split, s);
+      parts = dst;
+      nparts = S;
+      if (S > 1) logits_out = logits;
+    } else if (x_dtype == MOE_BF16 && gate_gemm_bf16_supported(shape->d, shape->E)) {
+      e = launch_gate_gemm_bf16(static_cast<const uint16_t*>(x), planes, out, shape->T, shape->d, shape->E, s);
+      parts = out;
+    } else {
+      e = launch_gate_gemm_simt(x, x_dtype, planes, out, shape->T, shape->d, shape->E, s);
+      parts = out;
+    }
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
-  return hip_status(launch_route_select(logits, bias, logit_offset, topk_idx, topk_w, block_counts,
-                                        shape->T, shape->E, shape->G, shape->M, shape->k,
+  return hip_status(launch_route_select(parts, nparts, logits_out, bias, logit_offset, topk_idx, topk_w,
+                                        block_counts, shape->T, shape->E, shape->G, shape->M, shape->k,
                                         shape->group_topk, s));
 }
 
@@ -495,7 +531,7 @@ size_t moe_workspace_size(int op, const moe_shape* shape, int dtype) {
   switch (op) {
     case MOE_OP_ROUTE:
       if (check_shape(shape) != MOE_OK) return 0;
-      return route_ws_bytes(shape, true);
+      return route_ws_bytes(shape, true, dtype);
     case MOE_OP_DISPATCH:
       if (check_shape(shape) != MOE_OK) return 0;
       return dispatch_ws_bytes(shape, 0, shape->E, dtype);

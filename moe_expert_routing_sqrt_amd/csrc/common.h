@@ -22,6 +22,9 @@ constexpr int kTicketStride = 16;  // ints between counters
 constexpr int kTicketInts = (kXcds + 1) * kTicketStride;
 constexpr size_t kTicketBytes = kTicketInts * sizeof(int);
 
+// the router gate product runs as at most this many split-K partial products
+constexpr int kMaxGateSplits = 8;
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

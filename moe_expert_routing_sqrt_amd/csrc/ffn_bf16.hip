@@ -89,8 +89,9 @@ constexpr int ST_BYTES = 8 * ST_PITCH;
 
 constexpr int kCtrStride = kTicketStride;
 
-// SAVE: also [a | u]; ACC_F32: C (fp32) += A B^T, one group
-enum { MODE_SWIGLU = 0, MODE_STORE = 1, MODE_SWIGLU_SAVE = 2, MODE_ACC_F32 = 3 };
+// SAVE: also [a | u]; ACC_F32: C (fp32) += A B^T, one group; GATE: the router's
+// gate product split over K (below)
+enum { MODE_SWIGLU = 0, MODE_STORE = 1, MODE_SWIGLU_SAVE = 2, MODE_ACC_F32 = 3, MODE_GATE = 4 };
 
 struct FfnArgs {
   const uint16_t* A;       // packed rows [rows, K]
@@ -114,6 +115,13 @@ struct FfnArgs {
   const uint16_t* Bx;      // its weights [*, K]
   uint16_t* Cx;            // [x_rows, ldc] output
   int64_t x_rows;
+  // GATE: K' = 3 * K / BK steps over the three bf16 planes of the gate weight
+  // (B, B + plane_bytes, B + 2 * plane_bytes, each [n_tiles * BN, K]), plane
+  // fastest; group g of the offsets holds the same T rows of A and takes steps
+  // [g * ksteps, (g + 1) * ksteps), writing its fp32 partial product to rows
+  // offsets[g] .. of Cf
+  int ksteps;
+  int64_t plane_bytes;
 };
 
 __device__ __forceinline__ void uniform_tile(TileInfo& t) {
@@ -155,6 +163,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
   const int xcd = blockIdx.x % kXcds;
   int* const tickets = p.tickets;
 
+  constexpr bool GATE = MODE == MODE_GATE;
   const int n_grp = tile_map_build(p.offsets, p.n_exp, p.rows_total, BM, s_map, p.x_rows);
   const int total = s_map[n_grp] * p.n_tiles;
   const int ch = xcd_chunk(total);
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
   const int l_first = __builtin_amdgcn_readfirstlane(s_tick);
 
   if (l_first < total) {
-    const int nsteps = p.K / BK;
+    const int nsteps = GATE ? p.ksteps : p.K / BK;
     TileInfo ti, tn;
     // the extra group's rows are counted from its own first row
     const int x_row0 = p.x_rows > 0 ? tile_map_offsets(s_map)[p.n_exp] : 0;
@@ -217,6 +226,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
       const char* a;  // activation row of the tile's first row
       const char* b;  // the tile's first weight row
       int rows;
+      int k0;         // GATE: the tile's first step of K'
     };
     auto src_of = [&](const TileInfo& t) __attribute__((always_inline)) {
       Src x;
@@ -226,6 +236,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
       x.b = reinterpret_cast<const char*>(ext ? p.Bx + w0 * p.K
                                               : p.B + (int64_t)t.group * p.b_group_stride + w0 * p.K);
       x.rows = t.rows;
+      x.k0 = 0;
+      if constexpr (GATE) {
+        // every group holds the same rows of A: count them from its first
+        x.a = reinterpret_cast<const char*>(p.A + (int64_t)(t.row0 - tile_map_offsets(s_map)[t.group]) * p.lda);
+        x.b = reinterpret_cast<const char*>(p.B + w0 * p.K);
+        x.k0 = t.group * p.ksteps;
+      }
       return x;
     };
     Src cur = src_of(ti), nxt = cur;
@@ -234,13 +251,21 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
     // stage (sa, sb).
     auto dma_one = [&](int kk, bool next, uint4* sa, uint4* sb, int q) __attribute__((always_inline)) {
       const Src& x = next ? nxt : cur;
-      const int kb = kk * BK * 2;  // byte offset of the step along K
+      int64_t kb = kk * BK * 2;  // byte offset of the step along K
+      int64_t kbb = kb;
+      if constexpr (GATE) {
+        // step kg of K': 64 columns kin of x times plane kg - 3 kin
+        const int kg = x.k0 + kk;
+        const int kin = kg / 3;
+        kb = (int64_t)kin * (BK * 2);
+        kbb = (int64_t)(kg - 3 * kin) * p.plane_bytes + kb;
+      }
       if (q < ADMA) {
         if ((wave + NW * q) * 8 < x.rows)
           dma16_s(x.a + kb, a_row[q] < x.rows ? a_off[q] : static_cast<uint32_t>(lch * 16),
                   lds_addr(sa) + (wave + NW * q) * 1024);
       } else {
-        dma16_s(x.b + kb, b_off[q - ADMA], lds_addr(sb) + (wave + NW * (q - ADMA)) * 1024);
+        dma16_s(x.b + kbb, b_off[q - ADMA], lds_addr(sb) + (wave + NW * (q - ADMA)) * 1024);
       }
     };
     // Step nsteps-2, after its barrier: take the next ticket and address
@@ -417,9 +442,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
       const int64_t col0 = (int64_t)ti.n_tile * OUT_COLS;
       const int lr0 = 4 * (lane >> 5);
       uint16_t* const cb = p.x_rows > 0 && ti.group == p.n_exp ? p.Cx : p.C;  // output buffer of the tile
-      if constexpr (MODE == MODE_ACC_F32) {
-        // fp32 read-modify-write straight from the registers: for a fixed
-        // register the 32 lanes of a half-wave cover 128 contiguous bytes
+      if constexpr (MODE == MODE_ACC_F32 || GATE) {
+        // fp32 read-modify-write (GATE: store) straight from the registers:
+        // for a fixed register the 32 lanes of a half-wave cover 128
+        // contiguous bytes
 #pragma unroll
         for (int i = 0; i < RM; ++i) {
           if (i >= nb) continue;
@@ -429,7 +455,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
             if (r >= ti.rows) continue;
             float* row = p.Cf + ((int64_t)ti.row0 + r) * p.ldc + col0 + wn * TN + (lane & 31);
 #pragma unroll
-            for (int j = 0; j < RN; ++j) row[j * 32] += acc[i][j][v];
+            for (int j = 0; j < RN; ++j) {
+              if constexpr (GATE) row[j * 32] = acc[i][j][v];
+              else row[j * 32] += acc[i][j][v];
+            }
           }
         }
         return;
@@ -573,7 +602,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_kernel(const FfnArgs p) 
 
 template <int MODE>
 hipError_t launch(FfnArgs& a, int64_t max_rows, hipStream_t s) {
-  if (a.K % (2 * BK) != 0 || a.K < 4 * BK) return hipErrorInvalidValue;
+  if (MODE == MODE_GATE) {
+    if (a.ksteps % 2 != 0 || a.ksteps < 4 || a.K % BK != 0) return hipErrorInvalidValue;
+  } else if (a.K % (2 * BK) != 0 || a.K < 4 * BK) {
+    return hipErrorInvalidValue;
+  }
   // 32-bit per-lane DMA offsets: a tile's rows and a group's weights
   constexpr bool swi = MODE == MODE_SWIGLU || MODE == MODE_SWIGLU_SAVE;
   const int64_t b_rows = swi ? 2 * (int64_t)a.d_ff : (int64_t)a.n_tiles * BN;
@@ -653,6 +686,49 @@ hipError_t launch_gemm_acc_f32(int64_t rows, int K, int N, const uint16_t* A, co
   a.K = K;
   a.n_tiles = N / BN;
   return launch<MODE_ACC_F32>(a, rows, s);
+}
+
+// The router gate product as S split-K partial products on this kernel (GATE
+// mode): parts[g] = x * (planes over steps [g*K'/S, (g+1)*K'/S))^T, fp32,
+// [S, T, E].  offsets = {0, T, 2T, ..., S*T} on the device.
+bool gate_split_supported(int d, int E) { return E % BN == 0 && d % BK == 0; }
+
+// The most splits that keep the launch at one tile per CU of an MI355X (256;
+// a fixed figure, so that the workspace size does not depend on the device),
+// with an even step count of at least 4 per split.
+int gate_split_count(int64_t T, int d, int E) {
+  if (!gate_split_supported(d, E)) return 0;
+  constexpr int64_t kTargetTiles = 256;
+  const int steps = 3 * (d / BK);
+  const int64_t tiles1 = (T + BM - 1) / BM * (E / BN);
+  int best = 0;
+  for (int S = 1; S <= kMaxGateSplits; ++S) {
+    if (steps % (2 * S) != 0 || steps / S < 4) continue;
+    if (S > 1 && tiles1 * S > kTargetTiles) break;
+    best = S;
+  }
+  return best;
+}
+
+hipError_t launch_gate_split_bf16(const uint16_t* x, const uint16_t* planes, float* parts, int64_t T,
+                                  int d, int E, int S, const int32_t* offsets, int* tickets,
+                                  hipStream_t s) {
+  if (S < 1 || 3 * (d / BK) % S != 0) return hipErrorInvalidValue;
+  FfnArgs a{};
+  a.tickets = tickets;
+  a.A = x;
+  a.lda = d;
+  a.B = planes;
+  a.Cf = parts;
+  a.ldc = E;
+  a.offsets = offsets;
+  a.n_exp = S;
+  a.rows_total = S * T;
+  a.K = d;
+  a.n_tiles = E / BN;
+  a.ksteps = 3 * (d / BK) / S;
+  a.plane_bytes = (int64_t)E * d * 2;
+  return launch<MODE_GATE>(a, S * T, s);
 }
 
 hipError_t launch_ffn_down_bf16(int n_exp, const int32_t* offsets, int64_t max_rows, int d,

@@ -18,11 +18,21 @@ hipError_t launch_gate_gemm_bf16(const uint16_t* x, const uint16_t* w_prep, floa
 hipError_t launch_gate_gemm_simt(const void* x, int x_dtype, const uint16_t* w_prep,
                                  float* logits, int64_t T, int d, int E, hipStream_t s);
 bool gate_gemm_bf16_supported(int d, int E);
+// the gate product as S split-K partial products [S, T, E] fp32 on the expert
+// GEMM kernel (E % 256 == 0, d % 64 == 0); gate_split_count: the S a launch
+// takes (0: not supported)
+bool gate_split_supported(int d, int E);
+int gate_split_count(int64_t T, int d, int E);
+hipError_t launch_gate_split_bf16(const uint16_t* x, const uint16_t* planes, float* parts, int64_t T,
+                                  int d, int E, int S, const int32_t* offsets, int* tickets,
+                                  hipStream_t s);
 
 // selection + block histogram
-hipError_t launch_route_select(const float* logits, const float* bias, const float* offset,
-                               int32_t* idx, float* w, int32_t* block_counts, int64_t T, int E,
-                               int G, int M, int k, int gk, hipStream_t s);
+// logits: nparts partial products [nparts][T, E] summed in order (1: the
+// logits themselves); logits_out: where the sums go, or nullptr
+hipError_t launch_route_select(const float* logits, int nparts, float* logits_out, const float* bias,
+                               const float* offset, int32_t* idx, float* w, int32_t* block_counts,
+                               int64_t T, int E, int G, int M, int k, int gk, hipStream_t s);
 bool route_select_supported(int E, int G, int k, int gk);
 
 // dispatch
@@ -85,8 +95,10 @@ hipError_t launch_combine(int64_t T, int k, int d, const int32_t* dest, const fl
                           int out_dtype, int accumulate, hipStream_t s);
 
 // weight preparation
+// split: the split gate product's ticket set and offsets (kTicketInts + S + 1
+// ints, reset by this launch), or nullptr
 hipError_t launch_gate_prepare(int d, int E, const float* w_gate, uint16_t* w_prep,
-                               hipStream_t s);
+                               hipStream_t s, int* split = nullptr, int S = 0, int64_t T = 0);
 hipError_t launch_quantize_rows(int64_t rows, int cols, const uint16_t* x, uint8_t* q, float* scale,
                                 hipStream_t s);
 hipError_t launch_quantize_blocks(int64_t n, int rows, int cols, const float* w, uint8_t* q,

@@ -20,8 +20,15 @@
 namespace moe {
 namespace {
 
+// split != nullptr: block 0 also writes the split gate product's ticket set
+// (zeros) and its group offsets {0, T, ..., S*T} after it.
 __global__ __launch_bounds__(256) void gate_prepare_kernel(int d, int E, const float* __restrict__ w,
-                                                           uint16_t* __restrict__ out) {
+                                                           uint16_t* __restrict__ out, int* split, int S,
+                                                           int64_t T) {
+  if (split != nullptr && blockIdx.x == 0) {
+    for (int j = threadIdx.x; j < kTicketInts; j += 256) split[j] = 0;
+    if (threadIdx.x <= S) split[kTicketInts + threadIdx.x] = static_cast<int>(threadIdx.x * T);
+  }
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over E*d, d fastest
   if (i >= (int64_t)E * d) return;
   const int e = static_cast<int>(i / d), kk = static_cast<int>(i % d);
@@ -121,10 +128,11 @@ hipError_t launch_quantize_rows(int64_t rows, int cols, const uint16_t* x, uint8
 }
 
 hipError_t launch_gate_prepare(int d, int E, const float* w_gate, uint16_t* w_prep,
-                               hipStream_t s) {
+                               hipStream_t s, int* split, int S, int64_t T) {
   const int64_t n = (int64_t)E * d;
+  if (split != nullptr && (S < 1 || S > kMaxGateSplits)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gate_prepare_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, d, E,
-                     w_gate, w_prep);
+                     w_gate, w_prep, split, S, T);
   return hipGetLastError();
 }
 

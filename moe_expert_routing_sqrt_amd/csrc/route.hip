@@ -100,7 +100,10 @@ constexpr int kTokPerBlock = MOE_ROUTE_BLOCK;
 constexpr int kWavesPerWg = 16;
 
 struct RouteArgs {
-  const float* logits;
+  const float* logits;     // nparts partial products [nparts][T, E], summed in order
+  int64_t part_stride;     // elements between parts
+  int nparts;
+  float* logits_out;       // [T, E]: the summed logits, or nullptr
   const float* bias;
   const float* offset;
   int32_t* idx;
@@ -137,7 +140,12 @@ __global__ __launch_bounds__(kWavesPerWg * kWave) void route_select_kernel(const
     float s[EPL], b[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      float l = lane_ok ? p.logits[t * E + e0 + i] : 0.0f;
+      float l = 0.0f;
+      if (lane_ok) {
+        l = p.logits[t * E + e0 + i];
+        for (int q = 1; q < p.nparts; ++q) l = l + p.logits[q * p.part_stride + t * E + e0 + i];
+        if (p.logits_out != nullptr) p.logits_out[t * E + e0 + i] = l;
+      }
       if (p.offset != nullptr) l = l + off_l[i];
       s[i] = affinity_spec(l);
       float bb = s[i] + bias_l[i];
@@ -236,10 +244,10 @@ bool route_select_supported(int E, int G, int k, int gk) {
   return gk <= 4 && k <= 16;
 }
 
-hipError_t launch_route_select(const float* logits, const float* bias, const float* offset,
-                               int32_t* idx, float* w, int32_t* block_counts, int64_t T, int E,
-                               int G, int M, int k, int gk, hipStream_t s) {
-  RouteArgs a{logits, bias, offset, idx, w, block_counts, T, E, G, M, k, gk};
+hipError_t launch_route_select(const float* logits, int nparts, float* logits_out, const float* bias,
+                               const float* offset, int32_t* idx, float* w, int32_t* block_counts,
+                               int64_t T, int E, int G, int M, int k, int gk, hipStream_t s) {
+  RouteArgs a{logits, T * E, nparts, logits_out, bias, offset, idx, w, block_counts, T, E, G, M, k, gk};
   switch ((E + 63) / 64) {
     case 1: return launch_sel<1>(a, s);
     case 2: return launch_sel<2>(a, s);

@@ -107,7 +107,13 @@ def test_workspace_sizes():
     assert ws(_lib.MOE_OP_EXPERT_FFN, v3) == 2 * 768
     assert ws(_lib.MOE_OP_EXPERT_FFN, None) == 2 * 768
     assert ws(_lib.MOE_OP_EXPERT_FFN_BACKWARD, v3) == 768
-    assert ws(_lib.MOE_OP_ROUTE, v3) == 3 * 256 * 7168 * 2 + 16384 * 256 * 4
+    # route: the weight planes; bf16 x at E = 256 splits the gate product in 4
+    # over its 336 steps (64 row tiles x 4 = 256 tiles): its counters and
+    # offsets (768 B), then 4 partial products; fp32 x: the logits
+    assert ws(_lib.MOE_OP_ROUTE, v3) == 3 * 256 * 7168 * 2 + 768 + 4 * 16384 * 256 * 4
+    assert ws(_lib.MOE_OP_ROUTE, v3, _lib.MOE_F32) == 3 * 256 * 7168 * 2 + 16384 * 256 * 4
+    big = _lib.MoeShape(65536, 7168, 256, 8, 4, 8, 2, 2048)   # 256 row tiles: one split
+    assert ws(_lib.MOE_OP_ROUTE, big) == 3 * 256 * 7168 * 2 + 768 + 65536 * 256 * 4
     assert ws(99, v3) == 0
     assert ws(_lib.MOE_OP_ROUTE, _lib.MoeShape(16, 64, 15, 4, 2, 4, 2, 32)) == 0   # invalid shape
 

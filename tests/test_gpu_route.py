@@ -38,9 +38,13 @@ def test_route_bitexact_from_oracle_logits(name, T):
     assert np.array_equal(bc, block_counts(o["idx"], cfg.E))
 
 
-@pytest.mark.parametrize("name,T", [("tiny", None), ("flash", None), ("v3", None), ("v3", 1000), ("flash", 77)])
+@pytest.mark.parametrize("name,T", [("tiny", None), ("flash", None), ("v3", None), ("v3", 1000), ("flash", 77),
+                                    ("v3", 1), ("v3", 300), ("v3_skew_ep0", 4100)])
 def test_gate_logits_tolerance(name, T):
-    """Full sizes, and token counts that end in a partial 128- or 64-row tile."""
+    """Full sizes, and token counts that end in a partial 256-, 128- or 64-row
+    tile.  At E = 256 with bf16 x the gate product is split over its reduction
+    into partial products that the selection sums: 4 at V3 (64 row tiles), 8
+    at 1, 300, 1000 and 4100 tokens."""
     dev = need_gpu()
     cfg, inp, o = router_inputs(name, T)
     print(f"route S1 {name} T={cfg.T}", flush=True)
@@ -56,11 +60,13 @@ def test_gate_logits_tolerance(name, T):
     assert np.array_equal(host(w).view(np.uint32), gw.view(np.uint32))
 
 
-def test_logits_kept_in_workspace():
-    """logits = NULL: the route keeps them in its workspace; the selection is
-    the same as with a logits buffer."""
+@pytest.mark.parametrize("name,T", [("flash", None), ("v3", 1000)])
+def test_logits_kept_in_workspace(name, T):
+    """logits = NULL: the route keeps them (or, split, their partial
+    products) in its workspace; the selection is the same as with a logits
+    buffer."""
     dev = need_gpu()
-    cfg, inp, o = router_inputs("flash")
+    cfg, inp, o = router_inputs(name, T)
     sh = moe_shape(cfg)
     ws = M.workspace(M.MOE_OP_ROUTE, sh, M.MOE_BF16, dev)
     L, idx, w, bc = M.route(sh, inp["x"], inp["w_gate"], inp["bias"], ws=ws)
