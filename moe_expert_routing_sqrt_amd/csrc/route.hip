@@ -152,24 +152,54 @@ __global__ __launch_bounds__(kWavesPerWg * kWave) void route_select_kernel(const
       b[i] = bb == 0.0f ? 0.0f : bb;  // one zero: +0
     }
 
-    // group score: the gk largest b of the group, added largest first
-    bool used[EPL];
+    // The lane's EPL (key, s) pairs sorted by key, largest first: every
+    // round below takes the largest key not yet taken, which is then the head
+    // of the lane's list, and only the winning lane moves its list on.
+    uint64_t key[EPL];
+    float ks[EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) used[i] = false;
-    float gscore = 0.0f;
-    for (int r = 0; r < p.gk; ++r) {
-      uint64_t key = 0;
+    for (int i = 0; i < EPL; ++i) {
+      key[i] = lane_ok ? make_key(b[i], e0 + i) : 0;
+      ks[i] = s[i];
+    }
+#pragma unroll
+    for (int a = 0; a + 1 < EPL; ++a) {
+#pragma unroll
+      for (int c = 0; c + 1 < EPL - a; ++c) {
+        const bool sw = key[c + 1] > key[c];
+        const uint64_t k0 = sw ? key[c + 1] : key[c], k1 = sw ? key[c] : key[c + 1];
+        const float s0 = sw ? ks[c + 1] : ks[c], s1 = sw ? ks[c] : ks[c + 1];
+        key[c] = k0;
+        key[c + 1] = k1;
+        ks[c] = s0;
+        ks[c + 1] = s1;
+      }
+    }
+    // drops the head of a list in the lanes where `win` holds
+    auto pop = [&](uint64_t (&kl)[EPL], float* sl, bool win) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
-        uint64_t kk = (lane_ok && !used[i]) ? make_key(b[i], e0 + i) : 0;
-        key = kk > key ? kk : key;
+        const uint64_t nk = i + 1 < EPL ? kl[i + 1] : 0;
+        kl[i] = win ? nk : kl[i];
+        if (sl != nullptr) {
+          const float ns = i + 1 < EPL ? sl[i + 1] : 0.0f;
+          sl[i] = win ? ns : sl[i];
+        }
       }
-      key = group_max_u64(key, lpg);
-      const float v = key_value(key);
-      gscore = r == 0 ? v : gscore + v;
-      const int win = key_index(key);
+    };
+
+    // group score: the gk largest b of the group, added largest first
+    float gscore = 0.0f;
+    {
+      uint64_t gl[EPL];
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) used[i] = used[i] || (e0 + i == win);
+      for (int i = 0; i < EPL; ++i) gl[i] = key[i];
+      for (int r = 0; r < p.gk; ++r) {
+        const uint64_t m = group_max_u64(gl[0], lpg);
+        const float v = key_value(m);
+        gscore = r == 0 ? v : gscore + v;
+        pop(gl, nullptr, gl[0] == m && m != 0);
+      }
     }
 
     // keep the M best groups
@@ -184,30 +214,14 @@ __global__ __launch_bounds__(kWavesPerWg * kWave) void route_select_kernel(const
     }
 
     // k best experts inside the kept groups
-    bool taken[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) taken[i] = false;
     float S = 0.0f, my_s = 0.0f;
     int my_idx = 0;
     for (int j = 0; j < p.k; ++j) {
-      uint64_t key = 0;
-      float best_s = 0.0f;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        uint64_t kk = (gsel && !taken[i]) ? make_key(b[i], e0 + i) : 0;
-        if (kk > key) {
-          key = kk;
-          best_s = s[i];
-        }
-      }
-      const uint64_t m = group_max_u64(key, kWave);
+      const uint64_t cand = gsel ? key[0] : 0;
+      const uint64_t m = group_max_u64(cand, kWave);
       const int win = key_index(m);
-      const int owner = win / EPL;
-      const float s_win = lane_value(best_s, owner);
-      if (lane == owner) {
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) taken[i] = taken[i] || (e0 + i == win);
-      }
+      const float s_win = lane_value(ks[0], win / EPL);
+      pop(key, ks, cand == m);
       S = j == 0 ? s_win : S + s_win;
       if (lane == j) {
         my_idx = win;
