@@ -98,6 +98,7 @@ __device__ __forceinline__ float lane_value(float v, int lane_uniform) {
 
 constexpr int kTokPerBlock = MOE_ROUTE_BLOCK;
 constexpr int kWavesPerWg = 16;
+constexpr int kRankGroups = 16;  // up to this many groups: top-M by rank
 
 struct RouteArgs {
   const float* logits;     // nparts partial products [nparts][T, E], summed in order
@@ -202,14 +203,27 @@ __global__ __launch_bounds__(kWavesPerWg * kWave) void route_select_kernel(const
       }
     }
 
-    // keep the M best groups
+    // keep the M best groups: with few groups, a group is kept when fewer
+    // than M groups have a larger key (each group's key read from its first
+    // lane); otherwise M rounds of a wave-wide max
     uint64_t gkey = lane_ok ? make_key(gscore, my_group) : 0;
     bool gsel = false;
-    for (int r = 0; r < p.M; ++r) {
-      const uint64_t m = group_max_u64(gkey, kWave);
-      if (lane_ok && gkey == m) {
-        gsel = true;
-        gkey = 0;
+    if (p.G <= kRankGroups) {
+      int rank = 0;
+      for (int g = 0; g < p.G; ++g) {
+        const int src = g * lpg;
+        const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(gkey), src);
+        const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(gkey >> 32), src);
+        rank += ((static_cast<uint64_t>(hi) << 32) | lo) > gkey ? 1 : 0;
+      }
+      gsel = lane_ok && rank < p.M;
+    } else {
+      for (int r = 0; r < p.M; ++r) {
+        const uint64_t m = group_max_u64(gkey, kWave);
+        if (lane_ok && gkey == m) {
+          gsel = true;
+          gkey = 0;
+        }
       }
     }
 
