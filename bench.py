@@ -438,8 +438,10 @@ def main():
                        "select_us": sel_us, "select_bytes": alg["route_select_bytes"],
                        "select_gb_s": gbs(alg["route_select_bytes"], sel_ms),
                        "select_frac_hbm": gbs(alg["route_select_bytes"], sel_ms) / PEAK_HBM_GBS,
-                       "note": "gate_ms = route stage minus the selection timed alone (the weight planes' "
-                               "preparation counts with the gate product); gate_tflops on 2*T*d*E useful flops"}
+                       "note": "gate_ms = route stage minus the selection timed alone from finished logits "
+                               "(the weight planes' preparation, and in the step the summing of the split gate "
+                               "product's partial products inside the selection, count with the gate product); "
+                               "gate_tflops on 2*T*d*E useful flops"}
     stages = {
         "route": (route_stage
                   if a.router == "topk" else
