@@ -41,16 +41,16 @@ _SHARED_SOURCES = ("moe_expert_routing_sqrt_amd/csrc/gemm_common.h",
 TRAFFIC = {
     # the bf16 up-projection launch with the shared expert inside it
     "v3": {"sources": ("moe_expert_routing_sqrt_amd/csrc/ffn_bf16.hip",) + _SHARED_SOURCES,
-           "sources_sha256": "b4645d78893de762c82ed6cffd81e04c9e2ff51e1c8bb881d7ced387a2bcdbce",
+           "sources_sha256": "2f9740eafc21bbc3ef9bf932486c6418753a7510e47540fd4aeb4161d103d39e",
            "merged": True,
-           "fetch_kib": 21045893.2, "fetch_scale": 1.99997,
+           "fetch_kib": 19050597.8, "fetch_scale": 1.99997,
            "write_kib": 590195.8, "write_scale": 1.0},
     # the e4m3 routed up-projection launch (the shared expert has launches of its own)
     "v3_fp8": {"sources": ("moe_expert_routing_sqrt_amd/csrc/gemm_fp8p.hip",) + _SHARED_SOURCES,
-               "sources_sha256": "4cc3618b4d22b2f59997c40d8e92991931b96b5290f009352ea7abc875b08f12",
+               "sources_sha256": "a0e3f39332d50afa4c778655b57283fb15a7836d79e863c8f15ee6b1b6f6c9c6",
                "merged": False,
-               "fetch_kib": 10694486.7, "fetch_scale": 1.99997,
-               "write_kib": 275932.4, "write_scale": 1.0},
+               "fetch_kib": 10423854.1, "fetch_scale": 1.99997,
+               "write_kib": 274993.2, "write_scale": 1.0},
 }
 
 
@@ -70,6 +70,10 @@ def parse():
                     help="also time forward+backward steps (bf16 top-k workload) and report the backward")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 2 GiB copy (counter calibration for --pmc passes)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="expert products on most CUs beside a copy of the packed rows (the exchange's "
+                         "payload) on CUs reserved by stream CU masks; one JSON line")
+    ap.add_argument("--reserve", type=int, default=16, help="CUs --overlap reserves for the copy (multiple of 8)")
     ap.add_argument("--up-variants", action="store_true",
                     help="instead of the bench: time the routed up-projection against the same rows in "
                          "equal shares per expert and against one expert's weights (one JSON line)")
@@ -324,6 +328,114 @@ def up_variants(torch, M, cfg, layer, x, ids):
     print(json.dumps({"up_variants": res, "workload": workload_name(cfg), "rows": rows}), flush=True)
 
 
+def cu_mask_streams(torch, n_cus, reserve):
+    """Two streams that split the CUs (hipExtStreamCreateWithCUMask): the
+    reserved set takes reserve/8 CUs of every XCD -- bits x*32 + j for XCD x
+    under a per-XCD block numbering, and bits whose index mod 8 is x under an
+    interleaved one, so it is spread evenly either way -- the other stream the
+    rest.  Default priority for both."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    words = (n_cus + 31) // 32
+    per = reserve // 8
+    res = [0] * words
+    for x in range(8):
+        for j in range(per):
+            bit = x * 32 + (per * x + j) % 32
+            res[bit // 32] |= 1 << (bit % 32)
+    rest = [(~r) & 0xFFFFFFFF for r in res]
+    streams = []
+    for m in (rest, res):
+        h = ctypes.c_void_p()
+        arr = (ctypes.c_uint32 * words)(*m)
+        st = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), ctypes.c_uint32(words), arr)
+        if st != 0:
+            raise RuntimeError(f"hipExtStreamCreateWithCUMask failed ({st})")
+        streams.append(torch.cuda.ExternalStream(h.value))
+    destroy = lambda: [hip.hipStreamDestroy(ctypes.c_void_p(st.cuda_stream)) for st in streams]
+    return streams, res, destroy
+
+
+def overlap(torch, M, cfg, layer, x, ids, reserve):
+    """The expert products of one forward (up + SwiGLU, down; the shared expert
+    inside) beside a copy of the packed rows -- the bytes an expert-parallel
+    exchange moves for this GPU -- on another stream: each alone on the whole
+    chip, each alone on its part of a CU split (reserve CUs for the copy, the
+    rest for the products), both at once on the split, and both at once on two
+    plain streams.  Mean of 5 back-to-back repetitions each; the products'
+    output on the split is checked equal to the whole-chip one."""
+    for _ in range(3):
+        layer.forward(x, token_ids=ids)
+    torch.cuda.synchronize()
+    b = layer.dbufs
+    payload = b["xp"]
+    recv = torch.empty_like(payload)
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    (s_main, s_comm), res_mask, destroy_streams = cu_mask_streams(torch, n_cus, reserve)
+    p1, p2 = torch.cuda.Stream(), torch.cuda.Stream()
+    extra = None
+    if layer.merge_shared:
+        extra = dict(rows=layer.T, x=x, w13=layer.sh_w13, w2=layer.sh_w2, h=layer.sh_h, y=layer.ysh)
+
+    def experts():
+        for st in (M.MOE_FFN_UP, M.MOE_FFN_DOWN):
+            M.expert_ffn(b["offsets"], layer.max_rows, b["xp"], layer.w13, layer.w2, layer.dtype,
+                         xp_scale=b["xp_scale"], w13_scale=layer.w13_s, w2_scale=layer.w2_s, h=layer.h,
+                         h_scale=layer.h_s, yp=layer.yp, stages=st, ws=layer.ffn_ws, extra=extra)
+
+    def copy():
+        recv.copy_(payload)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+
+    def timed(jobs, reps=5):
+        """jobs: (stream, fn) pairs started together; ms per repetition from a
+        start event that every stream waits for to the last stream's end."""
+        for st, fn in jobs:   # one untimed round
+            with torch.cuda.stream(st):
+                fn()
+        torch.cuda.synchronize()
+        start, ends = ev(), []
+        start.record(cur)
+        for st, _ in jobs:
+            st.wait_event(start)
+        for st, fn in jobs:
+            with torch.cuda.stream(st):
+                for _ in range(reps):
+                    fn()
+            e = ev()
+            e.record(st)
+            ends.append(e)
+        torch.cuda.synchronize()
+        return max(start.elapsed_time(e) for e in ends) / reps
+
+    res = {}
+    res["experts_whole_chip_ms"] = timed([(cur, experts)])
+    y_ref = layer.yp.clone()
+    res["copy_whole_chip_ms"] = timed([(cur, copy)])
+    res["experts_on_split_ms"] = timed([(s_main, experts)])
+    assert torch.equal(layer.yp, y_ref), "expert products on the CU split differ"
+    res["copy_on_reserved_ms"] = timed([(s_comm, copy)])
+    res["both_on_split_ms"] = timed([(s_main, experts), (s_comm, copy)])
+    res["both_on_plain_streams_ms"] = timed([(p1, experts), (p2, copy)])
+    assert torch.equal(layer.yp, y_ref)
+    assert torch.equal(recv, payload)
+    torch.cuda.synchronize()
+    destroy_streams()
+    serial = res["experts_whole_chip_ms"] + res["copy_whole_chip_ms"]
+    res["serial_ms"] = serial
+    res["hidden_fraction_of_copy_on_split"] = (serial - res["both_on_split_ms"]) / res["copy_whole_chip_ms"]
+    # the copy's own time on its reserved CUs that the products' span covers
+    res["copy_covered_on_split"] = ((res["experts_on_split_ms"] + res["copy_on_reserved_ms"] - res["both_on_split_ms"])
+                                    / res["copy_on_reserved_ms"])
+    res["hidden_fraction_of_copy_plain"] = (serial - res["both_on_plain_streams_ms"]) / res["copy_whole_chip_ms"]
+    print(json.dumps({"overlap": res, "reserved_cus": reserve, "cus": n_cus,
+                      "reserved_mask": [hex(m) for m in res_mask],
+                      "payload_bytes": payload.numel() * payload.element_size(),
+                      "workload": workload_name(cfg)}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -353,6 +465,9 @@ def main():
     print(f"setup {time.perf_counter() - t_setup:.1f}s: {workload_name(cfg, a.router)}", file=sys.stderr, flush=True)
     if a.up_variants:
         up_variants(torch, M, cfg, layer, x, ids)
+        return
+    if a.overlap:
+        overlap(torch, M, cfg, layer, x, ids, a.reserve)
         return
 
     for _ in range(a.warmup):

@@ -87,6 +87,27 @@ int device_cu_count() {
   }
   return n;
 }
+
+// CUs the stream's work may use: the population of its CU mask (a stream made
+// with hipExtStreamCreateWithCUMask, e.g. to leave CUs to communication
+// kernels on another stream), else the device's.  Persistent launches size
+// their grid by it, so that no work-group waits for a CU the mask keeps from
+// the launch.
+int stream_cu_count(hipStream_t s) {
+  const int n = device_cu_count();
+  if (s == nullptr) return n;
+  constexpr int kMaxWords = 64;
+  uint32_t mask[kMaxWords] = {};
+  const int words = (n + 31) / 32;
+  if (words > kMaxWords) return n;
+  if (hipExtStreamGetCUMask(s, static_cast<uint32_t>(words), mask) != hipSuccess) {
+    (void)hipGetLastError();  // the query's own failure is not the launch's
+    return n;
+  }
+  int c = 0;
+  for (int w = 0; w < words; ++w) c += __builtin_popcount(mask[w]);
+  return c > 0 && c <= n ? c : n;
+}
 }  // namespace moe
 
 extern "C" {

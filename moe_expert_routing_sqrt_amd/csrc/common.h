@@ -240,13 +240,13 @@ __device__ __forceinline__ bool map_tile(const int* __restrict__ offsets, int n_
 // Persistent launches deal the logical tiles to the XCDs in chunks of ch
 // tiles, round robin: the i-th ticket of XCD x is tile
 // ((i / ch) * kXcds + x) * ch + i % ch.  A chunk is one XCD's worth of
-// concurrently running tiles (32 CUs), which share weight and activation tiles
-// in its L2; dealing whole chunks round robin spreads every part of the tile
-// order (e.g. a trailing dense group) over all XCDs.  A launch of fewer than
-// kXcds * 32 tiles uses ch = ceil(total / kXcds), one chunk per XCD.
-constexpr int kChunkTiles = 32;
+// concurrently running tiles (its work-groups: 32 on a whole MI355X, fewer on
+// a stream whose CU mask keeps some CUs for other work), which share weight
+// and activation tiles in its L2; dealing whole chunks round robin spreads
+// every part of the tile order (e.g. a trailing dense group) over all XCDs.
+// A launch of fewer tiles uses ch = ceil(total / kXcds), one chunk per XCD.
 __device__ __forceinline__ int xcd_chunk(int total) {
-  return max(1, min(kChunkTiles, (total + kXcds - 1) / kXcds));
+  return max(1, min(static_cast<int>(gridDim.x) / kXcds, (total + kXcds - 1) / kXcds));
 }
 __device__ __forceinline__ int xcd_tile(int i, int xcd, int ch) {
   return ((i / ch) * kXcds + xcd) * ch + i % ch;

@@ -614,8 +614,9 @@ hipError_t launch(FfnArgs& a, int64_t max_rows, hipStream_t s) {
   const int64_t mt = max_row_tiles(max_rows, a.offsets == nullptr ? 1 : a.n_exp, BM, a.x_rows);
   const int64_t tiles = mt * a.n_tiles;
   if (tiles <= 0) return hipSuccess;
-  // one work-group per CU (the LDS holds one), a multiple of the XCD count
-  const int64_t grid = (std::min<int64_t>(tiles, device_cu_count()) + kXcds - 1) / kXcds * kXcds;
+  // one work-group per CU the stream may use (the LDS holds one), a multiple
+  // of the XCD count
+  const int64_t grid = (std::min<int64_t>(tiles, stream_cu_count(s)) + kXcds - 1) / kXcds * kXcds;
   if (a.tickets == nullptr) return hipErrorInvalidValue;
   hipLaunchKernelGGL((ffn_gemm_kernel<MODE>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();

@@ -568,7 +568,7 @@ hipError_t launch_ffn_wgrad_bf16(int n_exp, const int32_t* offsets, int64_t rows
   if (tiles <= 0) return hipSuccess;
   // tile numbers and the 32-bit per-lane DMA offsets (64 K rows of A and B)
   if (tiles >= (1LL << 31) || (int64_t)BK * std::max(M, N) * 2 >= (1LL << 31)) return hipErrorInvalidValue;
-  const int64_t grid = (std::min<int64_t>(tiles, device_cu_count()) + kXcds - 1) / kXcds * kXcds;
+  const int64_t grid = (std::min<int64_t>(tiles, stream_cu_count(s)) + kXcds - 1) / kXcds * kXcds;
   hipLaunchKernelGGL(ffn_wgrad_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

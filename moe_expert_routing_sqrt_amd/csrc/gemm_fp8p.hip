@@ -644,7 +644,7 @@ hipError_t launch(Fp8Args& a, int64_t max_rows, hipStream_t s) {
   const int64_t mt = max_row_tiles(max_rows, a.offsets == nullptr ? 1 : a.n_exp, BM);
   const int64_t tiles = mt * a.n_tiles;
   if (tiles <= 0) return hipSuccess;
-  const int64_t grid = (std::min<int64_t>(tiles, device_cu_count()) + kXcds - 1) / kXcds * kXcds;
+  const int64_t grid = (std::min<int64_t>(tiles, stream_cu_count(s)) + kXcds - 1) / kXcds * kXcds;
   if (a.tickets == nullptr) return hipErrorInvalidValue;
   hipLaunchKernelGGL((ffn_fp8_kernel<MODE>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();

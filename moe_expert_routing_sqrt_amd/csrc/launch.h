@@ -11,6 +11,8 @@ namespace moe {
 
 // compute units of the current device (cached per device; 256 if the query fails)
 int device_cu_count();
+// CUs a launch on stream s may use (its CU mask, else the device's)
+int stream_cu_count(hipStream_t s);
 
 // gate logits
 hipError_t launch_gate_gemm_bf16(const uint16_t* x, const uint16_t* w_prep, float* logits,

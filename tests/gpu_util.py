@@ -85,3 +85,15 @@ def expert_host(cfg, e, dev, shared=False):
     """fp32 host copies of one expert's weights as the GPU holds them."""
     w13, w2 = gen.expert_weights(cfg, e, device=dev, shared=shared)
     return host(w13), host(w2)
+
+
+def cu_mask_stream(torch, words_mask):
+    """A torch stream on a HIP stream limited to the CUs of a bit mask (one bit
+    per CU, 32 per word: hipExtStreamCreateWithCUMask), default priority."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    h = ctypes.c_void_p()
+    arr = (ctypes.c_uint32 * len(words_mask))(*words_mask)
+    st = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), ctypes.c_uint32(len(words_mask)), arr)
+    assert st == 0, f"hipExtStreamCreateWithCUMask failed ({st})"
+    return torch.cuda.ExternalStream(h.value)

@@ -13,7 +13,7 @@ import torch
 
 import moe_expert_routing_sqrt_amd as M
 from moe_inputs import configs as C, generate as gen
-from gpu_util import dev_i32, need_gpu
+from gpu_util import cu_mask_stream, dev_i32, need_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -67,6 +67,39 @@ def test_expert_ffn_on_four_streams(dtype):
         rows = c[1]
         for y in outs[i]:
             assert torch.equal(y[:rows], ref[i][:rows]), i
+
+
+@pytest.mark.parametrize("dtype", [M.MOE_BF16, M.MOE_E4M3])
+def test_expert_ffn_on_cu_masked_streams(dtype):
+    """Persistent launches size their grid by the stream's CU mask: on a
+    stream limited to 240 CUs and on one limited to 16 (two per XCD), each
+    beside the other, the products equal the whole-chip ones bit for bit."""
+    dev = need_gpu()
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    print(f"expert ffn on CU-masked streams, dtype={dtype}, {n_cus} CUs", flush=True)
+    words = (n_cus + 31) // 32
+    res = [0] * words
+    for x in range(min(8, words)):
+        res[x] = 3 << (2 * x)  # bits x*32 + 2x, x*32 + 2x + 1
+    rest = [(~r) & 0xFFFFFFFF for r in res]
+    big, small = cu_mask_stream(torch, rest), cu_mask_stream(torch, res)
+    d, d_ff = 1024, 512
+    cases = [_case(21 + i, d, d_ff, dtype, dev) for i in range(2)]
+    ref = [_run(*c).clone() for c in cases]
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    wss = [M.workspace(M.MOE_OP_EXPERT_FFN, None, dtype, dev) for _ in cases]
+    outs = [[], []]
+    for s in (big, small):
+        s.wait_stream(main)
+    for rep in range(2):
+        for i, s in enumerate((big, small)):
+            with torch.cuda.stream(s):
+                outs[i].append(_run(*cases[i], ws=wss[i]))
+    torch.cuda.synchronize()
+    for i, c in enumerate(cases):
+        for y in outs[i]:
+            assert torch.equal(y[:c[1]], ref[i][:c[1]]), i
 
 
 @pytest.mark.parametrize("dtype", [M.MOE_BF16, M.MOE_E4M3])
