@@ -119,8 +119,10 @@ def algorithmic(cfg, merged=False):
            if cfg.dtype == "fp8" else 0),
         "ffn_down_flops": lambda rows: 2 * d * d_ff * (rows + ms),
         "shared_flops": 0 if merged else 6 * d * d_ff * T,
+        # the packed rows and (dest, w) in, the shared expert's rows in (not for
+        # an expert-parallel share), the output out (a share: fp32, written)
         "combine_bytes": lambda rows: rows * d * act + 8 * T * k + (T * d * act if not cfg.local else 0)
-        + T * d * (4 * 2 if cfg.local else act),
+        + T * d * (4 if cfg.local else act),
         "pairs": P,
     }
 

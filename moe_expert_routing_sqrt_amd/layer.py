@@ -107,9 +107,10 @@ class MoELayer:
         save_for_backward: the expert FFNs also keep their pre-activations, so
         backward() does not recompute them (bf16 top-k layer).
         With a local expert range (one expert-parallel rank's share) the
-        output is that share in fp32: into self.out (cleared first) when `out`
-        is None, else added to the caller's fp32 `out` (a scatter-add of this
-        rank's share into a buffer that may hold the others')."""
+        output is that share in fp32: written to self.out (0 for tokens with no
+        local expert) when `out` is None, else added to the caller's fp32 `out`
+        (a scatter-add of this rank's share into a buffer that may hold the
+        others')."""
         self._saved = save_for_backward
         if save_for_backward:
             return self._forward_train(x, marks)
@@ -155,10 +156,12 @@ class MoELayer:
             ysh = self.ysh
         mark(5)
         if out is None:
+            # the layer's own output: every row written (a local share's rows
+            # without a local expert get 0), nothing read back
+            combine(sh, b["dest"], self.topk_w, self.yp, ysh, out=self.out, accumulate=False)
             out = self.out
-            if self.local:
-                out.zero_()
-        combine(sh, b["dest"], self.topk_w, self.yp, ysh, out=out, accumulate=self.local)
+        else:
+            combine(sh, b["dest"], self.topk_w, self.yp, ysh, out=out, accumulate=self.local)
         mark(6)
         return out
 

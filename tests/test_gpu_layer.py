@@ -195,8 +195,10 @@ def test_layer_v3_sampled_tokens(name):
 
 def test_layer_local_share_twice():
     """A local expert range forward into the layer's own fp32 output, twice in
-    a row without clearing it by hand: both results equal the oracle's share
-    (the layer clears its output before the scatter-add)."""
+    a row, the buffer holding NaN before the first: both results equal the
+    oracle's share (the layer writes every row of its own output, 0 where no
+    local expert was chosen).  Into a caller's fp32 buffer the share is added
+    to what the buffer holds."""
     dev = need_gpu()
     cfg = C.get("v3_skew_ep0").with_(T=2048, d=512, d_ff=256)
     print(f"layer local share twice T={cfg.T} d={cfg.d}", flush=True)
@@ -205,8 +207,11 @@ def test_layer_local_share_twice():
     layer = _layer(cfg, inp, ex)
     L = OR.gate_logits(host(inp["x"]), host(inp["w_gate"]))
     o = {"bias": host(inp["bias"]), "offset": host(inp["logit_offset"])}
+    layer.out.fill_(float("nan"))
     first = host(layer.forward(inp["x"])).copy()
     second = host(layer.forward(inp["x"]))
+    acc = torch.full((cfg.T, cfg.d), 1.0, dtype=torch.float32, device=dev)
+    added = host(layer.forward(inp["x"], out=acc))
     torch.cuda.synchronize()
     idx_g, w_g = host(layer.idx), host(layer.topk_w)
     # the oracle's share for the GPU's own routing (any flips are then shared)
@@ -218,3 +223,7 @@ def test_layer_local_share_twice():
     print(f"  local rows per expert {counts.tolist()}")
     assert rel_max_err(first, ref) <= 2e-2
     assert np.array_equal(first, second)
+    # the add starts from the buffer's value, so it rounds differently from
+    # 1 + share: a few fp32 ulps of the larger term
+    scale = 1.0 + float(np.abs(first).max())
+    assert float(np.abs(added.astype(np.float64) - (1.0 + first.astype(np.float64))).max()) <= 1e-5 * scale
