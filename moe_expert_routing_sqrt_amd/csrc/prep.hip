@@ -44,6 +44,58 @@ __global__ __launch_bounds__(256) void gate_prepare_kernel(int d, int E, const f
   out[2 * plane + i] = lo;
 }
 
+// The same split, 64 x 64 tiles through LDS (d % 64 == 0, E % 64 == 0): the
+// tile is read as 64 rows of W_g (64 experts, contiguous) and written as 64
+// plane rows (64 columns of d, contiguous), both in whole cache lines.
+__global__ __launch_bounds__(256) void gate_prepare_tiled_kernel(int d, int E, const float* __restrict__ w,
+                                                                 uint16_t* __restrict__ out, int* split, int S,
+                                                                 int64_t T) {
+  __shared__ float tile[64][65];
+  if (split != nullptr && blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int j = threadIdx.x; j < kTicketInts; j += 256) split[j] = 0;
+    if (threadIdx.x <= S) split[kTicketInts + threadIdx.x] = static_cast<int>(threadIdx.x * T);
+  }
+  const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int t = threadIdx.x;
+  {
+    const int c = (t % 16) * 4;  // 4 experts per thread
+#pragma unroll
+    for (int r = t / 16; r < 64; r += 16) {
+      const float4 v = *reinterpret_cast<const float4*>(w + (int64_t)(k0 + r) * E + e0 + c);
+      tile[r][c] = v.x;
+      tile[r][c + 1] = v.y;
+      tile[r][c + 2] = v.z;
+      tile[r][c + 3] = v.w;
+    }
+  }
+  __syncthreads();
+  const int e = t / 4, kc = (t % 4) * 16;  // 16 columns of d per thread
+  uint16_t hi[16], mid[16], lo[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float v = tile[kc + j][e];
+    hi[j] = f32_to_bf16(v);
+    const float r1 = v - bf16_to_f32(hi[j]);
+    mid[j] = f32_to_bf16(r1);
+    const float r2 = r1 - bf16_to_f32(mid[j]);
+    lo[j] = f32_to_bf16(r2);
+  }
+  const int64_t plane = (int64_t)E * d;
+  const int64_t base = (int64_t)(e0 + e) * d + k0 + kc;
+  auto put = [&](uint16_t* dst, const uint16_t* v) {
+    uint4 a, b;
+    a.x = v[0] | (uint32_t)v[1] << 16; a.y = v[2] | (uint32_t)v[3] << 16;
+    a.z = v[4] | (uint32_t)v[5] << 16; a.w = v[6] | (uint32_t)v[7] << 16;
+    b.x = v[8] | (uint32_t)v[9] << 16; b.y = v[10] | (uint32_t)v[11] << 16;
+    b.z = v[12] | (uint32_t)v[13] << 16; b.w = v[14] | (uint32_t)v[15] << 16;
+    reinterpret_cast<uint4*>(dst)[0] = a;
+    reinterpret_cast<uint4*>(dst)[1] = b;
+  };
+  put(out + base, hi);
+  put(out + plane + base, mid);
+  put(out + 2 * plane + base, lo);
+}
+
 constexpr int kBlk = MOE_FP8_TILE;
 
 __global__ __launch_bounds__(256) void quantize_blocks_kernel(int rows, int cols,
@@ -131,6 +183,12 @@ hipError_t launch_gate_prepare(int d, int E, const float* w_gate, uint16_t* w_pr
                                hipStream_t s, int* split, int S, int64_t T) {
   const int64_t n = (int64_t)E * d;
   if (split != nullptr && (S < 1 || S > kMaxGateSplits)) return hipErrorInvalidValue;
+  if (d % 64 == 0 && E % 64 == 0 && (reinterpret_cast<uintptr_t>(w_gate) & 15) == 0 &&
+      (reinterpret_cast<uintptr_t>(w_prep) & 31) == 0) {
+    hipLaunchKernelGGL(gate_prepare_tiled_kernel, dim3((unsigned)(d / 64), (unsigned)(E / 64)), dim3(256), 0, s,
+                       d, E, w_gate, w_prep, split, S, T);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(gate_prepare_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, d, E,
                      w_gate, w_prep, split, S, T);
   return hipGetLastError();
