@@ -89,6 +89,33 @@ def test_route_workspace():
     assert _route(ctypes.byref(s0), ws=FAKE, wsb=planes) == 0
 
 
+def test_route_workspace_split_gate():
+    """bf16 x with E = 256: with more than one split the partial products need
+    the same workspace whether or not the caller keeps the logits; with one
+    split (256 row tiles already fill the chip) the product writes the logits
+    directly, so a caller that keeps them needs only the planes and the
+    split's counters.  One byte less is rejected before anything is launched
+    (fp32 x takes the plain product: planes, plus the logits only when they
+    are not returned)."""
+    planes = 3 * 256 * 512 * 2
+    split = 768
+    # (24 steps at d = 512: a split count divides them into even parts of at
+    # least 4, so 6 at most)
+    for T, S in ((1, 6), (300, 6), (16384, 4), (65536, 1)):
+        s = _sh(T=T, d=512, E=256, G=8, M=4, k=8, gk=2)
+        sh = ctypes.byref(s)
+        need = L.moe_workspace_size(_lib.MOE_OP_ROUTE, sh, _lib.MOE_BF16)
+        logits_bytes = (T * 256 * 4 + 255) // 256 * 256
+        assert need == planes + split + (S if S > 1 else 1) * logits_bytes, (T, S)
+        assert _route(sh, logits=None, wsb=need - 1) == -3, T
+        kept = need if S > 1 else planes + split
+        assert _route(sh, logits=FAKE, wsb=kept - 1) == -3, T
+        need32 = L.moe_workspace_size(_lib.MOE_OP_ROUTE, sh, _lib.MOE_F32)
+        assert need32 == planes + (T * 256 * 4 + 255) // 256 * 256
+        assert _route(sh, xdt=_lib.MOE_F32, logits=None, wsb=need32 - 1) == -3
+        assert _route(sh, xdt=_lib.MOE_F32, logits=FAKE, wsb=planes - 1) == -3
+
+
 def test_route_unsupported_and_empty():
     sh = _sh(E=320, G=5, M=2, k=4, gk=2)
     assert _route(ctypes.byref(sh)) == -2
