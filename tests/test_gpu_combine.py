@@ -33,6 +33,33 @@ def test_combine_workload(name):
         assert np.all(np.abs(host(out) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max())
 
 
+@pytest.mark.timeout(400)
+def test_combine_max_size_sampled():
+    """65536 tokens at V3 (524288 rows of 7168): 2048 sampled tokens and the
+    last one against the oracle's combine of just those tokens' rows."""
+    dev = need_gpu()
+    cfg, inp, o = router_inputs("v3", 65536)
+    print(f"combine S5 v3 T={cfg.T} (sampled tokens)", flush=True)
+    counts, offsets, dest, src = OD.dispatch(o["idx"], cfg.E)
+    g = torch.Generator(device=dev).manual_seed(17)
+    yp = torch.randn((cfg.pairs, cfg.d), generator=g, device=dev).to(torch.bfloat16)
+    ysh = torch.randn((cfg.T, cfg.d), generator=g, device=dev).to(torch.bfloat16)
+    out = M.combine(moe_shape(cfg), dev_i32(dest, dev), dev_f32(o["w"], dev), yp, ysh)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    toks = np.array(sorted(set(rng.choice(cfg.T, 2048, replace=False).tolist()) | {cfg.T - 1}))
+    rows = dest[toks].reshape(-1)
+    tdev = torch.from_numpy(toks.astype(np.int64)).to(dev)
+    yp_sub = host(yp[torch.from_numpy(rows.astype(np.int64)).to(dev)])
+    dest_sub = np.arange(rows.size, dtype=np.int32).reshape(len(toks), cfg.k)
+    ref = OC.combine(yp_sub, dest_sub, o["w"][toks], ysh=host(ysh[tdev]))
+    got = host(out[tdev])
+    err = rel_max_err(got, ref)
+    print(f"  rel max err {err:.3e} on {len(toks)} tokens")
+    assert err <= 2e-2
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max())
+
+
 def test_identity_experts_give_weight_sum_times_x():
     dev = need_gpu()
     cfg, inp, o = router_inputs("flash")

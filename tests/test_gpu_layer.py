@@ -154,14 +154,14 @@ def _forward_with_oracle_routing(layer, cfg, o, x, dev):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["v3", "v3_skew_ep0", "v3_skew_ep63"])
-def test_layer_v3_sampled_tokens(name):
-    """Full V3 size (and one expert-parallel rank's share under skew): 1024
-    sampled tokens plus the last one; the flipped tokens are listed and
-    checked, the matched ones compared, and all of them compared again with
-    the oracle's routing substituted."""
+@pytest.mark.parametrize("name,T", [("v3", None), ("v3_skew_ep0", None), ("v3_skew_ep63", None), ("v3", 65536)])
+def test_layer_v3_sampled_tokens(name, T):
+    """Full V3 size (and one expert-parallel rank's share under skew; and 4x
+    the tokens, 524288 routed rows): 1024 sampled tokens plus the last one; the
+    flipped tokens are listed and checked, the matched ones compared, and all
+    of them compared again with the oracle's routing substituted."""
     dev = need_gpu()
-    cfg, inp, o = router_inputs(name)
+    cfg, inp, o = router_inputs(name, T)
     print(f"layer S6 {name} (sampled tokens)", flush=True)
     ex = gen.make_experts(cfg, device=dev)
     layer = _layer(cfg, inp, ex)
