@@ -7,7 +7,11 @@ shared expert -> combine) over one batch of T tokens, inputs and weights
 resident in HBM.  Prints one JSON line: tokens/s for the whole step, per-stage
 times from HIP events on the stream the kernels run on, the roofline of the
 dominant kernel (the routed up-projection GEMM + SwiGLU), and the CPU oracle
-timed on a bounded sample of the same workload.
+timed on a bounded sample of the same workload.  The full default report (V3,
+CPU baseline on) also runs the other workloads -- Flash, both V3 skew ranks,
+the e4m3 experts, the hash router and forward + backward -- each in a child
+process of its own, and adds their figures as other_workloads (--others off:
+skip them).
 """
 from __future__ import annotations
 
@@ -15,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -74,6 +79,11 @@ def parse():
                     help="expert products on most CUs beside a copy of the packed rows (the exchange's "
                          "payload) on CUs reserved by stream CU masks; one JSON line")
     ap.add_argument("--reserve", type=int, default=16, help="CUs --overlap reserves for the copy (multiple of 8)")
+    ap.add_argument("--others", default="auto", choices=("auto", "on", "off"),
+                    help="also run the other workloads (Flash, both V3 skew ranks, e4m3, hash router, "
+                         "forward + backward), each in a child process of its own, and add their figures "
+                         "to the line as other_workloads; auto: only on the full default report (V3, "
+                         "top-k, CPU baseline on)")
     ap.add_argument("--up-variants", action="store_true",
                     help="instead of the bench: time the routed up-projection against the same rows in "
                          "equal shares per expert and against one expert's weights (one JSON line)")
@@ -328,6 +338,48 @@ def up_variants(torch, M, cfg, layer, x, ids):
         ms = e0.elapsed_time(e1) / 5
         res[name] = {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
     print(json.dumps({"up_variants": res, "workload": workload_name(cfg), "rows": rows}), flush=True)
+
+
+# the other workloads of the full report: name, bench.py arguments
+OTHERS = (("flash", ["--workload", "flash"]),
+          ("v3_skew_ep0", ["--workload", "v3_skew_ep0"]),
+          ("v3_skew_ep63", ["--workload", "v3_skew_ep63"]),
+          ("v3_fp8", ["--workload", "v3_fp8"]),
+          ("v3_hash_router", ["--router", "hash"]),
+          ("v3_forward_backward", ["--backward"]))
+
+
+def other_workloads(steps, warmup):
+    """Each other workload in a child process of its own (its own weights and
+    buffers; this process's are idle meanwhile), summarised from the child's
+    line."""
+    out = {}
+    for name, args in OTHERS:
+        cmd = [sys.executable, "-u", os.path.abspath(__file__), *args, "--steps", str(steps), "--warmup",
+               str(warmup), "--cpu-sample", "0", "--others", "off"]
+        print(f"other workload {name} ...", file=sys.stderr, flush=True)
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
+        except subprocess.TimeoutExpired:
+            out[name] = {"error": "timed out after 900 s"}
+            continue
+        line = next((l for l in reversed(r.stdout.splitlines()) if l.startswith('{"metric"')), None)
+        if r.returncode != 0 or line is None:
+            out[name] = {"error": f"exit status {r.returncode}", "stderr_tail": r.stderr[-400:]}
+            continue
+        j = json.loads(line)
+        o = {"workload": j["config"]["workload"], "dtype": j["dtype"], "ms_per_step": j["ms_per_step"],
+             "tokens_per_s": j["value"], "steps": j["steps"],
+             "stages_ms": {k: v["ms"] for k, v in j["stages"].items()},
+             "up_projection_frac_of_peak": j["roofline"]["frac"], "gemm_frac_of_peak": j["gemm_mfma_frac"]}
+        for k in ("dispatch", "combine"):
+            o[f"{k}_frac_hbm"] = j["stages"][k].get("frac_hbm")
+        if "backward" in j:
+            b = j["backward"]
+            o["backward"] = {k: b[k] for k in ("steps", "fwd_bwd_ms_per_step", "fwd_bwd_tokens_per_s", "bwd_ms",
+                                               "stages_ms", "routed_experts_frac_mfma")}
+        out[name] = o
+    return out
 
 
 def cu_mask_streams(torch, n_cus, reserve):
@@ -641,6 +693,12 @@ def main():
                                               None if ids is None else ids.cpu().numpy())
     else:
         result["cpu_baseline"] = None
+    run_others = a.others == "on" or (a.others == "auto" and a.workload == "v3" and a.router == "topk" and
+                                      a.cpu_sample > 0 and not a.backward)
+    if run_others:
+        del layer, inp, ex, x
+        torch.cuda.empty_cache()
+        result["other_workloads"] = other_workloads(a.steps, a.warmup)
     print(json.dumps(result))
 
 
