@@ -156,14 +156,15 @@ size_t moe_workspace_size(int op, const moe_shape* shape, int dtype);
  * d % 64 == 0 and E % 64 == 0 (else fp32 vector products, same planes).
  *   ws            moe_workspace_size(MOE_OP_ROUTE, shape, x_dtype) bytes: the
  *                 planes [3, E, d] bf16 (rewritten by every call); for bf16 x
- *                 with E % 256 == 0 the gate product runs split over its
+ *                 on the matrix cores the gate product runs split over its
  *                 reduction (the 3*d/64 plane-and-column steps) into S <= 8
  *                 fp32 partial products [S, T, E] that the selection sums in
  *                 order (((p0 + p1) + p2) + ...), with S chosen from T, d and E
- *                 alone, so the workspace then also holds the split's counters
- *                 and, for S > 1, the partial products; otherwise the logits
- *                 when `logits` is NULL.  Nothing in it needs to start at
- *                 zero.  Unused with LOGITS_IN (may be NULL).
+ *                 alone, so the workspace then also holds, for S > 1, the
+ *                 partial products, and for E % 256 == 0 the split's
+ *                 counters; with S = 1 (or fp32 x) it holds the logits when
+ *                 `logits` is NULL.  Nothing in it needs to start at zero.
+ *                 Unused with LOGITS_IN (may be NULL).
  */
 int moe_route(const moe_shape* shape, const void* x, int x_dtype, const float* w_gate,
               const float* bias, const float* logit_offset, float* logits, int32_t* topk_idx,

@@ -131,21 +131,27 @@ const char* moe_status_str(int status) {
 static size_t route_planes_bytes(const moe_shape* s) {
   return align256(static_cast<size_t>(3) * s->E * s->d * sizeof(uint16_t));
 }
-// route workspace: the planes; for the split gate product (bf16 x) its ticket
-// set and offsets, then its S partial products when S > 1; the logits when
-// the caller keeps none and they are not the one partial product
+// route workspace: the planes; for the gate product on the expert GEMM
+// kernel (bf16 x, E % 256 == 0) its ticket set and offsets; the S partial
+// products of a split gate product when S > 1; else the logits when the
+// caller keeps none
 static size_t route_split_bytes() { return align256((kTicketInts + kMaxGateSplits + 1) * sizeof(int)); }
-static int route_splits(const moe_shape* s, int x_dtype) {
+// splits of the gate product on the expert GEMM kernel (0: not that path)
+static int route_gate_splits(const moe_shape* s, int x_dtype) {
   return x_dtype == MOE_BF16 ? gate_split_count(s->T, s->d, s->E) : 0;
+}
+// splits of the gate product on either matrix-core path (0: vector ALUs)
+static int route_splits(const moe_shape* s, int x_dtype) {
+  const int S = route_gate_splits(s, x_dtype);
+  if (S >= 1 || x_dtype != MOE_BF16) return S;
+  return gate_gemm_split_count(s->T, s->d, s->E);
 }
 static size_t route_ws_bytes(const moe_shape* s, bool logits_in_ws, int x_dtype) {
   const size_t logits_bytes = align256(static_cast<size_t>(s->T) * s->E * sizeof(float));
   size_t b = route_planes_bytes(s);
+  if (route_gate_splits(s, x_dtype) >= 1) b += route_split_bytes();
   const int S = route_splits(s, x_dtype);
-  if (S >= 1) {
-    b += route_split_bytes();
-    if (S > 1) return b + S * logits_bytes;
-  }
+  if (S > 1) return b + S * logits_bytes;
   return b + (logits_in_ws ? logits_bytes : 0);
 }
 
@@ -179,27 +185,27 @@ int moe_route(const moe_shape* shape, const void* x, int x_dtype, const float* w
     char* w = static_cast<char*>(ws);
     uint16_t* planes = reinterpret_cast<uint16_t*>(w);
     w += route_planes_bytes(shape);
+    const int Sg = route_gate_splits(shape, x_dtype);
     const int S = route_splits(shape, x_dtype);
     int* split = nullptr;
-    if (S >= 1) {
+    if (Sg >= 1) {
       split = reinterpret_cast<int*>(w);
       w += route_split_bytes();
     }
     float* out = logits != nullptr ? logits : reinterpret_cast<float*>(w);
-    hipError_t e = launch_gate_prepare(shape->d, shape->E, w_gate, planes, s, split, S, shape->T);
+    hipError_t e = launch_gate_prepare(shape->d, shape->E, w_gate, planes, s, split, Sg, shape->T);
     if (e != hipSuccess) return MOE_ERR_HIP;
+    // S > 1: partial products in the workspace, summed (and written to the
+    // caller's logits) by the selection
+    float* const dst = S > 1 ? reinterpret_cast<float*>(w) : out;
     if (S >= 1) {
-      // S > 1: partial products in the workspace, summed (and written to the
-      // caller's logits) by the selection
-      float* dst = S > 1 ? reinterpret_cast<float*>(w) : out;
-      e = launch_gate_split_bf16(static_cast<const uint16_t*>(x), planes, dst, shape->T, shape->d, shape->E, S,
-                                 split + kTicketInts, split, s);
+      const uint16_t* xb = static_cast<const uint16_t*>(x);
+      e = Sg >= 1 ? launch_gate_split_bf16(xb, planes, dst, shape->T, shape->d, shape->E, S, split + kTicketInts,
+                                           split, s)
+                  : launch_gate_gemm_bf16(xb, planes, dst, shape->T, shape->d, shape->E, S, s);
       parts = dst;
       nparts = S;
       if (S > 1) logits_out = logits;
-    } else if (x_dtype == MOE_BF16 && gate_gemm_bf16_supported(shape->d, shape->E)) {
-      e = launch_gate_gemm_bf16(static_cast<const uint16_t*>(x), planes, out, shape->T, shape->d, shape->E, s);
-      parts = out;
     } else {
       e = launch_gate_gemm_simt(x, x_dtype, planes, out, shape->T, shape->d, shape->E, s);
       parts = out;

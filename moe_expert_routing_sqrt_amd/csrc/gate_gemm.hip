@@ -19,6 +19,11 @@
 // the loads for step k+2 are in flight while step k computes, with one
 // barrier per step.
 //
+// Split over the reduction: the 3 * d / 64 plane-and-column steps divide into
+// S equal ranges, one per grid row (blockIdx.y), each writing its own fp32
+// partial product [T, E] (the route selection sums them in order), so that a
+// product with few output tiles still fills the chip.
+//
 #include "common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -40,6 +45,8 @@ struct GateArgs {
   int64_t rows_total;      // T
   int K;                   // d
   int n_tiles;             // E / BN
+  int ksteps;              // steps of each split (grid row y takes [y * ksteps, (y + 1) * ksteps))
+  int64_t c_split_stride;  // elements between the splits' partial products
 };
 
 template <int BM, int BN, int WAVES_M>
@@ -96,15 +103,18 @@ __global__ __launch_bounds__(kThreads, 1) void gate_gemm_kernel(const GateArgs p
     b_src[i] = p.B + (int64_t)(ti.n_tile * BN + r) * p.K + lch * 8;
   }
 
-  const int nkp = p.K / BK;
-  const int nsteps = PLANES * nkp;
+  const int split = blockIdx.y;
+  const int kbase = split * p.ksteps;  // this split's first plane-and-column step
+  const int nsteps = p.ksteps;
+  float* const C = p.C + (int64_t)split * p.c_split_stride;
 
   // DMA of one K step, split into parts so they can be spread between MFMA
   // groups (issuing all at once stalls the wave on address back-pressure).
   constexpr int NDMA = ADMA + BDMA;
   auto issue_part = [&](int kt, uint4* sa, uint4* sb, int q0, int q1) {
-    const int kin = kt / PLANES;
-    const int plane = kt - kin * PLANES;
+    const int kg = kbase + kt;
+    const int kin = kg / PLANES;
+    const int plane = kg - kin * PLANES;
     const int k0 = kin * BK;
     const uint32_t la = lds_addr(sa), lb = lds_addr(sb);
     const int64_t boff = (int64_t)plane * p.b_plane_stride + k0;
@@ -200,28 +210,55 @@ __global__ __launch_bounds__(kThreads, 1) void gate_gemm_kernel(const GateArgs p
   for (int q = tid; q < ti.rows * CPR; q += kThreads) {
     const int r = q / CPR, c = q % CPR;
     const uint4 v = *reinterpret_cast<const uint4*>(stage + r * PITCH + c * 16);
-    char* dst = reinterpret_cast<char*>(p.C + (ti.row0 + r) * p.ldc + col0) + c * 16;
+    char* dst = reinterpret_cast<char*>(C + (ti.row0 + r) * p.ldc + col0) + c * 16;
     *reinterpret_cast<uint4*>(dst) = v;
   }
 #endif
 }
 
 template <int BM, int BN, int WAVES_M>
-hipError_t launch(const GateArgs& a, hipStream_t s) {
+hipError_t launch(const GateArgs& a, int S, hipStream_t s) {
   const int64_t mt = (a.rows_total + BM - 1) / BM;
   const int64_t grid = (mt * a.n_tiles + kXcds - 1) / kXcds * kXcds;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gate_gemm_kernel<BM, BN, WAVES_M>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((gate_gemm_kernel<BM, BN, WAVES_M>), dim3((unsigned)grid, (unsigned)S), dim3(kThreads), 0,
+                     s, a);
   return hipGetLastError();
 }
+
+// the tile of a product with E output columns: 128 x 128 when E % 128 == 0,
+// else 64 x 64
+int tile_of(int E) { return E % 128 == 0 ? 128 : 64; }
 
 }  // namespace
 
 bool gate_gemm_bf16_supported(int d, int E) { return d % BK == 0 && E % 64 == 0; }
 
+// The most splits (up to kMaxGateSplits) that keep the launch within 256
+// work-groups (one per CU of an MI355X; a fixed figure, so that the workspace
+// size does not depend on the device), each with a whole number of at least
+// two steps.
+int gate_gemm_split_count(int64_t T, int d, int E) {
+  if (!gate_gemm_bf16_supported(d, E)) return 0;
+  constexpr int64_t kTargetTiles = 256;
+  const int tile = tile_of(E);
+  const int steps = PLANES * (d / BK);
+  const int64_t tiles1 = (T + tile - 1) / tile * (E / tile);
+  int best = 1;
+  for (int S = 2; S <= kMaxGateSplits; ++S) {
+    if (tiles1 * S > kTargetTiles) break;
+    if (steps % S == 0 && steps / S >= 2) best = S;
+  }
+  return best;
+}
+
 hipError_t launch_gate_gemm_bf16(const uint16_t* x, const uint16_t* w_prep, float* logits,
-                                 int64_t T, int d, int E, hipStream_t s) {
+                                 int64_t T, int d, int E, int S, hipStream_t s) {
+  const int steps = PLANES * (d / BK);
+  if (S < 1 || steps % S != 0) return hipErrorInvalidValue;
   GateArgs a{};
+  a.ksteps = steps / S;
+  a.c_split_stride = T * E;
   a.A = x;
   a.lda = d;
   a.B = w_prep;
@@ -230,12 +267,12 @@ hipError_t launch_gate_gemm_bf16(const uint16_t* x, const uint16_t* w_prep, floa
   a.ldc = E;
   a.rows_total = T;
   a.K = d;
-  if (E % 128 == 0) {
+  if (tile_of(E) == 128) {
     a.n_tiles = E / 128;
-    return launch<128, 128, 2>(a, s);
+    return launch<128, 128, 2>(a, S, s);
   }
   a.n_tiles = E / 64;
-  return launch<64, 64, 2>(a, s);
+  return launch<64, 64, 2>(a, S, s);
 }
 
 }  // namespace moe

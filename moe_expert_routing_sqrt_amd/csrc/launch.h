@@ -15,8 +15,11 @@ int device_cu_count();
 int stream_cu_count(hipStream_t s);
 
 // gate logits
+// S split products over the reduction: partial products [S, T, E] at logits
+// (S = 1: the logits themselves); gate_gemm_split_count: the S a launch takes
 hipError_t launch_gate_gemm_bf16(const uint16_t* x, const uint16_t* w_prep, float* logits,
-                                 int64_t T, int d, int E, hipStream_t s);
+                                 int64_t T, int d, int E, int S, hipStream_t s);
+int gate_gemm_split_count(int64_t T, int d, int E);
 hipError_t launch_gate_gemm_simt(const void* x, int x_dtype, const uint16_t* w_prep,
                                  float* logits, int64_t T, int d, int E, hipStream_t s);
 bool gate_gemm_bf16_supported(int d, int E);

@@ -116,6 +116,24 @@ def test_route_workspace_split_gate():
         assert _route(sh, xdt=_lib.MOE_F32, logits=FAKE, wsb=planes - 1) == -3
 
 
+def test_route_workspace_split_small_gate():
+    """bf16 x with E % 256 != 0 (E = 64, 64 x 64 tiles): the gate product is
+    split over its 96 steps at d = 2048 until the launch reaches 256 tiles, so
+    the workspace holds S partial products whether or not the caller keeps the
+    logits (no split counters on this path); with one split the product writes
+    the logits directly."""
+    planes = 3 * 64 * 2048 * 2
+    for T, S in ((77, 8), (4096, 4), (8192, 2), (16384, 1)):
+        s = _sh(T=T, d=2048, E=64, G=8, M=4, k=6, gk=1)
+        sh = ctypes.byref(s)
+        need = L.moe_workspace_size(_lib.MOE_OP_ROUTE, sh, _lib.MOE_BF16)
+        logits_bytes = (T * 64 * 4 + 255) // 256 * 256
+        assert need == planes + (S if S > 1 else 1) * logits_bytes, (T, S)
+        assert _route(sh, logits=None, wsb=need - 1) == -3, T
+        kept = need if S > 1 else planes
+        assert _route(sh, logits=FAKE, wsb=kept - 1) == -3, T
+
+
 def test_route_unsupported_and_empty():
     sh = _sh(E=320, G=5, M=2, k=4, gk=2)
     assert _route(ctypes.byref(sh)) == -2

@@ -47,7 +47,9 @@ def test_gate_logits_tolerance(name, T):
     tile.  At E = 256 with bf16 x the gate product is split over its reduction
     into partial products that the selection sums: 4 at V3 (64 row tiles), 8
     at 1, 300, 1000 and 4100 tokens, 3 at 20000, 2 at 32768, and none at 65536
-    tokens (256 row tiles fill the chip; the product writes the logits)."""
+    tokens (256 row tiles fill the chip; the product writes the logits).  At
+    E = 64 (Flash) the 64 x 64-tile product splits the same way: 4 partial
+    products at 4096 tokens, 8 at 77."""
     dev = need_gpu()
     cfg, inp, o = router_inputs(name, T)
     print(f"route S1 {name} T={cfg.T}", flush=True)
