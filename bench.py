@@ -84,6 +84,9 @@ def parse():
                          "forward + backward), each in a child process of its own, and add their figures "
                          "to the line as other_workloads; auto: only on the full default report (V3, "
                          "top-k, CPU baseline on)")
+    ap.add_argument("--down-variants", action="store_true",
+                    help="as --up-variants, for the down-projection (the routed rows' h against each "
+                         "variant's W2 groups; one JSON line)")
     ap.add_argument("--up-variants", action="store_true",
                     help="instead of the bench: time the routed up-projection against the same rows in "
                          "equal shares per expert and against one expert's weights (one JSON line)")
@@ -300,12 +303,12 @@ def cpu_baseline(cfg, inp, ex, S, ids=None):
             "seconds": total, "stages": st}
 
 
-def up_variants(torch, M, cfg, layer, x, ids):
-    """The routed up-projection of one forward, then the same packed rows split
-    equally over the experts (every tile full, every expert's own weights) and
-    given to one expert (one weight set), in that order: the mean of five
-    back-to-back launches each, printed as one JSON line.  Three forwards
-    first bring the clocks up."""
+def up_variants(torch, M, cfg, layer, x, ids, stage="up"):
+    """The routed up-projection (stage "down": down-projection) of one
+    forward, then the same packed rows split equally over the experts (every
+    tile full, every expert's own weights) and given to one expert (one weight
+    set), in that order: the mean of five back-to-back launches each, printed
+    as one JSON line.  Three forwards first bring the clocks up."""
     for _ in range(3):
         layer.forward(x, token_ids=ids)
     torch.cuda.synchronize()
@@ -320,14 +323,18 @@ def up_variants(torch, M, cfg, layer, x, ids):
                          layer.w13, layer.w13_s))
     variants.append(("dense", torch.tensor([0, rows], dtype=torch.int32, device=dev), layer.w13[:1],
                      first(layer.w13_s)))
-    flops = 4 * cfg.d * cfg.d_ff * rows
+    flops = (4 if stage == "up" else 2) * cfg.d * cfg.d_ff * rows
     res = {}
     for name, off, w13, w13_s in variants:
+        # the down-projection variants take W2 of the same experts (one for dense)
+        w2 = layer.w2 if name != "dense" else layer.w2[:1]
+        w2_s = layer.w2_s if name != "dense" else first(layer.w2_s)
         # five back-to-back launches between two events on the launch stream
         # (no host gap between them); the first (untimed) brings the clocks up
-        run = lambda: M.expert_ffn(off, layer.max_rows, b["xp"], w13, layer.w2, layer.dtype,
-                                   xp_scale=b["xp_scale"], w13_scale=w13_s, w2_scale=layer.w2_s, h=layer.h,
-                                   h_scale=layer.h_s, yp=layer.yp, stages=M.MOE_FFN_UP)
+        run = lambda: M.expert_ffn(off, layer.max_rows, b["xp"], w13, w2, layer.dtype,
+                                   xp_scale=b["xp_scale"], w13_scale=w13_s, w2_scale=w2_s, h=layer.h,
+                                   h_scale=layer.h_s, yp=layer.yp,
+                                   stages=M.MOE_FFN_UP if stage == "up" else M.MOE_FFN_DOWN)
         run()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -337,7 +344,7 @@ def up_variants(torch, M, cfg, layer, x, ids):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / 5
         res[name] = {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
-    print(json.dumps({"up_variants": res, "workload": workload_name(cfg), "rows": rows}), flush=True)
+    print(json.dumps({f"{stage}_variants": res, "workload": workload_name(cfg), "rows": rows}), flush=True)
 
 
 # the other workloads of the full report: name, bench.py arguments
@@ -518,8 +525,8 @@ def main():
     ids = gen.token_ids(cfg, device=dev) if a.router == "hash" else None
     torch.cuda.synchronize()
     print(f"setup {time.perf_counter() - t_setup:.1f}s: {workload_name(cfg, a.router)}", file=sys.stderr, flush=True)
-    if a.up_variants:
-        up_variants(torch, M, cfg, layer, x, ids)
+    if a.up_variants or a.down_variants:
+        up_variants(torch, M, cfg, layer, x, ids, "up" if a.up_variants else "down")
         return
     if a.overlap:
         overlap(torch, M, cfg, layer, x, ids, a.reserve)
